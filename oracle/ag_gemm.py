@@ -57,20 +57,16 @@ def ag_flag_units(ranks: int, shard_m: int, k: int, tile_m: int, tile_n: int, ti
     One flag per batch of tiles that are always read together ("Triton-
     distributed Semantics", Best Practices, batching signals): a unit is a
     row panel of min(tile_m, shard_m) rows of one shard and a K-range of
-    tiles_per_flag * tile_n columns (tiles_per_flag = 0: all of K).  The unit
-    index is (shard * panels_per_shard + panel) * batches + batch.
+    tiles_per_flag * tile_n columns (tiles_per_flag = 0: all of K).  The
+    pages leave ragged sizes open; here a shard's last panel and the last
+    K-range are simply shorter, so every row and column belongs to exactly
+    one unit.  The unit index is (shard * panels_per_shard + panel) *
+    batches + batch.
     """
     unit_rows = min(tile_m, shard_m)
-    if shard_m % unit_rows:
-        raise ValueError("shard rows must be a multiple of the unit rows")
-    panels = shard_m // unit_rows
-    if tiles_per_flag <= 0:
-        batches = 1
-    else:
-        width = tiles_per_flag * tile_n
-        if k % width:
-            raise ValueError("K must be a multiple of the flag batch width")
-        batches = k // width
+    panels = -(-shard_m // unit_rows)
+    width = k if tiles_per_flag <= 0 else tiles_per_flag * tile_n
+    batches = -(-k // width)
     return ranks * panels * batches, panels, batches
 
 

@@ -112,6 +112,21 @@ def test_flag_units(cfg, tpf, want):
     assert oracle.ag_flag_units(cfg.ranks, cfg.shard_m, cfg.k, cfg.tile_m, cfg.tile_n, tpf) == want
 
 
+def test_flag_units_ragged_cover_every_row_and_column_once():
+    # 3 ranks of 100 rows, 48-row panels (48, 48, 4), K = 200 in batches of
+    # 2 x 40 = 80 columns (80, 80, 40): 3 * 3 * 3 units.
+    units, panels, batches = oracle.ag_flag_units(3, 100, 200, 48, 40, 2)
+    assert (units, panels, batches) == (27, 3, 3)
+    covered = np.zeros((300, 200), dtype=np.int32)
+    for u in range(units):
+        b = u % batches
+        s, p = divmod(u // batches, panels)
+        r0 = s * 100 + p * 48
+        r1 = min(r0 + 48, (s + 1) * 100)
+        covered[r0:r1, b * 80:min(200, (b + 1) * 80)] += 1
+    assert (covered == 1).all()
+
+
 def test_expected_flags_layout():
     buf = oracle.expected_flags(5, 8, 3)
     assert buf.view(np.int64).tolist() == [3, 3, 3, 3, 3]
