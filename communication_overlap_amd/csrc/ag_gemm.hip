@@ -1,0 +1,471 @@
+// AllGather -> GEMM with tile-level producer/consumer overlap
+// ("Triton-distributed Semantics", Kernel Design Patterns, "AllGather and
+// GEMM Overlapping"; Producer-Consumer Model; Threadblock Swizzling).
+//
+// One persistent launch.  Workgroups [0, P) are producers: they take flag
+// units in the caller's producer order, copy each unit's rows and K-range
+// from its shard into the gathered buffer with 16-byte vectors, and publish
+// the unit's flag (agent-scope release).  Workgroups [P, P + C) are
+// consumers: each computes output tiles in arrival order; before the K-step
+// that enters a new K-batch it waits (wave-level acquire) on every unit that
+// covers the tile's rows in that batch, then loads the A tile from the
+// gathered buffer.  Tiles whose rows are all the own rank's read the own
+// shard directly and never wait.
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "device.h"
+#include "gemm_core.h"
+#include "host.h"
+
+namespace ovl {
+
+constexpr int kMaxRanks = 16;
+constexpr int kMaxRowTiles = 1024;  // consumer-order table held in LDS
+constexpr int kXcds = 8;            // MI355X: 8 accelerator complex dies, each with its own L2
+
+struct AgArgs {
+  const uint16_t* shards[kMaxRanks];
+  const uint16_t* b;
+  uint16_t* g;
+  float* c;
+  int64_t* flags;
+  ErrRec* err;
+  const int32_t* order;
+  int64_t shard_m, m, k, n;
+  int64_t flag_stride;  // in int64 slots
+  int64_t epoch;
+  uint64_t spin_limit;
+  int32_t ranks, rank;
+  int32_t unit_rows, panels, batches, batch_cols;
+  int32_t num_units;
+  int32_t producers, consumers;
+  int32_t tiles_m, tiles_n;
+};
+
+enum { kModeFused = 0, kModeBarrier = 1, kModeGemmOnly = 2 };
+
+// ---------------------------------------------------------------- producer
+
+// Copies rows x cols bf16 (cols a multiple of 8) between two row-major
+// matrices of row pitch ld, 16 bytes per lane, 8 vectors in flight per lane.
+__device__ inline void copy_block(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int64_t rows,
+                                  int64_t cols, int64_t ld) {
+  constexpr int U = 8;
+  const uint32_t vpr = (uint32_t)(cols / 8);
+  const uint32_t total = (uint32_t)(rows * vpr);
+  for (uint32_t base = 0; base < total; base += kThreads * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const uint32_t idx = base + j * kThreads + threadIdx.x;
+      if (idx < total) {
+        const uint32_t r = idx / vpr, c = idx - r * vpr;
+        v[j] = ld16_nt(src + r * ld + c * 8);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const uint32_t idx = base + j * kThreads + threadIdx.x;
+      if (idx < total) {
+        const uint32_t r = idx / vpr, c = idx - r * vpr;
+        st16(dst + r * ld + c * 8, v[j]);
+      }
+    }
+  }
+}
+
+__device__ inline void produce(const AgArgs& a, int w, int P) {
+  for (int i = w; i < a.num_units; i += P) {
+    const int u = a.order ? a.order[i] : i;
+    if (u < 0 || u >= a.num_units) continue;  // not a unit index: nothing to move
+    const int bt = u % a.batches;
+    const int sp = u / a.batches;
+    const int p = sp % a.panels;
+    const int s = sp / a.panels;
+    const int64_t r0 = (int64_t)p * a.unit_rows;
+    const int64_t rows = min((int64_t)a.unit_rows, a.shard_m - r0);
+    const int64_t c0 = (int64_t)bt * a.batch_cols;
+    const int64_t cols = min((int64_t)a.batch_cols, a.k - c0);
+    copy_block(a.shards[s] + r0 * a.k + c0, a.g + ((int64_t)s * a.shard_m + r0) * a.k + c0, rows, cols, a.k);
+    wg_publish(a.flags + (int64_t)u * a.flag_stride, a.epoch);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void ag_produce_kernel(AgArgs a) { produce(a, blockIdx.x, gridDim.x); }
+
+// ---------------------------------------------------------------- consumer order
+
+// Row tile rt covers gathered rows [rt*BM, min((rt+1)*BM, m)).  It is "own"
+// when all of them belong to the own rank's shard.
+__device__ inline bool row_tile_own(const AgArgs& a, int BM, int rt) {
+  const int64_t lo = (int64_t)rt * BM, hi = min(lo + BM, a.m);
+  return lo >= (int64_t)a.rank * a.shard_m && hi <= (int64_t)(a.rank + 1) * a.shard_m;
+}
+
+// Fills sorted[0 .. tiles_m) with the row tiles in consumer order: own tiles
+// first (ascending), then the others by the latest producer-order position
+// among the first-K-batch units covering their rows (ties by index).
+__device__ void build_consumer_order(const AgArgs& a, int BM, int* key, int* sorted) {
+  const int T = a.tiles_m;
+  for (int rt = threadIdx.x; rt < T; rt += kThreads) key[rt] = row_tile_own(a, BM, rt) ? -1 : 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < a.num_units; i += kThreads) {
+    const int u = a.order ? a.order[i] : i;
+    if (u < 0 || u >= a.num_units || u % a.batches) continue;
+    const int sp = u / a.batches;
+    const int p = sp % a.panels, s = sp / a.panels;
+    const int64_t r_lo = (int64_t)s * a.shard_m + (int64_t)p * a.unit_rows;
+    const int64_t r_hi = min(r_lo + a.unit_rows, (int64_t)(s + 1) * a.shard_m);
+    for (int rt = (int)(r_lo / BM); rt <= (int)((r_hi - 1) / BM); ++rt)
+      if (key[rt] >= 0) atomicMax(&key[rt], i);
+  }
+  __syncthreads();
+  for (int rt = threadIdx.x; rt < T; rt += kThreads) {
+    const int k0 = key[rt];
+    int rank = 0;
+    for (int q = 0; q < T; ++q) {
+      const int kq = key[q];
+      rank += (kq < k0) || (kq == k0 && q < rt);
+    }
+    sorted[rank] = rt;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- consumer
+
+template <int BM, int BN, int MODE>
+__device__ void consume(const AgArgs& a, int cidx, uint16_t* lds) {
+  using C = TileCfg<BM, BN>;
+  int* key = reinterpret_cast<int*>(lds + 2 * C::STAGE_ELEMS);
+  int* sorted = key + kMaxRowTiles;
+  build_consumer_order(a, BM, key, sorted);
+
+  bool timed_out = false;
+  if (MODE == kModeBarrier) {
+    // Every unit must have landed before any tile starts.
+    for (int u = lane_id(); u < a.num_units; u += 64) {
+      const int64_t* f = a.flags + (int64_t)u * a.flag_stride;
+      uint64_t polls = 0;
+      int64_t v;
+      while ((v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < a.epoch) {
+        if (++polls > a.spin_limit) {
+          report_error(a.err, OVL_ETIMEOUT, kSiteAgBarrier, u, v, a.epoch);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+
+  // Tiles in consumer order are dealt out in rounds of C; inside a round,
+  // consecutive tiles go to consumers on the same die (workgroup ids are
+  // dispatched round-robin over the dies), so that tiles sharing A rows or
+  // B columns share an L2.
+  const int Cn = a.consumers;
+  const int groups = (Cn % kXcds == 0) ? kXcds : 1;
+  const int per = Cn / groups;
+  const int x = cidx % groups, q = cidx / groups;
+  const int64_t total = (int64_t)a.tiles_m * a.tiles_n;
+  const int own_lo = a.rank;  // shard index of the own rank
+
+  for (int64_t w = 0;; ++w) {
+    const int64_t j = w * Cn + (int64_t)x * per + q;
+    if (j >= total) break;
+    const int rt = sorted[j / a.tiles_n];
+    const int nt = (int)(j % a.tiles_n);
+    const int64_t m0 = (int64_t)rt * BM, n0 = (int64_t)nt * BN;
+    const int64_t m_end = min(m0 + BM, a.m);
+    const bool own = row_tile_own(a, BM, rt);
+
+    Operands op;
+    op.b = a.b;
+    op.ldb = a.n;
+    op.n0 = n0;
+    op.n_valid = a.n;
+    op.k = a.k;
+    op.lda = a.k;
+    int64_t m0_op;
+    if (own) {
+      op.a = a.shards[own_lo];
+      op.m_valid = a.shard_m;
+      m0_op = m0 - (int64_t)a.rank * a.shard_m;
+    } else {
+      op.a = a.g;
+      op.m_valid = a.m;
+      m0_op = m0;
+    }
+
+    int last_batch = -1;
+    auto before_step = [&](int64_t k0) {
+      if (MODE != kModeFused || own || timed_out) return;
+      const int bt = (int)(k0 / a.batch_cols);
+      if (bt == last_batch) return;
+      last_batch = bt;
+      const int s_lo = (int)(m0 / a.shard_m), s_hi = (int)((m_end - 1) / a.shard_m);
+      for (int s = s_lo; s <= s_hi && !timed_out; ++s) {
+        const int64_t lo = max(m0, (int64_t)s * a.shard_m) - (int64_t)s * a.shard_m;
+        const int64_t hi = min(m_end, (int64_t)(s + 1) * a.shard_m) - (int64_t)s * a.shard_m;
+        for (int p = (int)(lo / a.unit_rows); p <= (int)((hi - 1) / a.unit_rows); ++p) {
+          const int64_t u = ((int64_t)s * a.panels + p) * a.batches + bt;
+          if (!wave_wait(a.flags + u * a.flag_stride, a.epoch, a.spin_limit, a.err, kSiteAgUnit, u)) {
+            timed_out = true;
+            break;
+          }
+        }
+      }
+    };
+
+    Acc<BM, BN> acc;
+    gemm_tile<BM, BN>(acc, op, m0_op, lds, before_step);
+    acc_store<BM, BN>(acc, a.c, a.n, m0, n0, a.m, a.n);
+  }
+}
+
+template <int BM, int BN, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void ag_gemm_kernel(AgArgs a) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  if ((int)blockIdx.x < a.producers) {
+    produce(a, blockIdx.x, a.producers);
+    return;
+  }
+  consume<BM, BN, MODE>(a, (int)blockIdx.x - a.producers, lds);
+}
+
+template <int BM, int BN>
+constexpr int ag_lds_bytes() {
+  return TileCfg<BM, BN>::LDS_BYTES + 2 * kMaxRowTiles * (int)sizeof(int);
+}
+
+}  // namespace ovl
+
+using namespace ovl;
+
+struct ag_gemm_plan_s {
+  ag_gemm_desc d;
+  int64_t m;
+  int32_t unit_rows, panels, batches, batch_cols;
+  int64_t num_units;
+  int bm, bn;
+  int tiles_m, tiles_n;
+};
+
+namespace {
+
+template <int BM, int BN, int MODE>
+ovl_status launch_fused(const AgArgs& a, hipStream_t stream) {
+  const void* fn = reinterpret_cast<const void*>(&ag_gemm_kernel<BM, BN, MODE>);
+  const int lds = ag_lds_bytes<BM, BN>();
+  ovl_status st = allow_lds(fn, lds);
+  if (st) return st;
+  hipLaunchKernelGGL((ag_gemm_kernel<BM, BN, MODE>), dim3(a.producers + a.consumers), dim3(kThreads), lds,
+                     stream, a);
+  OVL_HIP_TRY(hipGetLastError());
+  return OVL_OK;
+}
+
+template <int BM, int BN>
+ovl_status occupancy(int* out) {
+  const int lds = ag_lds_bytes<BM, BN>();
+  ovl_status st = allow_lds(reinterpret_cast<const void*>(&ag_gemm_kernel<BM, BN, kModeFused>), lds);
+  if (st) return st;
+  OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(out, ag_gemm_kernel<BM, BN, kModeFused>, kThreads,
+                                                           lds));
+  return OVL_OK;
+}
+
+template <int BM, int BN>
+ovl_status dispatch_mode(const AgArgs& a, uint32_t mode, hipStream_t stream) {
+  switch (mode) {
+    case OVL_MODE_FUSED: return launch_fused<BM, BN, kModeFused>(a, stream);
+    case OVL_MODE_BARRIER: return launch_fused<BM, BN, kModeBarrier>(a, stream);
+    case OVL_MODE_GEMM_ONLY: return launch_fused<BM, BN, kModeGemmOnly>(a, stream);
+    default: return OVL_EINVAL;
+  }
+}
+
+}  // namespace
+
+extern "C" ovl_status ag_gemm_plan(const ag_gemm_desc* d, ag_gemm_plan_t* out) {
+  if (!d || !out) return OVL_EINVAL;
+  *out = nullptr;
+  if (d->ranks < 1 || d->rank < 0 || d->rank >= d->ranks) return OVL_EINVAL;
+  if (d->ranks > kMaxRanks) return OVL_EUNSUPPORTED;
+  if (d->shard_m < 1 || d->k < 8 || d->n < 8 || d->tile_m < 1 || d->tile_n < 8 || d->tiles_per_flag < 0)
+    return OVL_ESHAPE;
+  if (d->k % 8 || d->n % 8 || d->tile_n % 8) return OVL_EALIGN;
+  if (d->flag_stride < 8 || d->flag_stride % 8) return OVL_EALIGN;
+  const int64_t m = (int64_t)d->ranks * d->shard_m;
+  if (m > (1 << 20) || d->k > (1 << 24) || d->n > (1 << 24)) return OVL_EUNSUPPORTED;
+
+  ag_gemm_plan_s* p = new (std::nothrow) ag_gemm_plan_s();
+  if (!p) return OVL_EINVAL;
+  p->d = *d;
+  p->m = m;
+  p->unit_rows = (int32_t)std::min<int64_t>(d->tile_m, d->shard_m);
+  p->panels = (int32_t)ceil_div(d->shard_m, p->unit_rows);
+  const int64_t width = d->tiles_per_flag ? (int64_t)d->tiles_per_flag * d->tile_n : d->k;
+  p->batch_cols = (int32_t)std::min<int64_t>(width, d->k);
+  p->batches = (int32_t)ceil_div(d->k, p->batch_cols);
+  p->num_units = (int64_t)d->ranks * p->panels * p->batches;
+  if (p->num_units > (1 << 24)) {
+    delete p;
+    return OVL_EUNSUPPORTED;
+  }
+  // Large problems use 256x256 tiles; small ones 128x128 so that more
+  // workgroups get work (half of MI355X's 256 compute units at least).
+  const int64_t big_tiles = ceil_div(m, 256) * ceil_div(d->n, 256);
+  if (m >= 256 && d->n >= 256 && big_tiles >= 128) {
+    p->bm = 256;
+    p->bn = 256;
+  } else {
+    p->bm = 128;
+    p->bn = 128;
+  }
+  p->tiles_m = (int)ceil_div(m, p->bm);
+  p->tiles_n = (int)ceil_div(d->n, p->bn);
+  if (p->tiles_m > kMaxRowTiles) {
+    delete p;
+    return OVL_EUNSUPPORTED;
+  }
+  *out = p;
+  return OVL_OK;
+}
+
+extern "C" ovl_status ag_gemm_consumer_order(ag_gemm_plan_t p, const int32_t* order, int32_t* out) {
+  if (!p || !out) return OVL_EINVAL;
+  const ag_gemm_desc& d = p->d;
+  const int T = p->tiles_m;
+  const int64_t lo_own = (int64_t)d.rank * d.shard_m, hi_own = lo_own + d.shard_m;
+  std::vector<int64_t> key(T);
+  for (int rt = 0; rt < T; ++rt) {
+    const int64_t lo = (int64_t)rt * p->bm, hi = std::min<int64_t>(lo + p->bm, p->m);
+    key[rt] = (lo >= lo_own && hi <= hi_own) ? -1 : 0;
+  }
+  for (int64_t i = 0; i < p->num_units; ++i) {
+    const int64_t u = order ? order[i] : i;
+    if (u < 0 || u >= p->num_units) return OVL_EINVAL;
+    if (u % p->batches) continue;
+    const int64_t sp = u / p->batches;
+    const int64_t pn = sp % p->panels, s = sp / p->panels;
+    const int64_t r_lo = s * d.shard_m + pn * p->unit_rows;
+    const int64_t r_hi = std::min<int64_t>(r_lo + p->unit_rows, (s + 1) * d.shard_m);
+    for (int64_t rt = r_lo / p->bm; rt <= (r_hi - 1) / p->bm; ++rt)
+      if (key[rt] >= 0) key[rt] = std::max<int64_t>(key[rt], i);
+  }
+  std::vector<int32_t> idx(T);
+  for (int rt = 0; rt < T; ++rt) idx[rt] = rt;
+  std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) { return key[x] < key[y]; });
+  for (int rt = 0; rt < T; ++rt) out[rt] = idx[rt];
+  return OVL_OK;
+}
+
+extern "C" int32_t ag_gemm_row_tiles(ag_gemm_plan_t p) { return p ? p->tiles_m : 0; }
+extern "C" int32_t ag_gemm_tile_rows(ag_gemm_plan_t p) { return p ? p->bm : 0; }
+
+extern "C" ovl_status ag_gemm_plan_destroy(ag_gemm_plan_t p) {
+  delete p;
+  return OVL_OK;
+}
+
+extern "C" int64_t ag_gemm_num_units(ag_gemm_plan_t p) { return p ? p->num_units : 0; }
+
+extern "C" size_t ag_gemm_flags_bytes(ag_gemm_plan_t p) {
+  return p ? (size_t)p->num_units * (size_t)p->d.flag_stride : 0;
+}
+
+extern "C" size_t ag_gemm_workspace_bytes(ag_gemm_plan_t p) { return p ? 256 : 0; }
+
+extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, const void* b, void* gathered,
+                                  float* c, int64_t* flags, void* workspace, int64_t epoch,
+                                  const int32_t* producer_order, const ovl_opts* opts, hipStream_t stream) {
+  if (!p || !shards || !workspace) return OVL_EINVAL;
+  const uint32_t mode = opts ? opts->mode : OVL_MODE_FUSED;
+  if (mode > OVL_MODE_BARRIER) return OVL_EINVAL;
+  const bool needs_copy = mode != OVL_MODE_GEMM_ONLY;
+  const bool needs_gemm = mode != OVL_MODE_COPY_ONLY;
+  const ag_gemm_desc& d = p->d;
+  if (!gathered) return OVL_EINVAL;
+  if (!aligned16(gathered) || !aligned16(workspace)) return OVL_EALIGN;
+  for (int s = 0; s < d.ranks; ++s) {
+    if (!needs_copy && s != d.rank) continue;
+    if (!shards[s]) return OVL_EINVAL;
+    if (!aligned16(shards[s])) return OVL_EALIGN;
+  }
+  if (needs_gemm) {
+    if (!b || !c) return OVL_EINVAL;
+    if (!aligned16(b) || !aligned16(c)) return OVL_EALIGN;
+  }
+  if (needs_copy || mode == OVL_MODE_BARRIER) {
+    if (!flags) return OVL_EINVAL;
+    if (reinterpret_cast<uintptr_t>(flags) & 7u) return OVL_EALIGN;
+  }
+  if (producer_order && (reinterpret_cast<uintptr_t>(producer_order) & 3u)) return OVL_EALIGN;
+
+  DeviceInfo di;
+  ovl_status st = current_device_info(&di);
+  if (st) return st;
+
+  AgArgs a = {};
+  for (int s = 0; s < d.ranks; ++s) a.shards[s] = static_cast<const uint16_t*>(shards[s]);
+  a.b = static_cast<const uint16_t*>(b);
+  a.g = static_cast<uint16_t*>(gathered);
+  a.c = c;
+  a.flags = flags;
+  a.err = static_cast<ErrRec*>(workspace);
+  a.order = producer_order;
+  a.shard_m = d.shard_m;
+  a.m = p->m;
+  a.k = d.k;
+  a.n = d.n;
+  a.flag_stride = d.flag_stride / 8;
+  a.epoch = epoch;
+  a.spin_limit = spin_limit_of(opts);
+  a.ranks = d.ranks;
+  a.rank = d.rank;
+  a.unit_rows = p->unit_rows;
+  a.panels = p->panels;
+  a.batches = p->batches;
+  a.batch_cols = p->batch_cols;
+  a.num_units = (int32_t)p->num_units;
+  a.tiles_m = p->tiles_m;
+  a.tiles_n = p->tiles_n;
+
+  const int64_t tiles = (int64_t)p->tiles_m * p->tiles_n;
+  const uint32_t req_prod = opts ? opts->producers : 0;
+
+  if (mode == OVL_MODE_COPY_ONLY) {
+    ovl_status st = epoch_accept(flags, epoch);
+    if (st) return st;
+    int P = req_prod ? (int)req_prod : di.cus * 4;
+    P = (int)std::max<int64_t>(1, std::min<int64_t>(P, a.num_units));
+    a.producers = P;
+    a.consumers = 0;
+    hipLaunchKernelGGL(ag_produce_kernel, dim3(P), dim3(kThreads), 0, stream, a);
+    OVL_HIP_TRY(hipGetLastError());
+    return OVL_OK;
+  }
+
+  int occ = 0;
+  st = (p->bm == 256) ? occupancy<256, 256>(&occ) : occupancy<128, 128>(&occ);
+  if (st) return st;
+  const int64_t resident = (int64_t)std::max(occ, 1) * di.cus;
+  int P = 0;
+  if (needs_copy) {
+    P = req_prod ? (int)req_prod : std::max(kXcds, di.cus / 8);
+    P = (int)std::min<int64_t>(P, a.num_units);
+    if (P >= resident) return OVL_EINVAL;
+  }
+  int64_t Cn = std::min<int64_t>(tiles, resident - P);
+  if (Cn > kXcds) Cn -= Cn % kXcds;  // keep whole die groups
+  a.producers = P;
+  a.consumers = (int32_t)Cn;
+  if (needs_copy) {
+    st = epoch_accept(flags, epoch);
+    if (st) return st;
+  }
+  return (p->bm == 256) ? dispatch_mode<256, 256>(a, mode, stream) : dispatch_mode<128, 128>(a, mode, stream);
+}

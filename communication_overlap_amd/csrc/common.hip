@@ -1,0 +1,159 @@
+// Flag/epoch reset, device error check, error strings, the plain copy
+// kernel, and the host bookkeeping shared by the entry points.
+#include <map>
+#include <mutex>
+#include <set>
+#include <utility>
+
+#include "device.h"
+#include "host.h"
+
+namespace ovl {
+
+namespace {
+
+std::mutex g_mu;
+std::map<const void*, int64_t> g_last_epoch;  // flag buffer -> last accepted epoch
+std::map<int, int> g_cus;                     // device -> compute units
+std::set<std::pair<const void*, int>> g_lds;  // kernels whose LDS limit was raised
+
+__global__ void zero_kernel(uint8_t* p, size_t bytes) {
+  const size_t vecs = bytes / 16;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < vecs; i += stride)
+    st16(p + i * 16, u32x4{0, 0, 0, 0});
+  if (blockIdx.x == 0 && threadIdx.x < (bytes & 15)) p[vecs * 16 + threadIdx.x] = 0;
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
+                                                   size_t vecs) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < vecs; i += 4 * stride) {
+    u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    dst[i] = a;
+    dst[i + stride] = b;
+    dst[i + 2 * stride] = c;
+    dst[i + 3 * stride] = d;
+  }
+  for (; i < vecs; i += stride) dst[i] = src[i];
+}
+
+ovl_status zero_async(void* p, size_t bytes, hipStream_t stream) {
+  if (!bytes) return OVL_OK;
+  if (!p) return OVL_EINVAL;
+  if (reinterpret_cast<uintptr_t>(p) & 15u) return OVL_EALIGN;
+  const size_t vecs = bytes / 16;
+  const int blocks = (int)std::min<size_t>(1024, std::max<size_t>(1, (vecs + 255) / 256));
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, stream, (uint8_t*)p, bytes);
+  OVL_HIP_TRY(hipGetLastError());
+  return OVL_OK;
+}
+
+}  // namespace
+
+ovl_status current_device_info(DeviceInfo* out) {
+  int dev = 0;
+  OVL_HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_cus.find(dev);
+  if (it == g_cus.end()) {
+    int cus = 0;
+    OVL_HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    it = g_cus.emplace(dev, cus).first;
+  }
+  out->device = dev;
+  out->cus = it->second;
+  return OVL_OK;
+}
+
+ovl_status epoch_check(const void* flags, int64_t epoch) {
+  if (epoch < 1) return OVL_EEPOCH;
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_last_epoch.find(flags);
+  if (it != g_last_epoch.end() && epoch <= it->second) return OVL_EEPOCH;
+  return OVL_OK;
+}
+
+ovl_status epoch_accept(const void* flags, int64_t epoch) {
+  if (epoch < 1) return OVL_EEPOCH;
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_last_epoch.find(flags);
+  if (it != g_last_epoch.end() && epoch <= it->second) return OVL_EEPOCH;
+  g_last_epoch[flags] = epoch;
+  return OVL_OK;
+}
+
+void epoch_forget(const void* flags) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_last_epoch.erase(flags);
+}
+
+ovl_status allow_lds(const void* kernel, int bytes) {
+  int dev = 0;
+  OVL_HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_lds.count({kernel, dev})) return OVL_OK;
+  if (bytes > 65536)
+    OVL_HIP_TRY(hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
+  g_lds.insert({kernel, dev});
+  return OVL_OK;
+}
+
+}  // namespace ovl
+
+using namespace ovl;
+
+extern "C" ovl_status ovl_flags_reset(int64_t* flags, size_t flag_bytes, void* workspace, size_t ws_bytes,
+                                      hipStream_t stream) {
+  if ((flag_bytes && !flags) || (ws_bytes && !workspace)) return OVL_EINVAL;
+  if ((flags && !aligned16(flags)) || (workspace && !aligned16(workspace))) return OVL_EALIGN;
+  ovl_status st = zero_async(flags, flag_bytes, stream);
+  if (st) return st;
+  st = zero_async(workspace, ws_bytes, stream);
+  if (st) return st;
+  if (flags) epoch_forget(flags);
+  return OVL_OK;
+}
+
+extern "C" ovl_status ovl_check(const void* workspace, int64_t* detail, hipStream_t stream) {
+  if (!workspace) return OVL_EINVAL;
+  OVL_HIP_TRY(hipStreamSynchronize(stream));
+  ErrRec rec;
+  OVL_HIP_TRY(hipMemcpy(&rec, workspace, sizeof(rec), hipMemcpyDeviceToHost));
+  if (detail) {
+    detail[0] = rec.site;
+    detail[1] = rec.index;
+    detail[2] = rec.observed;
+    detail[3] = rec.expected;
+  }
+  return rec.status;
+}
+
+extern "C" const char* ovl_strerror(ovl_status s) {
+  switch (s) {
+    case OVL_OK: return "ok";
+    case OVL_EINVAL: return "invalid argument";
+    case OVL_ESHAPE: return "shape does not fit the tiling rules";
+    case OVL_EALIGN: return "pointer not 16-byte aligned or row length not a multiple of 8";
+    case OVL_EEPOCH: return "epoch must be >= 1 and above the last epoch used on these flags";
+    case OVL_EHIP: return "HIP runtime error";
+    case OVL_ETIMEOUT: return "a flag wait exceeded its spin limit";
+    case OVL_EUNSUPPORTED: return "unsupported by this implementation";
+    default: return "unknown status";
+  }
+}
+
+extern "C" ovl_status ovl_copy(void* dst, const void* src, size_t bytes, int32_t blocks, hipStream_t stream) {
+  if (!bytes) return OVL_OK;
+  if (!dst || !src || blocks < 0) return OVL_EINVAL;
+  if (!aligned16(dst) || !aligned16(src) || (bytes & 15)) return OVL_EALIGN;
+  DeviceInfo di;
+  ovl_status st = current_device_info(&di);
+  if (st) return st;
+  const size_t vecs = bytes / 16;
+  if (!blocks) blocks = (int32_t)std::min<size_t>((size_t)di.cus * 8, (vecs + 255) / 256);
+  hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(256), 0, stream, (u32x4*)dst, (const u32x4*)src, vecs);
+  OVL_HIP_TRY(hipGetLastError());
+  return OVL_OK;
+}

@@ -1,0 +1,96 @@
+// Device-side building blocks shared by the overlap kernels: vector types,
+// the error record, the flag wait (acquire) and the flag publish (release).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ovl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;  // 4 wavefronts of 64 lanes per workgroup
+
+// Device error record at the start of every workspace (OVL_ERROR_RECORD_BYTES).
+struct ErrRec {
+  int32_t status;    // 0 or an ovl_status
+  int32_t site;      // which wait gave up
+  int64_t index;     // flag slot index
+  int64_t observed;  // last value read
+  int64_t expected;  // value awaited
+  int64_t pad[4];
+};
+static_assert(sizeof(ErrRec) == 64, "error record size");
+
+enum : int32_t { kSiteAgUnit = 1, kSiteAgBarrier = 2, kSiteRsIn = 3, kSiteA2aSlice = 4 };
+
+__device__ inline void report_error(ErrRec* e, int32_t code, int32_t site, int64_t index,
+                                    int64_t observed, int64_t expected) {
+  if (atomicCAS(&e->status, 0, code) == 0) {
+    e->site = site;
+    e->index = index;
+    e->observed = observed;
+    e->expected = expected;
+  }
+}
+
+__device__ inline int lane_id() { return threadIdx.x & 63; }
+
+// Wave-level acquire wait: every lane of the calling wavefront polls `flag`
+// (one load per poll, uniform address) with relaxed agent-scope loads until
+// it holds a value >= epoch, then issues one agent-scope acquire fence, so
+// that every load the wave issues afterwards sees the producer's data.
+// Returns false (after recording OVL_ETIMEOUT) if spin_limit polls pass.
+__device__ inline bool wave_wait(const int64_t* flag, int64_t epoch, uint64_t spin_limit,
+                                 ErrRec* err, int32_t site, int64_t index) {
+  int64_t v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t polls = 0;
+  bool ok = true;
+  while (__builtin_amdgcn_readfirstlane((int)(v < epoch))) {
+    if (++polls > spin_limit) {
+      ok = false;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+    v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (!ok) {
+    if (lane_id() == 0) report_error(err, -6 /* OVL_ETIMEOUT */, site, index, v, epoch);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return ok;
+}
+
+// Workgroup-level publish: every thread calls this after its own stores of
+// the unit.  Each wave releases its stores at agent scope (waits for them and
+// writes back its L2), the workgroup barrier orders all waves before thread
+// 0, and thread 0 stores the epoch with release semantics.
+__device__ inline void wg_publish(int64_t* flag, int64_t epoch) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup-level arrival on a counter: like wg_publish, but thread 0 adds 1
+// to `counter` (release) and returns the value it observed before the add
+// (only thread 0's return value is meaningful).
+__device__ inline int64_t wg_arrive(int64_t* counter) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  int64_t old = 0;
+  if (threadIdx.x == 0)
+    old = __hip_atomic_fetch_add(counter, (int64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  return old;
+}
+
+__device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ inline void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ inline u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+}  // namespace ovl

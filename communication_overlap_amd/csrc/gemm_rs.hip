@@ -1,0 +1,201 @@
+// GEMM -> ReduceScatter with tile-level overlap ("Triton-distributed
+// Semantics", Kernel Design Patterns, "GEMM and ReduceScatter Overlapping").
+//
+// One persistent launch of consumer-style GEMM workgroups.  The local
+// product's rows split into R blocks; tiles of the blocks destined for peers
+// come first, starting at block rank+1 (the mirror of the all-gather's
+// swizzle), and the own block comes last.
+//   - Peer tile: the fp32 tile is stored to that peer's partial buffer, then
+//     its out flag is published (put + signal).
+//   - Own tile: every wave waits (acquire) on the tile's in flag of each
+//     peer, then writes acc + P_q for q != rank in ascending q, in fp32.
+#include <algorithm>
+
+#include "device.h"
+#include "gemm_core.h"
+#include "host.h"
+
+namespace ovl {
+
+namespace {
+
+constexpr int kRsMaxRanks = 16;
+constexpr int kRsTile = 256;
+constexpr int kRsXcds = 8;
+
+struct RsArgs {
+  float* peer_out[kRsMaxRanks];
+  const float* peer_in[kRsMaxRanks];
+  const uint16_t* a;
+  const uint16_t* b;
+  float* out;
+  int64_t* out_flags;
+  const int64_t* in_flags;
+  ErrRec* err;
+  int64_t m, n, k, bm;  // bm = rows per block
+  int64_t flag_stride;  // int64 slots
+  int64_t epoch;
+  uint64_t spin_limit;
+  int32_t ranks, rank;
+  int32_t tr, tc;       // row / column tiles per block
+  int32_t workers;
+  int32_t wait_in;      // 0: do not wait on in_flags (GEMM-only timing)
+};
+
+template <int MODE_WAIT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs a) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  constexpr int BM = kRsTile, BN = kRsTile;
+  const int tpb = a.tr * a.tc;
+  const int64_t total = (int64_t)a.ranks * tpb;
+  const int Cn = a.workers;
+  const int groups = (Cn % kRsXcds == 0) ? kRsXcds : 1;
+  const int per = Cn / groups;
+  const int cidx = blockIdx.x;
+  const int x = cidx % groups, q = cidx / groups;
+  bool timed_out = false;
+
+  for (int64_t w = 0;; ++w) {
+    const int64_t j = w * Cn + (int64_t)x * per + q;
+    if (j >= total) break;
+    const int blk = (int)((a.rank + 1 + j / tpb) % a.ranks);
+    const int t = (int)(j % tpb);
+    const int trow = t / a.tc, tcol = t % a.tc;
+
+    Operands op;
+    op.a = a.a + (int64_t)blk * a.bm * a.k;
+    op.lda = a.k;
+    op.m_valid = a.bm;
+    op.b = a.b;
+    op.ldb = a.n;
+    op.n0 = (int64_t)tcol * BN;
+    op.n_valid = a.n;
+    op.k = a.k;
+    const int64_t m0 = (int64_t)trow * BM;
+
+    Acc<BM, BN> acc;
+    gemm_tile<BM, BN>(acc, op, m0, lds, [](int64_t) {});
+
+    if (blk != a.rank) {
+      float* dst = a.peer_out[blk];
+      acc_store<BM, BN>(acc, dst, a.n, m0, op.n0, a.bm, a.n);
+      wg_publish(a.out_flags + ((int64_t)blk * tpb + t) * a.flag_stride, a.epoch);
+    } else {
+      if (MODE_WAIT) {
+        for (int p = 0; p < a.ranks && !timed_out; ++p) {
+          if (p == a.rank) continue;
+          const int64_t idx = (int64_t)p * tpb + t;
+          if (!wave_wait(a.in_flags + idx * a.flag_stride, a.epoch, a.spin_limit, a.err, kSiteRsIn, idx))
+            timed_out = true;
+        }
+      }
+      const int64_t n0 = op.n0;
+      acc_foreach(acc, [&](int row, int col, float v) {
+        const int64_t mm = m0 + row, nn = n0 + col;
+        if (mm < a.bm && nn < a.n) {
+          const int64_t off = mm * a.n + nn;
+          for (int p = 0; p < a.ranks; ++p)
+            if (p != a.rank) v += a.peer_in[p][off];
+          a.out[off] = v;
+        }
+      });
+    }
+  }
+}
+
+constexpr int rs_lds_bytes() { return TileCfg<kRsTile, kRsTile>::LDS_BYTES; }
+
+}  // namespace
+
+}  // namespace ovl
+
+using namespace ovl;
+
+extern "C" size_t gemm_rs_flags_bytes(const gemm_rs_desc* d) {
+  if (!d || d->ranks < 1 || d->m < 1 || d->n < 1 || d->flag_stride < 8 || d->m % d->ranks) return 0;
+  const int64_t bm = d->m / d->ranks;
+  const int64_t tpb = ceil_div(bm, kRsTile) * ceil_div(d->n, kRsTile);
+  return (size_t)(d->ranks * tpb * d->flag_stride);
+}
+
+extern "C" size_t gemm_rs_workspace_bytes(const gemm_rs_desc* d) { return d ? 256 : 0; }
+
+extern "C" ovl_status gemm_rs_run(const gemm_rs_desc* d, const void* a, const void* b, float* const* peer_out,
+                                  const float* const* peer_in, float* out, int64_t* out_flags,
+                                  const int64_t* in_flags, void* workspace, int64_t epoch, const ovl_opts* opts,
+                                  hipStream_t stream) {
+  if (!d || !a || !b || !out || !workspace) return OVL_EINVAL;
+  if (d->ranks < 1 || d->rank < 0 || d->rank >= d->ranks) return OVL_EINVAL;
+  if (d->ranks > kRsMaxRanks) return OVL_EUNSUPPORTED;
+  if (d->tile_m != kRsTile || d->tile_n != kRsTile) return OVL_EUNSUPPORTED;
+  if (d->m < 1 || d->n < 8 || d->k < 8 || d->m % d->ranks) return OVL_ESHAPE;
+  if (d->n % 8 || d->k % 8 || d->flag_stride < 8 || d->flag_stride % 8) return OVL_EALIGN;
+  if (d->m > (1 << 20) || d->n > (1 << 24) || d->k > (1 << 24)) return OVL_EUNSUPPORTED;
+  const uint32_t mode = opts ? opts->mode : OVL_MODE_FUSED;
+  if (mode != OVL_MODE_FUSED && mode != OVL_MODE_GEMM_ONLY) return OVL_EINVAL;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(out) || !aligned16(workspace)) return OVL_EALIGN;
+  if (d->ranks > 1) {
+    if (!peer_out || !peer_in || !out_flags || !in_flags) return OVL_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(out_flags) & 7u) || (reinterpret_cast<uintptr_t>(in_flags) & 7u))
+      return OVL_EALIGN;
+    for (int p = 0; p < d->ranks; ++p) {
+      if (p == d->rank) continue;
+      if (!peer_out[p] || !peer_in[p]) return OVL_EINVAL;
+      if (!aligned16(peer_out[p]) || !aligned16(peer_in[p])) return OVL_EALIGN;
+    }
+  }
+  DeviceInfo di;
+  ovl_status st = current_device_info(&di);
+  if (st) return st;
+
+  RsArgs r = {};
+  for (int p = 0; p < d->ranks; ++p) {
+    if (p == d->rank) continue;
+    r.peer_out[p] = peer_out[p];
+    r.peer_in[p] = peer_in[p];
+  }
+  r.a = static_cast<const uint16_t*>(a);
+  r.b = static_cast<const uint16_t*>(b);
+  r.out = out;
+  r.out_flags = out_flags;
+  r.in_flags = in_flags;
+  r.err = static_cast<ErrRec*>(workspace);
+  r.m = d->m;
+  r.n = d->n;
+  r.k = d->k;
+  r.bm = d->m / d->ranks;
+  r.flag_stride = d->flag_stride / 8;
+  r.epoch = epoch;
+  r.spin_limit = spin_limit_of(opts);
+  r.ranks = d->ranks;
+  r.rank = d->rank;
+  r.tr = (int32_t)ceil_div(r.bm, kRsTile);
+  r.tc = (int32_t)ceil_div(d->n, kRsTile);
+  r.wait_in = mode == OVL_MODE_FUSED;
+
+  const int lds = rs_lds_bytes();
+  const void* fn = (mode == OVL_MODE_FUSED) ? reinterpret_cast<const void*>(&gemm_rs_kernel<1>)
+                                            : reinterpret_cast<const void*>(&gemm_rs_kernel<0>);
+  st = allow_lds(fn, lds);
+  if (st) return st;
+  st = allow_lds(reinterpret_cast<const void*>(&gemm_rs_kernel<1>), lds);
+  if (st) return st;
+  int occ = 0;
+  OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_rs_kernel<1>, kThreads, lds));
+  const int64_t total = (int64_t)d->ranks * r.tr * r.tc;
+  int64_t workers = std::min<int64_t>(total, (int64_t)std::max(occ, 1) * di.cus);
+  if (workers > kRsXcds) workers -= workers % kRsXcds;
+  r.workers = (int32_t)workers;
+  if (d->ranks > 1) {
+    st = epoch_accept(out_flags, epoch);
+    if (st) return st;
+  } else if (epoch < 1) {
+    return OVL_EEPOCH;
+  }
+  if (mode == OVL_MODE_FUSED)
+    hipLaunchKernelGGL(gemm_rs_kernel<1>, dim3(workers), dim3(kThreads), lds, stream, r);
+  else
+    hipLaunchKernelGGL(gemm_rs_kernel<0>, dim3(workers), dim3(kThreads), lds, stream, r);
+  OVL_HIP_TRY(hipGetLastError());
+  return OVL_OK;
+}

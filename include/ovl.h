@@ -1,0 +1,290 @@
+/*
+ * ovl.h: tile-centric overlap of communication with computation on one
+ * MI355X (gfx950).
+ *
+ * Three operations, each one persistent HIP launch in which producer
+ * workgroups move tiles and publish one int64 flag per tile batch, and
+ * consumer workgroups wait on each flag and compute on that tile at once
+ * ("Triton-distributed Semantics": Producer-Consumer Model, Signal-Based
+ * Synchronization, Kernel Design Patterns).  The other ranks of a group are
+ * emulated: their buffers are ordinary device buffers in the same HBM, and
+ * a "peer" is a pointer in a host-side table (the role the symmetric heap's
+ * per-rank base table plays in "Distributed Architecture Design", 5.3).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers unless marked HOST.  All buffers belong to
+ *    the caller; the library never allocates device memory and keeps no
+ *    pointer after a call returns.
+ *  - bf16 is stored as uint16 bit patterns.  Matrices are row-major.
+ *  - Device buffers must be 16-byte aligned, and row lengths (K, N, hidden)
+ *    multiples of 8 elements, so that every row moves in 16-byte vectors.
+ *  - *_run calls are asynchronous on `stream`: they validate, enqueue one or
+ *    two kernels and return.  Argument errors are returned before anything
+ *    is enqueued and nothing is written.  Errors found on the device (a
+ *    wait that timed out) are recorded in the workspace and returned by
+ *    ovl_check().
+ *  - Flags: a flag slot is an int64 holding the epoch of the last signal
+ *    (0 = never signalled).  A consumer waits until the slot is >= the
+ *    epoch; the wait never modifies the slot, so any number of waiters may
+ *    share it, and clearing is the reset's job (the pages' wait is
+ *    non-consuming: "Triton-distributed Semantics", Wait Polling Mechanism).
+ *    Epochs used on one flag buffer must increase from call to call; zero
+ *    the buffer with ovl_flags_reset() before its first use, after which
+ *    epochs start again at 1.
+ *  - Ordering: a producer's data stores are released at agent scope before
+ *    its flag store; a consumer acquires at agent scope after its flag load
+ *    and issues its tile loads only afterwards (the role consume_token plays
+ *    in "Triton-distributed Semantics", Token-Based Data Dependency).  No
+ *    system-scope ordering is used: every peer lives in the same HBM.
+ *  - Two calls must not run concurrently on the same flags or workspace.
+ *  - Results do not depend on the producer order, the mode or the number of
+ *    producer workgroups: every output element is accumulated in one fixed
+ *    order.
+ */
+#ifndef OVL_H_
+#define OVL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ovl_status;
+
+enum {
+  OVL_OK = 0,
+  OVL_EINVAL = -1,       /* null pointer, bad rank, bad mode, bad option */
+  OVL_ESHAPE = -2,       /* sizes that do not fit the tiling rules */
+  OVL_EALIGN = -3,       /* pointer not 16-byte aligned, or a row length not a multiple of 8 */
+  OVL_EEPOCH = -4,       /* epoch < 1, or not above the last epoch used on these flags */
+  OVL_EHIP = -5,         /* a HIP runtime call failed */
+  OVL_ETIMEOUT = -6,     /* device: a wait exceeded its spin limit */
+  OVL_EUNSUPPORTED = -7  /* a limit of this implementation (listed at each call) */
+};
+
+/* Run modes.  FUSED is the method; the others exist to measure it and to
+ * test it.  BARRIER lets every consumer start only after every unit has
+ * been moved (the pages' debugging advice: rule out fine-grained
+ * synchronisation bugs by synchronising everything first); COPY_ONLY runs
+ * the producers alone; GEMM_ONLY runs the consumers alone, without any
+ * wait, on operands the caller has already gathered or flagged. */
+enum {
+  OVL_MODE_FUSED = 0,
+  OVL_MODE_COPY_ONLY = 1,
+  OVL_MODE_GEMM_ONLY = 2,
+  OVL_MODE_BARRIER = 3
+};
+
+typedef struct ovl_opts {
+  uint32_t mode;        /* OVL_MODE_* */
+  uint32_t producers;   /* producer workgroups; 0 = library default */
+  uint64_t spin_limit;  /* polls before a wait gives up (OVL_ETIMEOUT); 0 = default (~2^22) */
+} ovl_opts;
+
+/* Size in bytes of the device-side error record at the start of every
+ * workspace; the workspaces below are at least this large. */
+#define OVL_ERROR_RECORD_BYTES 64
+
+/* ------------------------------------------------------------------------
+ * AllGather -> GEMM ("Triton-distributed Semantics", Kernel Design Patterns,
+ * "AllGather and GEMM Overlapping").
+ *
+ * R ranks each hold an A shard of shard_m x k bf16; B is k x n bf16.  The
+ * producer copies every shard s into rows [s*shard_m, (s+1)*shard_m) of
+ * `gathered` (the own shard too, so that gathered is the concatenation of
+ * all shards) and signals each flag unit; the consumer computes
+ * C = gathered @ B in fp32 as the units arrive.
+ *
+ * Flag units: a unit is a row panel of min(tile_m, shard_m) rows of one
+ * shard and a K-range of tiles_per_flag * tile_n columns (tiles_per_flag =
+ * 0: all of k); the last panel of a shard and the last K-range may be
+ * shorter.  Unit u = (shard * panels_per_shard + panel) * batches + batch;
+ * its slot is at byte u * flag_stride of `flags`.  Tiles of one panel that
+ * are always read together share one flag ("Triton-distributed Semantics",
+ * Best Practices: batch signals when possible).
+ *
+ * Consumer order: tiles whose rows are all the own rank's are computed
+ * first, straight from the own shard (they wait on nothing: Threadblock
+ * Swizzling, start on local data); the others follow in the order their
+ * first K-batch arrives under `producer_order`.
+ * ---------------------------------------------------------------------- */
+typedef struct ag_gemm_desc {
+  int32_t ranks;           /* R, 1..16 */
+  int32_t rank;            /* this rank, 0 <= rank < R */
+  int64_t shard_m;         /* rows per shard, >= 1 */
+  int64_t k;               /* >= 8, multiple of 8 */
+  int64_t n;               /* >= 8, multiple of 8 */
+  int32_t tile_m;          /* flag-unit rows (capped at shard_m), >= 1 */
+  int32_t tile_n;          /* K-tile width for tiles_per_flag, multiple of 8 */
+  int32_t tiles_per_flag;  /* K-tiles per flag unit, >= 0 (0 = all of k) */
+  int32_t flag_stride;     /* bytes between flag slots, multiple of 8, >= 8 */
+} ag_gemm_desc;
+
+typedef struct ag_gemm_plan_s* ag_gemm_plan_t;
+
+/* Validates `desc` and builds an immutable, host-only plan (thread-safe to
+ * share; touches no device).  Errors: EINVAL, ESHAPE, EALIGN; EUNSUPPORTED if R > 16 or the
+ * gathered row count exceeds 2^20. */
+ovl_status ag_gemm_plan(const ag_gemm_desc* desc, ag_gemm_plan_t* out);
+ovl_status ag_gemm_plan_destroy(ag_gemm_plan_t plan);
+
+int64_t ag_gemm_num_units(ag_gemm_plan_t plan);       /* R * panels_per_shard * batches */
+size_t ag_gemm_flags_bytes(ag_gemm_plan_t plan);      /* num_units * flag_stride */
+size_t ag_gemm_workspace_bytes(ag_gemm_plan_t plan);  /* >= OVL_ERROR_RECORD_BYTES */
+
+/* Consumer tiling of the plan: the kernel's output tile has
+ * ag_gemm_tile_rows(plan) rows, and there are ag_gemm_row_tiles(plan) rows
+ * of tiles. */
+int32_t ag_gemm_row_tiles(ag_gemm_plan_t plan);
+int32_t ag_gemm_tile_rows(ag_gemm_plan_t plan);
+
+/* The order in which consumers take rows of output tiles for a given
+ * producer order (HOST int32 [num_units] permutation, or NULL = ascending):
+ * writes ag_gemm_row_tiles(plan) row-tile indices to `out` (HOST).  Rows of
+ * tiles whose rows are all the own rank's come first (the pages' Threadblock
+ * Swizzling: each rank starts on its local data), then the others by the
+ * latest position, in the producer order, of a first-K-batch unit covering
+ * them; ties keep ascending index.  The device follows the same rule; this
+ * host copy exists to inspect and test the schedule.  Errors: EINVAL for a
+ * unit index out of range. */
+ovl_status ag_gemm_consumer_order(ag_gemm_plan_t plan, const int32_t* producer_order, int32_t* out);
+
+/* shards:   HOST array of R device pointers, bf16 [shard_m][k] each (read only).
+ * b:        bf16 [k][n] (read only).
+ * gathered: bf16 [R*shard_m][k], written by the producer (bit-exact copy).
+ * c:        fp32 [R*shard_m][n], written by the consumer.
+ * flags:    ag_gemm_flags_bytes(plan) bytes; unit slots are set to `epoch`.
+ * workspace: ag_gemm_workspace_bytes(plan) bytes, zeroed by ovl_flags_reset.
+ * producer_order: device int32 [num_units], a permutation of the unit
+ *           indices giving the order in which producers move units; NULL =
+ *           ascending.  Entries outside [0, num_units) are skipped; a unit
+ *           that never appears is never moved, and waits on it end in
+ *           OVL_ETIMEOUT.
+ * opts:     NULL = FUSED with defaults.
+ * In GEMM_ONLY mode `gathered` must already hold the gathered operand and
+ * neither flags nor shards other than the own one are read. */
+ovl_status ag_gemm_run(ag_gemm_plan_t plan, const void* const* shards, const void* b,
+                       void* gathered, float* c, int64_t* flags, void* workspace,
+                       int64_t epoch, const int32_t* producer_order,
+                       const ovl_opts* opts, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * GEMM -> ReduceScatter ("Triton-distributed Semantics", Kernel Design
+ * Patterns, "GEMM and ReduceScatter Overlapping").
+ *
+ * This rank computes its local product L = A @ B (A: m x k bf16, B: k x n
+ * bf16, fp32 result) whose m rows split into R blocks of m/R rows.  Block
+ * p != rank is a partial destined for rank p: each tile of it is stored to
+ * peer_out[p] and signalled in out_flags (put + signal).  For its own block
+ * the rank waits for every peer's partial tile (in_flags) and writes
+ *   out = L[rank block] + sum over p != rank, ascending, of peer_in[p]
+ * in fp32.  Tiles of peer blocks are computed first, starting at block
+ * rank+1; the own block comes last.
+ *
+ * Flag layout (both buffers): R rows of tiles_per_block slots, tile t of
+ * block p at byte (p * tiles_per_block + t) * flag_stride, with
+ * tiles_per_block = ceil((m/R) / tile_m) * ceil(n / tile_n) and tiles
+ * numbered row-major.  The own rank's row is never written.
+ * ---------------------------------------------------------------------- */
+typedef struct gemm_rs_desc {
+  int32_t ranks;        /* R, 1..16; m must be a multiple of R */
+  int32_t rank;
+  int64_t m, n, k;      /* n, k multiples of 8 */
+  int32_t tile_m;       /* flag tile: must be 256 */
+  int32_t tile_n;       /* flag tile: must be 256 */
+  int32_t flag_stride;  /* bytes, multiple of 8, >= 8 */
+} gemm_rs_desc;
+
+size_t gemm_rs_flags_bytes(const gemm_rs_desc* desc);      /* per flag buffer */
+size_t gemm_rs_workspace_bytes(const gemm_rs_desc* desc);
+
+/* a: bf16 [m][k]; b: bf16 [k][n].
+ * peer_out: HOST array[R] of fp32 [m/R][n] device buffers (entry `rank` ignored).
+ * peer_in:  HOST array[R] of fp32 [m/R][n] device buffers holding the peers'
+ *           partials for this rank's block (entry `rank` ignored), valid once
+ *           their in_flags slot reaches `epoch`.
+ * out:      fp32 [m/R][n].
+ * out_flags: written (epoch) per sent tile.  in_flags: read only.
+ * Errors as for ag_gemm_run; EUNSUPPORTED if tile_m/tile_n are not 256. */
+ovl_status gemm_rs_run(const gemm_rs_desc* desc, const void* a, const void* b,
+                       float* const* peer_out, const float* const* peer_in, float* out,
+                       int64_t* out_flags, const int64_t* in_flags, void* workspace,
+                       int64_t epoch, const ovl_opts* opts, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * All-to-all dispatch of routed tokens, then a grouped expert GEMM (the
+ * Aboleth README's all-to-all with one program per peer, which puts a slice
+ * at an offset indexed by the sender's rank and sets that sender's flag on
+ * the receiver; and its compiled MoE dispatch).
+ *
+ * This rank owns experts [rank*E, (rank+1)*E), E = experts_per_rank.
+ * Source s (every rank, this one included) sends, for each (token t,
+ * choice j) with topk_idx[s][t][j] in that range, a copy of token row t.
+ * Slice s of the receive buffers holds these rows ordered by (local expert,
+ * token id); it has room for cap = tokens * min(topk, E) rows.  When slice s
+ * is complete its flag is set to the epoch; the grouped GEMM waits on it and
+ * computes y[s][row] = recv_x[s][row] @ w[local expert of row] in fp32.
+ * Rows past a slice's count are never written (the caller zero-fills the
+ * receive buffers once).
+ * ---------------------------------------------------------------------- */
+typedef struct a2a_desc {
+  int32_t ranks;             /* R, 1..16 */
+  int32_t rank;
+  int64_t tokens;            /* tokens per source, 0..2^20 */
+  int64_t hidden;            /* multiple of 8 */
+  int64_t n;                 /* expert output width, multiple of 8 */
+  int32_t topk;              /* 1..8, distinct experts per token */
+  int32_t num_experts;       /* global experts = ranks * experts_per_rank */
+  int32_t experts_per_rank;  /* 1..64 */
+  int32_t flag_stride;       /* bytes, multiple of 8, >= 8 */
+} a2a_desc;
+
+size_t a2a_flags_bytes(const a2a_desc* desc);      /* ranks * flag_stride */
+size_t a2a_workspace_bytes(const a2a_desc* desc);
+
+/* x:        HOST array[R] of bf16 [tokens][hidden] device buffers.
+ * topk_idx: HOST array[R] of int32 [tokens][topk] device buffers (global expert ids;
+ *           ids outside [0, num_experts) are ignored).
+ * w:        bf16 [experts_per_rank][hidden][n].
+ * recv_x:   bf16 [R][cap][hidden];  recv_src: int32 [R][cap] source token ids;
+ * recv_count: int32 [R][experts_per_rank];  y: fp32 [R][cap][n].
+ * flags:    a2a_flags_bytes(desc) bytes, slot s = slice from source s. */
+ovl_status a2a_dispatch_grouped_gemm_run(const a2a_desc* desc, const void* const* x,
+                                         const int32_t* const* topk_idx, const void* w,
+                                         void* recv_x, int32_t* recv_src, int32_t* recv_count,
+                                         float* y, int64_t* flags, void* workspace,
+                                         int64_t epoch, const ovl_opts* opts,
+                                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Flags, errors, measurement.
+ * ---------------------------------------------------------------------- */
+
+/* Zeroes flag_bytes of `flags` and ws_bytes of `workspace` on `stream`
+ * (either pointer may be NULL with size 0) and restarts the epoch sequence
+ * of `flags` at 1.  Uses a fill kernel, not a memset node, so it may be
+ * captured in a graph. */
+ovl_status ovl_flags_reset(int64_t* flags, size_t flag_bytes, void* workspace, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* Waits for `stream`, then returns the status recorded on the device in
+ * `workspace` (OVL_OK or OVL_ETIMEOUT).  detail (HOST, may be NULL) receives
+ * {site, flag index, observed value, awaited value}. */
+ovl_status ovl_check(const void* workspace, int64_t* detail, hipStream_t stream);
+
+const char* ovl_strerror(ovl_status status);
+
+/* Plain 16-byte-vector copy of `bytes` bytes (a multiple of 16) from src to
+ * dst, with `blocks` workgroups (0 = default).  A reference point for the
+ * HBM roofline and for scaling hardware byte counters. */
+ovl_status ovl_copy(void* dst, const void* src, size_t bytes, int32_t blocks, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OVL_H_ */

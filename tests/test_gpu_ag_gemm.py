@@ -1,0 +1,215 @@
+"""GPU parity of the AllGather -> GEMM path against the oracle (through the C-ABI)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.conftest import gemm_tol
+from tests.gpu_util import dev, host, say, zeros_bytes, zeros_f32, zeros_u16, max_err
+
+pytestmark = pytest.mark.gpu
+
+
+def ovl():
+    from communication_overlap_amd import ovl as _o
+    return _o
+
+
+class AgCase:
+    def __init__(self, cfg, kind="normal", tiles_per_flag=0, flag_stride=8, rank=0):
+        o = ovl()
+        self.cfg = cfg
+        self.shards, self.b = synth.ag_inputs(cfg, kind)
+        self.plan = o.ag_gemm_plan(cfg.ranks, rank, cfg.shard_m, cfg.k, cfg.n, cfg.tile_m, cfg.tile_n,
+                                   tiles_per_flag, flag_stride)
+        self.units, self.panels, self.batches = oracle.ag_flag_units(cfg.ranks, cfg.shard_m, cfg.k, cfg.tile_m,
+                                                                     cfg.tile_n, tiles_per_flag)
+        assert self.plan.num_units == self.units
+        assert self.plan.flags_bytes == self.units * flag_stride
+        self.stride = flag_stride
+        self.d_shards = [dev(s) for s in self.shards]
+        self.d_b = dev(self.b)
+        self.g = zeros_u16(cfg.m, cfg.k)
+        self.c = zeros_f32(cfg.m, cfg.n)
+        self.flags = zeros_bytes(self.plan.flags_bytes)
+        self.ws = zeros_bytes(self.plan.workspace_bytes)
+        o.ovl_flags_reset(self.flags, self.plan.flags_bytes, self.ws, self.plan.workspace_bytes)
+
+    def order(self, epoch, kind="panels"):
+        return synth.producer_order(self.cfg.seed, epoch, self.cfg.ranks * self.panels, self.batches, True, kind)
+
+    def run(self, epoch, order=None, mode=0, producers=0, spin_limit=0):
+        o = ovl()
+        d_order = dev(order) if order is not None else None
+        say(f"  ag_gemm_run {self.cfg.name} epoch={epoch} mode={mode} order={'none' if order is None else 'set'}")
+        o.ag_gemm_run(self.plan, self.d_shards, self.d_b, self.g, self.c, self.flags, self.ws, epoch, d_order,
+                      mode=mode, producers=producers, spin_limit=spin_limit)
+        return o.ovl_check(self.ws, raise_on_error=False)
+
+    def check_gathered_and_flags(self, epoch):
+        g = host(self.g, np.uint16)
+        assert np.array_equal(g, oracle.all_gather(self.shards)), "gathered != concatenation of shards"
+        fl = host(self.flags)[: self.plan.flags_bytes]
+        assert np.array_equal(fl, oracle.expected_flags(self.units, self.stride, epoch)), "flag bytes differ"
+
+
+def _full_check(case):
+    g_ref, c_ref = oracle.ag_gemm(case.shards, case.b)
+    c = host(case.c)
+    tol = gemm_tol(case.cfg.k, float(np.abs(c_ref).max()))
+    err = max_err(c, c_ref)
+    assert err <= tol, f"max err {err} > tol {tol}"
+    return c
+
+
+def _small(name, R, Ms, K, N, tm, tn, seed=5):
+    return synth.AgGemmCfg(name, R, Ms, K, N, tm, tn, 1.0, 1.0 / 16, seed, True)
+
+
+# ------------------------------------------------------------------ small / ragged
+
+def test_small_fused_matches_oracle():
+    case = AgCase(synth.CONFIGS["ag_r2_128x256x256"])
+    st, det = case.run(1)
+    assert st == 0, det
+    case.check_gathered_and_flags(1)
+    _full_check(case)
+
+
+@pytest.mark.parametrize("mode", [0, 3])
+def test_small_integers_bit_exact(mode):
+    case = AgCase(synth.CONFIGS["ag_r2_128x256x256"], "smallint")
+    st, det = case.run(1, mode=mode)
+    assert st == 0, det
+    _, c_ref = oracle.ag_gemm(case.shards, case.b)
+    assert np.array_equal(host(case.c), c_ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("shape", [
+    # R, shard_m, K, N, tile_m, tile_n, tiles_per_flag
+    (3, 100, 200, 136, 48, 40, 2),   # ragged panels, ragged K-batch, ragged N tile
+    (2, 300, 520, 264, 256, 64, 1),  # 256-row panels with a short last panel
+    (5, 16, 64, 8, 128, 32, 0),      # shards shorter than the tile: unit = whole shard
+    (1, 129, 8, 16, 64, 8, 1),       # one rank, K of one vector
+])
+def test_ragged_shapes_match_oracle(shape):
+    R, Ms, K, N, tm, tn, tpf = shape
+    cfg = _small("ragged", R, Ms, K, N, tm, tn)
+    case = AgCase(cfg, tiles_per_flag=tpf)
+    order = case.order(1, "units")
+    st, det = case.run(1, order)
+    assert st == 0, det
+    case.check_gathered_and_flags(1)
+    _full_check(case)
+
+
+def test_epochs_reuse_flags_without_reset():
+    case = AgCase(synth.CONFIGS["ag_r2_128x256x256"], tiles_per_flag=2, flag_stride=128)
+    first = None
+    for epoch in range(1, 6):
+        st, det = case.run(epoch, case.order(epoch, "units"))
+        assert st == 0, det
+        case.check_gathered_and_flags(epoch)
+        c = host(case.c).copy()
+        if first is None:
+            first = c
+            _full_check(case)
+        assert np.array_equal(c.view(np.uint32), first.view(np.uint32)), "C bits changed with producer order"
+
+
+def test_epoch_rules():
+    o = ovl()
+    case = AgCase(synth.CONFIGS["ag_r2_128x256x256"])
+    with pytest.raises(o.OvlError) as e:
+        case.run(0)
+    assert e.value.status == o.OVL_EEPOCH
+    assert case.run(3)[0] == 0
+    for bad in (3, 2):
+        with pytest.raises(o.OvlError) as e:
+            case.run(bad)
+        assert e.value.status == o.OVL_EEPOCH
+    o.ovl_flags_reset(case.flags, case.plan.flags_bytes, case.ws, case.plan.workspace_bytes)
+    assert case.run(1)[0] == 0
+    case.check_gathered_and_flags(1)
+
+
+def test_missing_unit_times_out():
+    # A producer order that repeats one unit and omits another leaves the
+    # omitted unit unsignalled: its waiters must give up with OVL_ETIMEOUT.
+    o = ovl()
+    case = AgCase(synth.CONFIGS["ag_r2_128x256x256"])
+    order = np.arange(case.units, dtype=np.int32)
+    missing = case.units - 1
+    order[missing] = 0
+    st, det = case.run(1, order, spin_limit=2000)
+    assert st == o.OVL_ETIMEOUT
+    assert det[1] == missing and det[3] == 1
+
+
+def test_modes_compose_to_the_same_bits():
+    o = ovl()
+    cfg = _small("modes", 4, 192, 384, 320, 64, 64)
+    case = AgCase(cfg, tiles_per_flag=2)
+    assert case.run(1, case.order(1))[0] == 0
+    fused = host(case.c).copy()
+    case.c.zero_()
+    assert case.run(2, mode=o.MODE_BARRIER)[0] == 0
+    assert np.array_equal(host(case.c).view(np.uint32), fused.view(np.uint32))
+    case.c.zero_()
+    case.g.zero_()
+    assert case.run(3, case.order(3), mode=o.MODE_COPY_ONLY)[0] == 0
+    case.check_gathered_and_flags(3)
+    assert case.run(4, mode=o.MODE_GEMM_ONLY)[0] == 0
+    assert np.array_equal(host(case.c).view(np.uint32), fused.view(np.uint32))
+    _full_check(case)
+
+
+# ------------------------------------------------------------------ full sizes
+
+def _sampled_check(case, count=1500, seed=0, exact=False):
+    cfg = case.cfg
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, cfg.m, count)
+    cols = rng.integers(0, cfg.n, count)
+    g = oracle.all_gather(case.shards)
+    ref = oracle.gemm_entries(g, case.b, rows, cols)
+    got = host(case.c)[rows, cols].astype(np.float64)
+    if exact:
+        assert np.array_equal(got, ref)
+    else:
+        # max|ref| over the sample stands in for the full max (never larger).
+        tol = gemm_tol(cfg.k, float(np.abs(ref).max()))
+        assert max_err(got, ref) <= tol
+
+
+@pytest.mark.parametrize("name,tpf", [("ag_r8_8192x3584x4096", 1), ("ag_r8_skinny_128x7168x8192", 4)])
+def test_full_size_random_orders_and_modes(name, tpf):
+    o = ovl()
+    cfg = synth.CONFIGS[name]
+    case = AgCase(cfg, tiles_per_flag=tpf)
+    bits = None
+    for epoch in range(1, 4):
+        st, det = case.run(epoch, case.order(epoch))
+        assert st == 0, det
+        case.check_gathered_and_flags(epoch)
+        c = host(case.c)
+        if bits is None:
+            bits = c.view(np.uint32).copy()
+            _sampled_check(case)
+        else:
+            assert np.array_equal(c.view(np.uint32), bits)
+    case.c.zero_()
+    assert case.run(4, mode=o.MODE_BARRIER)[0] == 0
+    assert np.array_equal(host(case.c).view(np.uint32), bits)
+    case.c.zero_()
+    assert case.run(5, mode=o.MODE_GEMM_ONLY)[0] == 0
+    assert np.array_equal(host(case.c).view(np.uint32), bits)
+
+
+def test_full_size_small_integers_exact():
+    cfg = synth.CONFIGS["ag_r8_8192x3584x4096"]
+    case = AgCase(cfg, "smallint", tiles_per_flag=1)
+    st, det = case.run(1, case.order(1))
+    assert st == 0, det
+    _sampled_check(case, count=3000, exact=True)

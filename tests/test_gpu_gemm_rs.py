@@ -1,0 +1,126 @@
+"""GPU parity of the GEMM -> ReduceScatter path against the oracle (through the C-ABI)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.conftest import gemm_tol
+from tests.gpu_util import dev, host, say, zeros_bytes, zeros_f32, max_err
+
+pytestmark = pytest.mark.gpu
+
+
+def ovl():
+    from communication_overlap_amd import ovl as _o
+    return _o
+
+
+class RsCase:
+    def __init__(self, cfg, kind="normal"):
+        o = ovl()
+        self.cfg = cfg
+        self.a, self.b, self.parts = synth.rs_inputs(cfg, kind)
+        R, bm = cfg.ranks, cfg.block_m
+        self.desc = o.gemm_rs_desc(R, cfg.rank, cfg.m, cfg.n, cfg.k, 256, 256, 8)
+        self.fbytes = o.gemm_rs_flags_bytes(self.desc)
+        self.tpb = self.fbytes // 8 // R
+        self.d_a, self.d_b = dev(self.a), dev(self.b)
+        self.peer_out = [None if p == cfg.rank else zeros_f32(bm, cfg.n) for p in range(R)]
+        self.peer_in = [None if p == cfg.rank else dev(self.parts[p]) for p in range(R)]
+        self.out = zeros_f32(bm, cfg.n)
+        self.out_flags = zeros_bytes(self.fbytes)
+        self.in_flags = zeros_bytes(self.fbytes)
+        self.ws = zeros_bytes(o.gemm_rs_workspace_bytes(self.desc))
+        o.ovl_flags_reset(self.out_flags, self.fbytes, self.ws, self.ws.numel())
+
+    def set_in_flags(self, epoch):
+        v = self.in_flags.view(dtype=__import__("torch").int64).view(self.cfg.ranks, self.tpb)
+        v.fill_(epoch)
+        v[self.cfg.rank].zero_()
+
+    def run(self, epoch, mode=0, spin_limit=0):
+        o = ovl()
+        say(f"  gemm_rs_run {self.cfg.name} epoch={epoch} mode={mode}")
+        o.gemm_rs_run(self.desc, self.d_a, self.d_b, self.peer_out, self.peer_in, self.out, self.out_flags,
+                      self.in_flags, self.ws, epoch, mode=mode, spin_limit=spin_limit)
+        return o.ovl_check(self.ws, raise_on_error=False)
+
+
+def _small(R=4, rank=1, bm=300, n=264, k=200, seed=9):
+    return synth.GemmRsCfg("rs_small", R, R * bm, k, n, 256, 256, 1.0, 0.25, 1.0, seed, rank)
+
+
+def test_small_ragged_matches_oracle():
+    cfg = _small()
+    case = RsCase(cfg)
+    case.set_in_flags(1)
+    st, det = case.run(1)
+    assert st == 0, det
+    loc, outb, own = oracle.gemm_rs(case.a, case.b, case.parts, cfg.rank, cfg.ranks)
+    tol = gemm_tol(cfg.k, float(np.abs(loc).max()))
+    for p in range(cfg.ranks):
+        if p != cfg.rank:
+            assert max_err(host(case.peer_out[p]), outb[p]) <= tol
+    assert max_err(host(case.out), own) <= gemm_tol(cfg.k, float(np.abs(own).max()))
+    fl = host(case.out_flags)[: case.fbytes]
+    assert np.array_equal(fl, oracle.rs_expected_flags(cfg.ranks, cfg.rank, case.tpb, 8, 1))
+
+
+def test_small_integers_bit_exact():
+    cfg = _small(R=8, rank=0, bm=256, n=512, k=320)
+    case = RsCase(cfg, "smallint")
+    case.set_in_flags(1)
+    assert case.run(1)[0] == 0
+    loc, outb, own = oracle.gemm_rs(case.a, case.b, case.parts, cfg.rank, cfg.ranks)
+    assert np.array_equal(host(case.out), own.astype(np.float32))
+    for p in range(1, 8):
+        assert np.array_equal(host(case.peer_out[p]), outb[p].astype(np.float32))
+
+
+def test_single_rank_is_plain_gemm():
+    cfg = _small(R=1, rank=0, bm=520, n=136, k=64)
+    case = RsCase(cfg)
+    st, det = case.run(1)
+    assert st == 0, det
+    ref = oracle.gemm(case.a, case.b)
+    assert max_err(host(case.out), ref) <= gemm_tol(cfg.k, float(np.abs(ref).max()))
+
+
+def test_withheld_partial_times_out():
+    o = ovl()
+    cfg = _small()
+    case = RsCase(cfg)
+    case.set_in_flags(1)
+    v = case.in_flags.view(dtype=__import__("torch").int64).view(cfg.ranks, case.tpb)
+    v[3, 2] = 0  # peer 3 never sent tile 2 of this rank's block
+    st, det = case.run(1, spin_limit=2000)
+    assert st == o.OVL_ETIMEOUT
+    assert det[1] == 3 * case.tpb + 2
+
+
+def test_full_size_sampled():
+    cfg = synth.CONFIGS["rs_r8_8192x4096x1792"]
+    case = RsCase(cfg)
+    case.set_in_flags(1)
+    st, det = case.run(1)
+    assert st == 0, det
+    rng = np.random.default_rng(1)
+    bm = cfg.block_m
+    rows = rng.integers(0, bm, 600)
+    cols = rng.integers(0, cfg.n, 600)
+    # own block (rank 0): product rows of block 0 plus the peers' partials
+    ref_own = oracle.gemm_entries(case.a, case.b, rows, cols)
+    for p in range(1, cfg.ranks):
+        ref_own = ref_own + case.parts[p][rows, cols].astype(np.float64)
+    got = host(case.out)[rows, cols]
+    assert max_err(got, ref_own) <= gemm_tol(cfg.k, float(np.abs(ref_own).max()))
+    for p in (1, 4, 7):
+        ref = oracle.gemm_entries(case.a, case.b, rows + p * bm, cols)
+        got = host(case.peer_out[p])[rows, cols]
+        assert max_err(got, ref) <= gemm_tol(cfg.k, float(np.abs(ref).max()))
+    fl = host(case.out_flags)[: case.fbytes]
+    assert np.array_equal(fl, oracle.rs_expected_flags(cfg.ranks, cfg.rank, case.tpb, 8, 1))
+    first = host(case.out).view(np.uint32).copy()
+    assert case.run(2, mode=ovl().MODE_GEMM_ONLY)[0] == 0
+    assert np.array_equal(host(case.out).view(np.uint32), first)
