@@ -1,0 +1,288 @@
+"""Benchmark of the tile-overlap hot path on one MI355X.
+
+A step is one fused AllGather -> GEMM (producer copy + per-unit flags +
+consumer MFMA GEMM, one persistent launch) on the R=8 workload: shards of
+1024 x 4096 bf16 N(0,1) per rank (gathered M = 8192), B 4096 x 3584 bf16
+N(0, 0.02^2), 256 x 256 tiles, one flag per (256-row panel, 256-column K-tile),
+a new seeded random producer order every epoch, epochs increasing without
+reset.  Prints one JSON line.
+
+Beside the headline number it measures, each with the 256 MB last-level
+cache flushed before every repetition: copy-only and GEMM-only times of the
+same launch (for overlap efficiency), the GEMM -> ReduceScatter and skinny
+AllGather -> GEMM workloads, and the CPU oracle on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, published
+METRIC = "fused AG-GEMM TFLOP/s (% bf16 MFMA peak) + overlap eff. vs copy+GEMM serial"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+class Flusher:
+    """Writes 512 MiB so that no operand is served from the 256 MB cache."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def __call__(self):
+        self.buf.zero_()
+
+
+def timed_reps(fn, reps, flush=None):
+    """Median / p10 / p90 of fn's device time in microseconds (HIP events on
+    the current stream around fn only)."""
+    import torch
+    times = []
+    for _ in range(reps):
+        if flush:
+            flush()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    t = np.array(times)
+    return {"median_us": float(np.median(t)), "p10_us": float(np.percentile(t, 10)),
+            "p90_us": float(np.percentile(t, 90))}
+
+
+class AgBench:
+    def __init__(self, cfg, tiles_per_flag):
+        import torch
+        import synth
+        from communication_overlap_amd import ovl
+        self.ovl = ovl
+        self.cfg = cfg
+        shards, b = synth.ag_inputs(cfg)
+        self.plan = ovl.ag_gemm_plan(cfg.ranks, 0, cfg.shard_m, cfg.k, cfg.n, cfg.tile_m, cfg.tile_n,
+                                     tiles_per_flag, 8)
+        units = self.plan.num_units
+        pps = -(-cfg.shard_m // min(cfg.tile_m, cfg.shard_m))  # panels per shard
+        batches = units // (cfg.ranks * pps)
+        self.d_shards = [dev(s) for s in shards]
+        self.d_b = dev(b)
+        self.g = torch.zeros(cfg.m, cfg.k, dtype=torch.int16, device="cuda")
+        self.c = torch.zeros(cfg.m, cfg.n, dtype=torch.float32, device="cuda")
+        self.flags = torch.zeros(self.plan.flags_bytes, dtype=torch.uint8, device="cuda")
+        self.ws = torch.zeros(self.plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+        ovl.ovl_flags_reset(self.flags, self.plan.flags_bytes, self.ws, self.plan.workspace_bytes)
+        n_panels = cfg.ranks * pps
+        self.orders = [dev(synth.producer_order(cfg.seed, e, n_panels, batches, cfg.random_order))
+                       for e in range(1, 6)]
+        self.epoch = 0
+
+    def run(self, mode=0, producers=0):
+        self.epoch += 1
+        self.ovl.ag_gemm_run(self.plan, self.d_shards, self.d_b, self.g, self.c, self.flags, self.ws,
+                             self.epoch, self.orders[(self.epoch - 1) % 5], mode=mode, producers=producers)
+
+    def check(self):
+        st, det = self.ovl.ovl_check(self.ws, raise_on_error=False)
+        if st != 0:
+            raise RuntimeError(f"device error {st} {det}")
+
+
+def cpu_baseline(cfg):
+    """The oracle (gather + float64 GEMM) on the full workload, on host cores."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    shards, b = synth.ag_inputs(cfg)
+    t0 = time.perf_counter()
+    g, c = oracle.ag_gemm(shards, b)
+    dt = time.perf_counter() - t0
+    return {"value": cfg.flops() / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"the whole {cfg.m}x{cfg.n}x{cfg.k} workload: gather + float64 GEMM, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=20, help="repetitions of each side measurement")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the side workloads")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the other ranks "
+              "are emulated as buffers in the same HBM)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from communication_overlap_amd import ovl
+
+    torch.cuda.set_device(0)
+    ovl.lib()
+    cfg = synth.CONFIGS["ag_r8_8192x3584x4096"]
+    log(f"[bench] inputs {cfg.name}")
+    ag = AgBench(cfg, tiles_per_flag=1)
+    flush = Flusher()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        ag.run()
+    ag.check()
+
+    log(f"[bench] timing {args.steps} fused steps")
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        ag.run()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ag.check()
+    kern_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+    value = cfg.flops() / (wall / args.steps) / 1e12
+    achieved = cfg.flops() / (kern_us * 1e-6) / 1e12
+
+    log("[bench] overlap: fused / copy-only / gemm-only, cache flushed")
+    fused = timed_reps(lambda: ag.run(ovl.MODE_FUSED), args.reps, flush)
+    copy_only = timed_reps(lambda: ag.run(ovl.MODE_COPY_ONLY), args.reps, flush)
+    gemm_only = timed_reps(lambda: ag.run(ovl.MODE_GEMM_ONLY), args.reps, flush)
+    ag.check()
+    copy_bytes = 2 * cfg.m * cfg.k * 2
+    overlap = {
+        "fused_us": fused, "copy_only_us": copy_only, "gemm_only_us": gemm_only,
+        "fused_over_copy_plus_gemm": fused["median_us"] / (copy_only["median_us"] + gemm_only["median_us"]),
+        "fused_over_gemm_only": fused["median_us"] / gemm_only["median_us"],
+        "copy_only_GBps": copy_bytes / (copy_only["median_us"] * 1e-6) / 1e9,
+        "gemm_only_TFLOPs": cfg.flops() / (gemm_only["median_us"] * 1e-6) / 1e12,
+        "fused_flushed_TFLOPs": cfg.flops() / (fused["median_us"] * 1e-6) / 1e12,
+    }
+
+    extra = {}
+    if not args.no_extra:
+        extra = side_workloads(args.reps, flush)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "AG-GEMM R=8 emulated ranks, A shard 1024x4096 bf16 N(0,1) per rank "
+                               "(M=8192), B 4096x3584 bf16 N(0,0.02), tile 256x256, seeded random producer "
+                               "order, epochs increasing on one flag buffer",
+                   "m": cfg.m, "n": cfg.n, "k": cfg.k, "ranks": cfg.ranks, "tile": [cfg.tile_m, cfg.tile_n],
+                   "tiles_per_flag": 1},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "ag_gemm_kernel<256,256,fused>", "avg_launch_us": round(kern_us, 2)},
+        "overlap": overlap,
+        "side": extra,
+    }
+    if not args.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+def side_workloads(reps, flush):
+    import torch
+    import synth
+    from communication_overlap_amd import ovl
+    res = {}
+
+    # Skinny decode-like AllGather -> GEMM (HBM bound: B is 117 MB).
+    cfg = synth.CONFIGS["ag_r8_skinny_128x7168x8192"]
+    log(f"[bench] side {cfg.name}")
+    sk = AgBench(cfg, tiles_per_flag=4)
+    sk.run()
+    t = timed_reps(lambda: sk.run(), reps, flush)
+    gemm = timed_reps(lambda: sk.run(ovl.MODE_GEMM_ONLY), reps, flush)
+    copy = timed_reps(lambda: sk.run(ovl.MODE_COPY_ONLY), reps, flush)
+    sk.check()
+    bytes_min = cfg.k * cfg.n * 2 + 2 * cfg.m * cfg.k * 2 + cfg.m * cfg.n * 4
+    res[cfg.name] = {"fused_us": t, "gemm_only_us": gemm, "copy_only_us": copy,
+                     "GBps": bytes_min / (t["median_us"] * 1e-6) / 1e9,
+                     "pct_of_hbm_peak": 100 * bytes_min / (t["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                     "TFLOPs": cfg.flops() / (t["median_us"] * 1e-6) / 1e12}
+    del sk
+
+    # GEMM -> ReduceScatter.
+    cfg = synth.CONFIGS["rs_r8_8192x4096x1792"]
+    log(f"[bench] side {cfg.name}")
+    a, b, parts = synth.rs_inputs(cfg)
+    desc = ovl.gemm_rs_desc(cfg.ranks, 0, cfg.m, cfg.n, cfg.k)
+    fb = ovl.gemm_rs_flags_bytes(desc)
+    bm = cfg.block_m
+    d_a, d_b = dev(a), dev(b)
+    peer_out = [None] + [torch.zeros(bm, cfg.n, device="cuda") for _ in range(1, cfg.ranks)]
+    peer_in = [None] + [dev(parts[p]) for p in range(1, cfg.ranks)]
+    out = torch.zeros(bm, cfg.n, device="cuda")
+    out_flags = torch.zeros(fb, dtype=torch.uint8, device="cuda")
+    in_flags = torch.zeros(fb, dtype=torch.uint8, device="cuda")
+    in_flags.view(torch.int64).fill_(1 << 40)
+    ws = torch.zeros(ovl.gemm_rs_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    ovl.ovl_flags_reset(out_flags, fb, ws, ws.numel())
+    ep = [0]
+
+    def rs(mode=0):
+        ep[0] += 1
+        ovl.gemm_rs_run(desc, d_a, d_b, peer_out, peer_in, out, out_flags, in_flags, ws, ep[0], mode=mode)
+
+    rs()
+    t = timed_reps(rs, reps, flush)
+    g = timed_reps(lambda: rs(ovl.MODE_GEMM_ONLY), reps, flush)
+    ovl.ovl_check(ws)
+    res[cfg.name] = {"fused_us": t, "gemm_only_us": g,
+                     "TFLOPs": cfg.flops() / (t["median_us"] * 1e-6) / 1e12,
+                     "pct_of_bf16_peak": 100 * cfg.flops() / (t["median_us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
+
+    # Plain copy, for the HBM reference point.
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    t = timed_reps(lambda: ovl.ovl_copy(dst, src, src.numel()), reps, flush)
+    res["plain_copy_256MiB"] = {"us": t, "GBps": 2 * src.numel() / (t["median_us"] * 1e-6) / 1e9}
+    return res
+
+
+if __name__ == "__main__":
+    main()

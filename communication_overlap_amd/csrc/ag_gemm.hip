@@ -299,7 +299,10 @@ extern "C" ovl_status ag_gemm_plan(const ag_gemm_desc* d, ag_gemm_plan_t* out) {
   if (d->k % 8 || d->n % 8 || d->tile_n % 8) return OVL_EALIGN;
   if (d->flag_stride < 8 || d->flag_stride % 8) return OVL_EALIGN;
   const int64_t m = (int64_t)d->ranks * d->shard_m;
-  if (m > (1 << 20) || d->k > (1 << 24) || d->n > (1 << 24)) return OVL_EUNSUPPORTED;
+  // Every operand below 1 GiB and rows below 2^20 elements: buffer offsets stay in 32 bits.
+  if (m > (1 << 20) || d->k > (1 << 20) || d->n > (1 << 20) || m * d->k * 2 > (1ll << 30) ||
+      d->k * d->n * 2 > (1ll << 30) || m * d->n * 4 > (1ll << 30))
+    return OVL_EUNSUPPORTED;
 
   ag_gemm_plan_s* p = new (std::nothrow) ag_gemm_plan_s();
   if (!p) return OVL_EINVAL;

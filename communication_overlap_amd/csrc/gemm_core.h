@@ -12,6 +12,11 @@
 // LDS rows are padded by 16 bytes (pitch 144 B), which spreads the 16-byte
 // fragment reads and the staging writes over all banks.
 //
+// Global traffic goes through buffer resources whose size ends exactly at
+// the tile's last valid row: loads past it return zero and stores past it
+// are dropped by the hardware, so ragged M and K tails cost no branches;
+// columns past N get an out-of-range offset once per tile.
+//
 // Accumulation order of every output element is fixed: K ascending in steps
 // of 16 (one MFMA each), whatever the order tiles or flags arrive in.
 #pragma once
@@ -22,6 +27,31 @@ namespace ovl {
 
 constexpr int kBK = 64;        // K per pipeline stage
 constexpr int kKP = kBK + 8;   // LDS row pitch in bf16 elements
+constexpr uint32_t kOOB = 0x80000000u;  // an offset past every buffer (operands are < 2 GiB)
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over [base, base + bytes); bytes is clamped to [0, 2^31 - 1].
+__device__ inline rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+__device__ inline u32x4 bload128(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ inline u32x2 bload64(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
+__device__ inline uint32_t bload32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ inline float bloadf(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ inline void bstoref(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
+}
 
 template <int BM, int BN>
 struct TileCfg {
@@ -50,6 +80,24 @@ struct BRow<4> { u32x2 d; };
 template <>
 struct BRow<2> { uint32_t d; };
 
+template <int BV>
+__device__ inline BRow<BV> load_brow(rsrc_t r, uint32_t off);
+template <>
+__device__ inline BRow<8> load_brow<8>(rsrc_t r, uint32_t off) { return {bload128(r, off)}; }
+template <>
+__device__ inline BRow<4> load_brow<4>(rsrc_t r, uint32_t off) { return {bload64(r, off)}; }
+template <>
+__device__ inline BRow<2> load_brow<2>(rsrc_t r, uint32_t off) { return {bload32(r, off)}; }
+
+template <int BV>
+__device__ inline uint32_t brow_word(const BRow<BV>& r, int w);
+template <>
+__device__ inline uint32_t brow_word<8>(const BRow<8>& r, int w) { return r.d[w]; }
+template <>
+__device__ inline uint32_t brow_word<4>(const BRow<4>& r, int w) { return r.d[w]; }
+template <>
+__device__ inline uint32_t brow_word<2>(const BRow<2>& r, int) { return r.d; }
+
 template <int BM, int BN>
 struct Stage {
   u32x4 a[TileCfg<BM, BN>::AV];
@@ -69,50 +117,46 @@ struct Operands {
   int64_t k;
 };
 
-template <int BV>
-__device__ inline BRow<BV> load_brow(const uint16_t* p);
-template <>
-__device__ inline BRow<8> load_brow<8>(const uint16_t* p) { return {*reinterpret_cast<const u32x4*>(p)}; }
-template <>
-__device__ inline BRow<4> load_brow<4>(const uint16_t* p) { return {*reinterpret_cast<const u32x2*>(p)}; }
-template <>
-__device__ inline BRow<2> load_brow<2>(const uint16_t* p) { return {*reinterpret_cast<const uint32_t*>(p)}; }
-
-template <int BV>
-__device__ inline uint32_t brow_word(const BRow<BV>& r, int w);
-template <>
-__device__ inline uint32_t brow_word<8>(const BRow<8>& r, int w) { return r.d[w]; }
-template <>
-__device__ inline uint32_t brow_word<4>(const BRow<4>& r, int w) { return r.d[w]; }
-template <>
-__device__ inline uint32_t brow_word<2>(const BRow<2>& r, int w) { return r.d; }
-
-// Global -> registers for the K-step starting at k0 (tile rows start at m0 of A).
+// Per-tile, per-lane addressing of the global loads.
 template <int BM, int BN>
-__device__ inline void stage_load(Stage<BM, BN>& st, const Operands& op, int64_t m0, int64_t k0) {
+struct TileAddr {
+  rsrc_t ra, rb;
+  uint32_t a_off;   // this lane's A offset at k0 = 0 for vector v = 0 (bytes)
+  uint32_t a_vstep; // bytes between the rows of consecutive A vectors (32 rows)
+  uint32_t b_off;   // this lane's B offset at k0 = 0, or kOOB for columns past N
+  uint32_t ldb_b;   // B row pitch in bytes
+  int32_t k;
+  int32_t kchunk;   // this lane's K offset within a stage (elements)
+};
+
+template <int BM, int BN>
+__device__ inline TileAddr<BM, BN> tile_addr(const Operands& op, int64_t m0) {
   using C = TileCfg<BM, BN>;
-  const int t = threadIdx.x;
-  const int chunk = t & 7;
-  const int64_t kc = k0 + chunk * 8;
+  TileAddr<BM, BN> t;
+  const int tid = threadIdx.x;
+  t.ra = make_rsrc(op.a + m0 * op.lda, (op.m_valid - m0) * op.lda * 2);
+  t.rb = make_rsrc(op.b + op.n0, op.k * op.ldb * 2 - op.n0 * 2);
+  t.kchunk = (tid & 7) * 8;
+  t.a_off = (uint32_t)(((tid >> 3) * op.lda + t.kchunk) * 2);
+  t.a_vstep = (uint32_t)(32 * op.lda * 2);
+  const int kb = (tid & 7) * 8;
+  const int nb = (tid >> 3) * C::BV;
+  t.ldb_b = (uint32_t)(op.ldb * 2);
+  t.b_off = (op.n0 + nb < op.n_valid) ? (uint32_t)(kb * op.ldb * 2 + nb * 2) : kOOB;
+  t.k = (int32_t)op.k;
+  return t;
+}
+
+// Global -> registers for the K-step starting at k0.
+template <int BM, int BN>
+__device__ inline void stage_load(Stage<BM, BN>& st, const TileAddr<BM, BN>& t, int32_t k0) {
+  using C = TileCfg<BM, BN>;
+  const uint32_t abase = (k0 + t.kchunk < t.k) ? t.a_off + (uint32_t)k0 * 2 : kOOB;
 #pragma unroll
-  for (int v = 0; v < C::AV; ++v) {
-    const int64_t r = m0 + v * 32 + (t >> 3);
-    if (r < op.m_valid && kc < op.k)
-      st.a[v] = ld16(op.a + r * op.lda + kc);
-    else
-      st.a[v] = u32x4{0, 0, 0, 0};
-  }
-  const int kb = (t & 7) * 8;
-  const int64_t n = op.n0 + (t >> 3) * C::BV;
-  const bool nvalid = n < op.n_valid;
+  for (int v = 0; v < C::AV; ++v) st.a[v] = bload128(t.ra, abase + v * t.a_vstep);
+  const uint32_t bbase = t.b_off + (uint32_t)k0 * t.ldb_b;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t k = k0 + kb + i;
-    if (nvalid && k < op.k)
-      st.b[i] = load_brow<C::BV>(op.b + k * op.ldb + n);
-    else
-      st.b[i] = BRow<C::BV>{};
-  }
+  for (int i = 0; i < 8; ++i) st.b[i] = load_brow<C::BV>(t.rb, bbase + i * t.ldb_b);
 }
 
 // Registers -> LDS stage buffer (B transposed to [n][k]).
@@ -143,9 +187,51 @@ __device__ inline void stage_store(const Stage<BM, BN>& st, uint16_t* lds_stage)
   }
 }
 
-// MFMA over one LDS stage (4 sub-steps of K=16).
 template <int BM, int BN>
-__device__ inline void stage_compute(Acc<BM, BN>& acc, const uint16_t* lds_stage) {
+struct Frags {
+  bf16x8 a[TileCfg<BM, BN>::FM];
+  bf16x8 b[TileCfg<BM, BN>::FN];
+};
+
+template <int BM, int BN>
+__device__ inline void load_frags(Frags<BM, BN>& f, const uint16_t* la, const uint16_t* lb, int kk) {
+  using C = TileCfg<BM, BN>;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+    f.a[fm] = *reinterpret_cast<const bf16x8*>(la + fm * 32 * kKP + kk * 16);
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn)
+    f.b[fn] = *reinterpret_cast<const bf16x8*>(lb + fn * 32 * kKP + kk * 16);
+}
+
+template <int BM, int BN>
+__device__ inline void mfma_frags(Acc<BM, BN>& acc, const Frags<BM, BN>& f) {
+  using C = TileCfg<BM, BN>;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+      acc.v[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[fm], f.b[fn], acc.v[fm][fn], 0, 0, 0);
+}
+
+// Keeps the compiler from treating x as loop-invariant (the value is
+// unchanged), so that address arithmetic built on it is not hoisted out of
+// the persistent tile loop and kept live in hundreds of registers.
+__device__ inline uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
+#define OVL_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// MFMA over one LDS stage (4 sub-steps of K=16), fragments double-buffered
+// so that the LDS reads of sub-step kk+1 are in flight during the MFMAs of
+// kk.  The scheduling fences keep that pipeline shape.  When `next` is not
+// null, the next stage's registers are written to it during the last
+// sub-step, under the MFMAs.
+template <int BM, int BN>
+__device__ inline void stage_compute(Acc<BM, BN>& acc, const uint16_t* lds_stage, const Stage<BM, BN>* st,
+                                     uint16_t* next) {
   using C = TileCfg<BM, BN>;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
@@ -153,21 +239,21 @@ __device__ inline void stage_compute(Acc<BM, BN>& acc, const uint16_t* lds_stage
   const int wn = (wave & 1) * (BN / 2);
   const uint16_t* la = lds_stage + (wm + (lane & 31)) * kKP + (lane >> 5) * 8;
   const uint16_t* lb = lds_stage + C::A_ELEMS + (wn + (lane & 31)) * kKP + (lane >> 5) * 8;
-#pragma unroll
-  for (int kk = 0; kk < kBK / 16; ++kk) {
-    bf16x8 af[C::FM], bfr[C::FN];
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
-      af[fm] = *reinterpret_cast<const bf16x8*>(la + fm * 32 * kKP + kk * 16);
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
-      bfr[fn] = *reinterpret_cast<const bf16x8*>(lb + fn * 32 * kKP + kk * 16);
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-        acc.v[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc.v[fm][fn], 0, 0, 0);
-  }
+  Frags<BM, BN> f0, f1;
+  load_frags(f0, la, lb, 0);
+  OVL_SCHED_FENCE();
+  load_frags(f1, la, lb, 1);
+  mfma_frags(acc, f0);
+  OVL_SCHED_FENCE();
+  load_frags(f0, la, lb, 2);
+  mfma_frags(acc, f1);
+  OVL_SCHED_FENCE();
+  load_frags(f1, la, lb, 3);
+  mfma_frags(acc, f0);
+  if (next) stage_store(*st, next);
+  OVL_SCHED_FENCE();
+  mfma_frags(acc, f1);
+  OVL_SCHED_FENCE();
 }
 
 template <int BM, int BN>
@@ -189,20 +275,20 @@ __device__ inline void gemm_tile(Acc<BM, BN>& acc, const Operands& op, int64_t m
                                  BeforeStep before_step) {
   using C = TileCfg<BM, BN>;
   acc_zero(acc);
-  const int64_t steps = (op.k + kBK - 1) / kBK;
+  const TileAddr<BM, BN> ta = tile_addr<BM, BN>(op, m0);
+  const int32_t steps = (int32_t)((op.k + kBK - 1) / kBK);
   Stage<BM, BN> st;
   before_step(0);
-  stage_load(st, op, m0, 0);
+  stage_load(st, ta, 0);
   stage_store(st, lds);
   __syncthreads();
-  for (int64_t s = 0; s < steps; ++s) {
+  for (int32_t s = 0; s < steps; ++s) {
     const bool more = s + 1 < steps;
     if (more) {
-      before_step((s + 1) * kBK);
-      stage_load(st, op, m0, (s + 1) * kBK);
+      before_step((int64_t)(s + 1) * kBK);
+      stage_load(st, ta, (s + 1) * kBK);
     }
-    stage_compute(acc, lds + (s & 1) * C::STAGE_ELEMS);
-    if (more) stage_store(st, lds + ((s + 1) & 1) * C::STAGE_ELEMS);
+    stage_compute(acc, lds + (s & 1) * C::STAGE_ELEMS, &st, more ? lds + ((s + 1) & 1) * C::STAGE_ELEMS : nullptr);
     __syncthreads();
   }
 }
@@ -229,14 +315,38 @@ __device__ inline void acc_foreach(const Acc<BM, BN>& acc, F f) {
       }
 }
 
+// fp32 output view of one tile of a row-major matrix with pitch ldc: the
+// resource spans rows [0, m_valid) of the whole matrix, so rows past the
+// last are dropped by the hardware; the tile origin is folded into the
+// per-lane offset, and columns past n_valid get kOOB.
+struct OutTile {
+  rsrc_t r;
+  uint32_t ldc_b;   // row pitch in bytes (opaque to loop-invariant motion)
+  uint32_t base;    // byte offset of the tile origin
+  int64_t n_left;   // columns that exist from the tile origin on
+};
+
+__device__ inline OutTile out_tile(float* c, int64_t ldc, int64_t m0, int64_t n0, int64_t m_valid,
+                                   int64_t n_valid) {
+  OutTile o;
+  o.r = make_rsrc(c, m_valid * ldc * 4);
+  o.ldc_b = opaque((uint32_t)(ldc * 4));
+  o.base = (uint32_t)(m0 * ldc * 4 + n0 * 4);
+  o.n_left = n_valid - n0;
+  return o;
+}
+
+// Byte offset of (row, col) of the tile, or kOOB for a column past N.
+__device__ inline uint32_t out_off(const OutTile& o, int row, int col) {
+  return col < o.n_left ? o.base + (uint32_t)row * o.ldc_b + (uint32_t)col * 4 : kOOB;
+}
+
 // Stores the tile to fp32 C (row pitch ldc) at (m0, n0), clipped to m_valid x n_valid.
 template <int BM, int BN>
 __device__ inline void acc_store(const Acc<BM, BN>& acc, float* c, int64_t ldc, int64_t m0, int64_t n0,
                                  int64_t m_valid, int64_t n_valid) {
-  acc_foreach(acc, [&](int row, int col, float v) {
-    const int64_t m = m0 + row, n = n0 + col;
-    if (m < m_valid && n < n_valid) c[m * ldc + n] = v;
-  });
+  const OutTile o = out_tile(c, ldc, m0, n0, m_valid, n_valid);
+  acc_foreach(acc, [&](int row, int col, float v) { bstoref(o.r, out_off(o, row, col), v); });
 }
 
 }  // namespace ovl

@@ -89,15 +89,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs a) {
             timed_out = true;
         }
       }
-      const int64_t n0 = op.n0;
+      const OutTile o = out_tile(a.out, a.n, m0, op.n0, a.bm, a.n);
+      rsrc_t rin[kRsMaxRanks];
+      for (int p = 0; p < a.ranks; ++p) rin[p] = make_rsrc(p == a.rank ? a.out : a.peer_in[p], a.bm * a.n * 4);
       acc_foreach(acc, [&](int row, int col, float v) {
-        const int64_t mm = m0 + row, nn = n0 + col;
-        if (mm < a.bm && nn < a.n) {
-          const int64_t off = mm * a.n + nn;
-          for (int p = 0; p < a.ranks; ++p)
-            if (p != a.rank) v += a.peer_in[p][off];
-          a.out[off] = v;
-        }
+        const uint32_t off = out_off(o, row, col);
+        for (int p = 0; p < a.ranks; ++p)
+          if (p != a.rank) v += bloadf(rin[p], off);
+        bstoref(o.r, off, v);
       });
     }
   }
@@ -130,7 +129,10 @@ extern "C" ovl_status gemm_rs_run(const gemm_rs_desc* d, const void* a, const vo
   if (d->tile_m != kRsTile || d->tile_n != kRsTile) return OVL_EUNSUPPORTED;
   if (d->m < 1 || d->n < 8 || d->k < 8 || d->m % d->ranks) return OVL_ESHAPE;
   if (d->n % 8 || d->k % 8 || d->flag_stride < 8 || d->flag_stride % 8) return OVL_EALIGN;
-  if (d->m > (1 << 20) || d->n > (1 << 24) || d->k > (1 << 24)) return OVL_EUNSUPPORTED;
+  // Every operand below 1 GiB and rows below 2^20 elements: buffer offsets stay in 32 bits.
+  if (d->m > (1 << 20) || d->n > (1 << 20) || d->k > (1 << 20) || d->m * d->k * 2 > (1ll << 30) ||
+      d->k * d->n * 2 > (1ll << 30) || d->m * d->n * 4 > (1ll << 30))
+    return OVL_EUNSUPPORTED;
   const uint32_t mode = opts ? opts->mode : OVL_MODE_FUSED;
   if (mode != OVL_MODE_FUSED && mode != OVL_MODE_GEMM_ONLY) return OVL_EINVAL;
   if (!aligned16(a) || !aligned16(b) || !aligned16(out) || !aligned16(workspace)) return OVL_EALIGN;

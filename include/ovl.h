@@ -127,8 +127,9 @@ typedef struct ag_gemm_desc {
 typedef struct ag_gemm_plan_s* ag_gemm_plan_t;
 
 /* Validates `desc` and builds an immutable, host-only plan (thread-safe to
- * share; touches no device).  Errors: EINVAL, ESHAPE, EALIGN; EUNSUPPORTED if R > 16 or the
- * gathered row count exceeds 2^20. */
+ * share; touches no device).  Errors: EINVAL, ESHAPE, EALIGN; EUNSUPPORTED if
+ * R > 16, if R*shard_m, k or n exceeds 2^20, or if an operand (gathered, B
+ * or C) exceeds 1 GiB. */
 ovl_status ag_gemm_plan(const ag_gemm_desc* desc, ag_gemm_plan_t* out);
 ovl_status ag_gemm_plan_destroy(ag_gemm_plan_t plan);
 
@@ -209,7 +210,8 @@ size_t gemm_rs_workspace_bytes(const gemm_rs_desc* desc);
  *           their in_flags slot reaches `epoch`.
  * out:      fp32 [m/R][n].
  * out_flags: written (epoch) per sent tile.  in_flags: read only.
- * Errors as for ag_gemm_run; EUNSUPPORTED if tile_m/tile_n are not 256. */
+ * Errors as for ag_gemm_run; EUNSUPPORTED if tile_m/tile_n are not 256, if
+ * m, n or k exceeds 2^20, or if A, B or the local product exceeds 1 GiB. */
 ovl_status gemm_rs_run(const gemm_rs_desc* desc, const void* a, const void* b,
                        float* const* peer_out, const float* const* peer_in, float* out,
                        int64_t* out_flags, const int64_t* in_flags, void* workspace,
