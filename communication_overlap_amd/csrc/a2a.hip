@@ -1,6 +1,268 @@
-// All-to-all dispatch of routed tokens followed by a grouped expert GEMM.
+// All-to-all dispatch of routed tokens, then a grouped expert GEMM, with
+// slice-level overlap (the Aboleth README's all-to-all with one program per
+// peer: put the slice at an offset indexed by the sender's rank, then set
+// the receiver's flag for that sender; "Triton-distributed Semantics",
+// Producer-Consumer Model).
+//
+// Two launches on the caller's stream:
+//  1. Layout, one workgroup per source s: for every local expert e, the
+//     number of (token, choice) pairs of s routed to e and, for each pair, its
+//     row in slice s, ordered by (e, token id).  Integer block scans only, so
+//     the layout is bit-exact and does not depend on timing.  It also zeroes
+//     the slice arrival counters of this run.
+//  2. Fused: producer workgroups copy 32-row chunks of every slice (the own
+//     slice first, then rank+1, rank+2, ...) from the source's token rows;
+//     after each chunk the workgroup arrives on its slice's counter, and the
+//     workgroup that completes a slice publishes the slice flag (signal ADD
+//     for the arrivals, signal SET for the flag).  Consumer workgroups walk a
+//     flattened list of (slice, expert, m-tile, n-tile) tiles in the same
+//     slice order, wait on the slice flag once per tile, and run the MFMA
+//     GEMM of the expert's rows against that expert's weight.
+#include <algorithm>
+
 #include "device.h"
+#include "gemm_core.h"
 #include "host.h"
+
+namespace ovl {
+
+namespace {
+
+constexpr int kA2aMaxRanks = 16;
+constexpr int kA2aMaxExperts = 64;
+constexpr int kChunkRows = 32;
+constexpr int kGbm = 256, kGbn = 128;  // grouped GEMM tile
+constexpr int kA2aXcds = 8;
+
+struct A2aArgs {
+  const uint16_t* x[kA2aMaxRanks];
+  const int32_t* topk[kA2aMaxRanks];
+  const uint16_t* w;
+  uint16_t* recv_x;
+  int32_t* recv_src;
+  int32_t* recv_count;
+  float* y;
+  int64_t* flags;
+  int64_t* counters;  // [R] slice arrival counters (workspace)
+  ErrRec* err;
+  int64_t tokens, hidden, n, cap;
+  int64_t flag_stride;  // int64 slots
+  int64_t epoch;
+  uint64_t spin_limit;
+  int32_t ranks, rank, topk_n, experts;  // experts = experts per rank
+  int32_t producers, consumers;
+};
+
+// ---------------------------------------------------------------- layout
+
+__device__ inline int wave_incl_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// Exclusive scan of v over the workgroup (blockDim.x = 256); *total gets the sum.
+__device__ inline int block_excl_scan(int v, int* total, int* smem) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) smem[wave] = incl;
+  __syncthreads();
+  int before = 0, sum = 0;
+  for (int i = 0; i < kThreads / 64; ++i) {
+    const int wsum = smem[i];
+    if (i < wave) before += wsum;
+    sum += wsum;
+  }
+  __syncthreads();
+  *total = sum;
+  return before + incl - v;
+}
+
+__global__ __launch_bounds__(kThreads) void a2a_layout_kernel(A2aArgs a) {
+  __shared__ int smem[8];
+  const int s = blockIdx.x;
+  const int32_t* idx = a.topk[s];
+  const int e_lo = a.rank * a.experts;
+  const int64_t T = a.tokens;
+  const int64_t chunk = (T + kThreads - 1) / kThreads;
+  const int64_t t0 = min(T, chunk * threadIdx.x), t1 = min(T, t0 + chunk);
+  int base = 0;
+  for (int e = 0; e < a.experts; ++e) {
+    const int ge = e_lo + e;
+    int c = 0;
+    for (int64_t t = t0; t < t1; ++t)
+      for (int j = 0; j < a.topk_n; ++j) c += idx[t * a.topk_n + j] == ge;
+    int total;
+    const int off = block_excl_scan(c, &total, smem);
+    int pos = base + off;
+    for (int64_t t = t0; t < t1; ++t)
+      for (int j = 0; j < a.topk_n; ++j)
+        if (idx[t * a.topk_n + j] == ge) a.recv_src[(int64_t)s * a.cap + pos++] = (int32_t)t;
+    if (threadIdx.x == 0) a.recv_count[s * a.experts + e] = total;
+    base += total;
+  }
+  if (threadIdx.x == 0) a.counters[s] = 0;
+}
+
+// ---------------------------------------------------------------- shared schedule
+
+// Per-run geometry, rebuilt by every workgroup from recv_count.
+struct Geometry {
+  int32_t count[kA2aMaxRanks * kA2aMaxExperts];  // recv_count, by (slice, expert)
+  int32_t slice_rows[kA2aMaxRanks];   // by slice
+  int32_t chunk_base[kA2aMaxRanks + 1];  // by position in slice order
+  int32_t tile_base[kA2aMaxRanks * kA2aMaxExperts + 1];  // by (order position, expert)
+  int32_t seg_start[kA2aMaxRanks * kA2aMaxExperts];      // by (order position, expert)
+};
+
+__device__ inline int slice_at(const A2aArgs& a, int pos) { return (a.rank + pos) % a.ranks; }
+
+__device__ void build_geometry(const A2aArgs& a, Geometry* g) {
+  for (int i = threadIdx.x; i < a.ranks * a.experts; i += kThreads) g->count[i] = a.recv_count[i];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int ntn = (int)((a.n + kGbn - 1) / kGbn);
+    int chunks = 0, tiles = 0;
+    for (int pos = 0; pos < a.ranks; ++pos) {
+      const int s = slice_at(a, pos);
+      int rows = 0;
+      g->chunk_base[pos] = chunks;
+      for (int e = 0; e < a.experts; ++e) {
+        const int c = g->count[s * a.experts + e];
+        g->seg_start[pos * a.experts + e] = rows;
+        g->tile_base[pos * a.experts + e] = tiles;
+        tiles += ((c + kGbm - 1) / kGbm) * ntn;
+        rows += c;
+      }
+      g->slice_rows[s] = rows;
+      chunks += (rows + kChunkRows - 1) / kChunkRows;
+    }
+    g->chunk_base[a.ranks] = chunks;
+    g->tile_base[a.ranks * a.experts] = tiles;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- producer
+
+__device__ void a2a_produce(const A2aArgs& a, const Geometry* g, int w, int P) {
+  // Slices that receive nothing are complete at once.
+  if (w == 0 && threadIdx.x < a.ranks && g->slice_rows[threadIdx.x] == 0)
+    __hip_atomic_store(a.flags + (int64_t)threadIdx.x * a.flag_stride, a.epoch, __ATOMIC_RELEASE,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  const int total = g->chunk_base[a.ranks];
+  const int vpr = (int)(a.hidden / 8);  // 16-byte vectors per row
+  for (int ch = w; ch < total; ch += P) {
+    int pos = 0;
+    while (g->chunk_base[pos + 1] <= ch) ++pos;
+    const int s = slice_at(a, pos);
+    const int r0 = (ch - g->chunk_base[pos]) * kChunkRows;
+    const int rows = min(kChunkRows, g->slice_rows[s] - r0);
+    const uint16_t* src = a.x[s];
+    uint16_t* dst = a.recv_x + ((int64_t)s * a.cap + r0) * a.hidden;
+    const int32_t* srcrow = a.recv_src + (int64_t)s * a.cap + r0;
+    constexpr int U = 8;
+    const int totalv = rows * vpr;
+    for (int base = 0; base < totalv; base += kThreads * U) {
+      u32x4 v[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int i = base + j * kThreads + threadIdx.x;
+        if (i < totalv) {
+          const int r = i / vpr, c = i - r * vpr;
+          v[j] = ld16_nt(src + (int64_t)srcrow[r] * a.hidden + c * 8);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int i = base + j * kThreads + threadIdx.x;
+        if (i < totalv) {
+          const int r = i / vpr, c = i - r * vpr;
+          st16(dst + (int64_t)r * a.hidden + c * 8, v[j]);
+        }
+      }
+    }
+    const int need = g->chunk_base[pos + 1] - g->chunk_base[pos];
+    const int64_t old = wg_arrive(a.counters + s);
+    if (threadIdx.x == 0 && old + 1 == need)
+      __hip_atomic_store(a.flags + (int64_t)s * a.flag_stride, a.epoch, __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void a2a_produce_kernel(A2aArgs a) {
+  __shared__ Geometry g;
+  build_geometry(a, &g);
+  a2a_produce(a, &g, blockIdx.x, gridDim.x);
+}
+
+// ---------------------------------------------------------------- consumer
+
+template <bool WAIT>
+__device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint16_t* lds) {
+  const int ntn = (int)((a.n + kGbn - 1) / kGbn);
+  const int nseg = a.ranks * a.experts;
+  const int total = g->tile_base[nseg];
+  const int Cn = a.consumers;
+  const int groups = (Cn % kA2aXcds == 0) ? kA2aXcds : 1;
+  const int per = Cn / groups;
+  const int x = cidx % groups, q = cidx / groups;
+  int seg = 0;
+  int64_t waited_slice = -1;
+  bool timed_out = false;
+  for (int64_t wv = 0;; ++wv) {
+    const int64_t j = wv * Cn + (int64_t)x * per + q;
+    if (j >= total) break;
+    while (g->tile_base[seg + 1] <= j) ++seg;  // tiles only move forward
+    const int pos = seg / a.experts, e = seg % a.experts;
+    const int s = slice_at(a, pos);
+    const int local = (int)(j - g->tile_base[seg]);
+    const int mt = local / ntn, nt = local % ntn;
+    const int seg0 = g->seg_start[seg];
+    const int seg_end = seg0 + g->count[s * a.experts + e];
+
+    if (WAIT && waited_slice != s && !timed_out) {
+      if (!wave_wait(a.flags + (int64_t)s * a.flag_stride, a.epoch, a.spin_limit, a.err, kSiteA2aSlice, s))
+        timed_out = true;
+      waited_slice = s;
+    }
+    Operands op;
+    op.a = a.recv_x + (int64_t)s * a.cap * a.hidden;
+    op.lda = a.hidden;
+    op.m_valid = seg_end;
+    op.b = a.w + (int64_t)e * a.hidden * a.n;
+    op.ldb = a.n;
+    op.n0 = (int64_t)nt * kGbn;
+    op.n_valid = a.n;
+    op.k = a.hidden;
+    const int64_t m0 = seg0 + (int64_t)mt * kGbm;
+    Acc<kGbm, kGbn> acc;
+    gemm_tile<kGbm, kGbn>(acc, op, m0, lds, [](int64_t) {});
+    acc_store<kGbm, kGbn>(acc, a.y + (int64_t)s * a.cap * a.n, a.n, m0, op.n0, seg_end, a.n);
+  }
+}
+
+template <int MODE>  // 0 fused, 2 GEMM only
+__global__ __launch_bounds__(kThreads, 1) void a2a_fused_kernel(A2aArgs a) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  Geometry* g = reinterpret_cast<Geometry*>(lds + 2 * TileCfg<kGbm, kGbn>::STAGE_ELEMS);
+  build_geometry(a, g);
+  if ((int)blockIdx.x < a.producers) {
+    a2a_produce(a, g, blockIdx.x, a.producers);
+    return;
+  }
+  a2a_consume<MODE == 0>(a, g, (int)blockIdx.x - a.producers, lds);
+}
+
+constexpr int a2a_lds_bytes() { return TileCfg<kGbm, kGbn>::LDS_BYTES + (int)sizeof(Geometry); }
+
+}  // namespace
+
+}  // namespace ovl
 
 using namespace ovl;
 
@@ -9,14 +271,111 @@ extern "C" size_t a2a_flags_bytes(const a2a_desc* d) {
   return (size_t)d->ranks * (size_t)d->flag_stride;
 }
 
-extern "C" size_t a2a_workspace_bytes(const a2a_desc* d) { return d ? 256 : 0; }
+extern "C" size_t a2a_workspace_bytes(const a2a_desc* d) {
+  if (!d || d->ranks < 1) return 0;
+  return OVL_ERROR_RECORD_BYTES + 8 * (size_t)kA2aMaxRanks;
+}
 
 extern "C" ovl_status a2a_dispatch_grouped_gemm_run(const a2a_desc* d, const void* const* x,
                                                     const int32_t* const* topk_idx, const void* w, void* recv_x,
                                                     int32_t* recv_src, int32_t* recv_count, float* y,
                                                     int64_t* flags, void* workspace, int64_t epoch,
                                                     const ovl_opts* opts, hipStream_t stream) {
-  (void)d; (void)x; (void)topk_idx; (void)w; (void)recv_x; (void)recv_src; (void)recv_count; (void)y;
-  (void)flags; (void)workspace; (void)epoch; (void)opts; (void)stream;
-  return OVL_EUNSUPPORTED;
+  if (!d || !x || !topk_idx || !recv_x || !recv_src || !recv_count || !flags || !workspace) return OVL_EINVAL;
+  if (d->ranks < 1 || d->rank < 0 || d->rank >= d->ranks) return OVL_EINVAL;
+  if (d->ranks > kA2aMaxRanks || d->experts_per_rank > kA2aMaxExperts) return OVL_EUNSUPPORTED;
+  if (d->experts_per_rank < 1 || d->topk < 1 || d->topk > 8 || d->tokens < 0 ||
+      d->num_experts != d->ranks * d->experts_per_rank)
+    return OVL_ESHAPE;
+  if (d->hidden < 8 || d->n < 8 || d->hidden % 8 || d->n % 8 || d->flag_stride < 8 || d->flag_stride % 8)
+    return OVL_EALIGN;
+  const int64_t cap = d->tokens * std::min<int64_t>(d->topk, d->experts_per_rank);
+  // Every operand below 1 GiB and rows below 2^20 elements: buffer offsets stay in 32 bits.
+  if (d->tokens > (1 << 20) || d->hidden > (1 << 20) || d->n > (1 << 20) ||
+      (int64_t)d->ranks * cap * d->hidden * 2 > (1ll << 30) || (int64_t)d->ranks * cap * d->n * 4 > (1ll << 30) ||
+      (int64_t)d->experts_per_rank * d->hidden * d->n * 2 > (1ll << 30))
+    return OVL_EUNSUPPORTED;
+  const uint32_t mode = opts ? opts->mode : OVL_MODE_FUSED;
+  if (mode != OVL_MODE_FUSED && mode != OVL_MODE_GEMM_ONLY && mode != OVL_MODE_COPY_ONLY) return OVL_EINVAL;
+  const bool gemm = mode != OVL_MODE_COPY_ONLY;
+  if (gemm && (!w || !y)) return OVL_EINVAL;
+  if (!aligned16(recv_x) || !aligned16(workspace) || (gemm && (!aligned16(w) || !aligned16(y))) ||
+      (reinterpret_cast<uintptr_t>(flags) & 7u) || (reinterpret_cast<uintptr_t>(recv_src) & 3u) ||
+      (reinterpret_cast<uintptr_t>(recv_count) & 3u))
+    return OVL_EALIGN;
+  for (int s = 0; s < d->ranks; ++s) {
+    if (mode == OVL_MODE_GEMM_ONLY) break;
+    if (!x[s] || !topk_idx[s]) return OVL_EINVAL;
+    if (!aligned16(x[s]) || (reinterpret_cast<uintptr_t>(topk_idx[s]) & 3u)) return OVL_EALIGN;
+  }
+  DeviceInfo di;
+  ovl_status st = current_device_info(&di);
+  if (st) return st;
+
+  A2aArgs a = {};
+  for (int s = 0; s < d->ranks; ++s) {
+    if (mode == OVL_MODE_GEMM_ONLY) break;
+    a.x[s] = static_cast<const uint16_t*>(x[s]);
+    a.topk[s] = topk_idx[s];
+  }
+  a.w = static_cast<const uint16_t*>(w);
+  a.recv_x = static_cast<uint16_t*>(recv_x);
+  a.recv_src = recv_src;
+  a.recv_count = recv_count;
+  a.y = y;
+  a.flags = flags;
+  a.err = static_cast<ErrRec*>(workspace);
+  a.counters = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(workspace) + OVL_ERROR_RECORD_BYTES);
+  a.tokens = d->tokens;
+  a.hidden = d->hidden;
+  a.n = d->n;
+  a.cap = cap;
+  a.flag_stride = d->flag_stride / 8;
+  a.epoch = epoch;
+  a.spin_limit = spin_limit_of(opts);
+  a.ranks = d->ranks;
+  a.rank = d->rank;
+  a.topk_n = d->topk;
+  a.experts = d->experts_per_rank;
+
+  const int lds = a2a_lds_bytes();
+  const void* fk = (mode == OVL_MODE_GEMM_ONLY) ? reinterpret_cast<const void*>(&a2a_fused_kernel<2>)
+                                                : reinterpret_cast<const void*>(&a2a_fused_kernel<0>);
+  st = allow_lds(fk, lds);
+  if (st) return st;
+  int occ = 0;
+  OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &occ, (mode == OVL_MODE_GEMM_ONLY) ? a2a_fused_kernel<2> : a2a_fused_kernel<0>, kThreads, lds));
+  const int64_t resident = (int64_t)std::max(occ, 1) * di.cus;
+  const uint32_t req = opts ? opts->producers : 0;
+
+  if (mode != OVL_MODE_GEMM_ONLY) {
+    st = epoch_accept(flags, epoch);
+    if (st) return st;
+    hipLaunchKernelGGL(a2a_layout_kernel, dim3(d->ranks), dim3(kThreads), 0, stream, a);
+    OVL_HIP_TRY(hipGetLastError());
+  }
+  if (mode == OVL_MODE_COPY_ONLY) {
+    const int P = req ? (int)req : di.cus * 4;
+    a.producers = P;
+    a.consumers = 0;
+    hipLaunchKernelGGL(a2a_produce_kernel, dim3(P), dim3(kThreads), 0, stream, a);
+    OVL_HIP_TRY(hipGetLastError());
+    return OVL_OK;
+  }
+  int P = 0;
+  if (mode == OVL_MODE_FUSED) {
+    P = req ? (int)req : std::max(kA2aXcds, di.cus / 8);
+    if (P >= resident) return OVL_EINVAL;
+  }
+  int64_t Cn = resident - P;
+  if (Cn > kA2aXcds) Cn -= Cn % kA2aXcds;
+  a.producers = P;
+  a.consumers = (int32_t)Cn;
+  if (mode == OVL_MODE_FUSED)
+    hipLaunchKernelGGL(a2a_fused_kernel<0>, dim3(P + Cn), dim3(kThreads), lds, stream, a);
+  else
+    hipLaunchKernelGGL(a2a_fused_kernel<2>, dim3(Cn), dim3(kThreads), lds, stream, a);
+  OVL_HIP_TRY(hipGetLastError());
+  return OVL_OK;
 }

@@ -3,33 +3,42 @@
 // One workgroup of 4 wavefronts computes a BM x BN output tile; the waves
 // form a 2 x 2 grid, each owning a (BM/2) x (BN/2) sub-tile made of 32 x 32
 // blocks computed with v_mfma_f32_32x32x16_bf16.  K advances in steps of 64
-// through a two-stage LDS ring:
-//   - A (row-major, K contiguous) is copied to LDS as is, 16 bytes a lane;
-//   - B (row-major, N contiguous) is transposed on its way to LDS: each lane
-//     loads an 8 (k) x BV (n) block, transposes it in registers and writes
-//     BV vectors of 8 consecutive k values, so that both MFMA operands read
-//     K-contiguous 16-byte fragments from LDS.
-// LDS rows are padded by 16 bytes (pitch 144 B), which spreads the 16-byte
-// fragment reads and the staging writes over all banks.
+// through a two-stage LDS ring.
 //
-// Global traffic goes through buffer resources whose size ends exactly at
-// the tile's last valid row: loads past it return zero and stores past it
-// are dropped by the hardware, so ragged M and K tails cost no branches;
-// columns past N get an out-of-range offset once per tile.
+// Both operands travel global -> LDS with buffer loads that write LDS
+// directly (16 bytes a lane; lane i of an instruction lands at byte 16*i of
+// a 1 KiB LDS block), so staging costs neither registers nor LDS-write
+// instructions:
+//   - A (row-major, K contiguous) is kept as [row][k] (128 B per row);
+//   - B (row-major, N contiguous) is kept as [k][n] and its MFMA fragments
+//     are read with ds_read_b64_tr_b16, which transposes 4 x 4 blocks of
+//     16-bit elements across each group of 16 lanes: source lane s of a
+//     group points at row s/4, columns 4*(s%4)..+3 of a 4 x 16 block, and
+//     lane i receives column i of the block's 4 rows, i.e. 4 consecutive k
+//     of one n; two such reads give the 8 consecutive k of one MFMA operand.
+// Each LDS row's 16-byte chunks are stored XOR-permuted (the permutation is
+// applied when each lane picks the global address it fetches), so that the
+// fragment reads hit every bank once.
 //
-// Accumulation order of every output element is fixed: K ascending in steps
-// of 16 (one MFMA each), whatever the order tiles or flags arrive in.
+// Global traffic goes through buffer resources whose size ends at the last
+// valid row: loads past it return zero, so ragged M and K tails cost no
+// branches; chunks past K (for A) or past N (for B) get an out-of-range
+// offset.
+//
+// Accumulation order of every output element is fixed (K ascending in steps
+// of 16, one MFMA each), whatever the order tiles or flags arrive in.
 #pragma once
 
 #include "device.h"
 
 namespace ovl {
 
-constexpr int kBK = 64;        // K per pipeline stage
-constexpr int kKP = kBK + 8;   // LDS row pitch in bf16 elements
-constexpr uint32_t kOOB = 0x80000000u;  // an offset past every buffer (operands are < 2 GiB)
+constexpr int kBK = 64;                 // K per pipeline stage
+constexpr uint32_t kOOB = 0x80000000u;  // an offset past every buffer (operands are < 1 GiB)
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define OVL_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 // Raw buffer resource over [base, base + bytes); bytes is clamped to [0, 2^31 - 1].
 __device__ inline rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -37,15 +46,6 @@ __device__ inline rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
-__device__ inline u32x4 bload128(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-}
-__device__ inline u32x2 bload64(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
-}
-__device__ inline uint32_t bload32(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
-}
 __device__ inline float bloadf(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
@@ -53,55 +53,60 @@ __device__ inline void bstoref(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
 }
 
+// Buffer descriptor as four scalar words, for the inline-asm loads below
+// (base address, stride 0, size in bytes, raw-buffer format word).
+__device__ inline u32x4 make_srd(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0x7fffffff ? 0x7fffffffu : (uint32_t)bytes);
+  u32x4 d;
+  d.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  d.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  d.z = __builtin_amdgcn_readfirstlane(n);
+  d.w = 0x00020000u;
+  return d;
+}
+
+// LDS byte address of a pointer into the workgroup's LDS.
+__device__ inline uint32_t lds_addr(const void* p) { return (uint32_t)(size_t)OVL_LDS(const void, p); }
+
+// 16 bytes per lane from global (buffer offset) straight into LDS at
+// lds_block + 16 * lane.  Issued through inline assembly on purpose: the
+// compiler cannot tell that these writes go to the other half of the LDS
+// ring from the one being read, and would otherwise wait for them before
+// the very next LDS read, serialising the prefetch with the MFMAs.  The
+// caller waits for them (vmcnt(0)) before the barrier that publishes the
+// stage.
+__device__ inline void load_to_lds(const u32x4& srd, uint32_t lds_block, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_block), "v"(off), "s"(srd)
+               : "memory", "m0");
+}
+
+// Chunk permutations.  A row r (8 chunks of 16 B): physical chunk p holds
+// logical chunk p ^ swz_a(r).  B row k (BN/8 chunks): p holds p ^ swz_b(k).
+__device__ inline uint32_t swz_a(uint32_t r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ inline uint32_t swz_b(uint32_t k) { return (0xCA60u >> ((k & 3) * 4)) & 15; }  // 0, 6, 10, 12
+
 template <int BM, int BN>
 struct TileCfg {
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && BN <= 256 && BM <= 256, "tile shape");
-  static constexpr int FM = BM / 64;        // 32-row blocks per wave
-  static constexpr int FN = BN / 64;        // 32-col blocks per wave
-  static constexpr int AV = BM / 32;        // 16-byte A vectors per thread per stage
-  static constexpr int BV = BN / 32;        // B columns per thread per stage (8 k-rows each)
-  static constexpr int A_ELEMS = BM * kKP;
-  static constexpr int B_ELEMS = BN * kKP;
-  static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
-  static constexpr int LDS_BYTES = 2 * STAGE_ELEMS * 2;
+  static_assert(BM % 64 == 0 && BN % 128 == 0 && BN <= 256 && BM <= 256, "tile shape");
+  static constexpr int FM = BM / 64;             // 32-row blocks per wave
+  static constexpr int FN = BN / 64;             // 32-col blocks per wave
+  static constexpr int A_BYTES = BM * kBK * 2;
+  static constexpr int B_BYTES = BN * kBK * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int STAGE_ELEMS = STAGE_BYTES / 2;  // in bf16
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int QA = BM / 32;             // A load instructions per wave per stage
+  static constexpr int QB = BN / 32;             // B load instructions per wave per stage
+  static constexpr int B_LPR = BN / 8;           // lanes per B row in one instruction
+  static constexpr int B_RPI = 64 / B_LPR;       // B rows per instruction
 };
 
 template <int BM, int BN>
 struct Acc {
   f32x16 v[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN];
-};
-
-template <int BV>
-struct BRow;
-template <>
-struct BRow<8> { u32x4 d; };
-template <>
-struct BRow<4> { u32x2 d; };
-template <>
-struct BRow<2> { uint32_t d; };
-
-template <int BV>
-__device__ inline BRow<BV> load_brow(rsrc_t r, uint32_t off);
-template <>
-__device__ inline BRow<8> load_brow<8>(rsrc_t r, uint32_t off) { return {bload128(r, off)}; }
-template <>
-__device__ inline BRow<4> load_brow<4>(rsrc_t r, uint32_t off) { return {bload64(r, off)}; }
-template <>
-__device__ inline BRow<2> load_brow<2>(rsrc_t r, uint32_t off) { return {bload32(r, off)}; }
-
-template <int BV>
-__device__ inline uint32_t brow_word(const BRow<BV>& r, int w);
-template <>
-__device__ inline uint32_t brow_word<8>(const BRow<8>& r, int w) { return r.d[w]; }
-template <>
-__device__ inline uint32_t brow_word<4>(const BRow<4>& r, int w) { return r.d[w]; }
-template <>
-__device__ inline uint32_t brow_word<2>(const BRow<2>& r, int) { return r.d; }
-
-template <int BM, int BN>
-struct Stage {
-  u32x4 a[TileCfg<BM, BN>::AV];
-  BRow<TileCfg<BM, BN>::BV> b[8];
 };
 
 // Operand view for one tile: A rows [0, m_valid) at a (row pitch lda),
@@ -117,74 +122,106 @@ struct Operands {
   int64_t k;
 };
 
-// Per-tile, per-lane addressing of the global loads.
+// Per-tile, per-lane addressing of the global -> LDS loads.
 template <int BM, int BN>
 struct TileAddr {
-  rsrc_t ra, rb;
-  uint32_t a_off;   // this lane's A offset at k0 = 0 for vector v = 0 (bytes)
-  uint32_t a_vstep; // bytes between the rows of consecutive A vectors (32 rows)
-  uint32_t b_off;   // this lane's B offset at k0 = 0, or kOOB for columns past N
-  uint32_t ldb_b;   // B row pitch in bytes
+  u32x4 ra, rb;
+  uint32_t a_off[2];   // lane offset of A instruction q = 0 / 1 at k0 = 0 (bytes), before the row step
+  uint32_t a_kc[2];    // lane's K column (elements) for even / odd instructions
+  uint32_t a_qstep;    // bytes between consecutive A instructions (8 rows)
+  uint32_t b_off[2];   // lane offset of B instruction parity 0 / 1 at k0 = 0, or kOOB past N
+  uint32_t b_qstep;    // bytes between consecutive B instructions
+  uint32_t ldb_b;
   int32_t k;
-  int32_t kchunk;   // this lane's K offset within a stage (elements)
 };
 
 template <int BM, int BN>
 __device__ inline TileAddr<BM, BN> tile_addr(const Operands& op, int64_t m0) {
   using C = TileCfg<BM, BN>;
   TileAddr<BM, BN> t;
-  const int tid = threadIdx.x;
-  t.ra = make_rsrc(op.a + m0 * op.lda, (op.m_valid - m0) * op.lda * 2);
-  t.rb = make_rsrc(op.b + op.n0, op.k * op.ldb * 2 - op.n0 * 2);
-  t.kchunk = (tid & 7) * 8;
-  t.a_off = (uint32_t)(((tid >> 3) * op.lda + t.kchunk) * 2);
-  t.a_vstep = (uint32_t)(32 * op.lda * 2);
-  const int kb = (tid & 7) * 8;
-  const int nb = (tid >> 3) * C::BV;
-  t.ldb_b = (uint32_t)(op.ldb * 2);
-  t.b_off = (op.n0 + nb < op.n_valid) ? (uint32_t)(kb * op.ldb * 2 + nb * 2) : kOOB;
+  const uint32_t l = lane_id();
+  const uint32_t w = threadIdx.x >> 6;
+  t.ra = make_srd(op.a + m0 * op.lda, (op.m_valid - m0) * op.lda * 2);
+  t.rb = make_srd(op.b + op.n0, op.k * op.ldb * 2 - op.n0 * 2);
   t.k = (int32_t)op.k;
+  // A: instruction iq = w*QA + q covers tile rows iq*8 .. iq*8+7; lane l
+  // fills row iq*8 + l/8, physical chunk l%8.
+  const uint32_t lda_b = (uint32_t)(op.lda * 2);
+  for (int par = 0; par < 2; ++par) {
+    const uint32_t lc = (l & 7) ^ (l >> 3) ^ (uint32_t)par;  // swz_a of row iq*8 + l/8 for iq parity par
+    t.a_kc[par] = lc * 8;
+    t.a_off[par] = (w * C::QA * 8 + (l >> 3)) * lda_b + lc * 16;
+  }
+  t.a_qstep = 8 * lda_b;
+  // B: instruction iq = w*QB + q covers k rows iq*RPI .. +RPI-1; lane l
+  // fills row iq*RPI + l/LPR, physical chunk l%LPR.
+  t.ldb_b = (uint32_t)(op.ldb * 2);
+  for (int par = 0; par < 2; ++par) {
+    const uint32_t row = (w * C::QB + par) * C::B_RPI + l / C::B_LPR;  // row of instruction q = par
+    const uint32_t lc = (l % C::B_LPR) ^ swz_b(row);
+    const bool nvalid = op.n0 + (int64_t)lc * 8 < op.n_valid;
+    t.b_off[par] = nvalid ? row * t.ldb_b + lc * 16 : kOOB;
+  }
+  t.b_qstep = (uint32_t)(C::B_RPI * t.ldb_b);
   return t;
 }
 
-// Global -> registers for the K-step starting at k0.
+// Issues this wave's share of the global -> LDS loads of the K-step at k0:
+// the A part and the B part separately, so that each can sit under MFMAs.
 template <int BM, int BN>
-__device__ inline void stage_load(Stage<BM, BN>& st, const TileAddr<BM, BN>& t, int32_t k0) {
+__device__ inline void stage_issue_a(const TileAddr<BM, BN>& t, uint32_t stage, int32_t k0) {
   using C = TileCfg<BM, BN>;
-  const uint32_t abase = (k0 + t.kchunk < t.k) ? t.a_off + (uint32_t)k0 * 2 : kOOB;
+  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int v = 0; v < C::AV; ++v) st.a[v] = bload128(t.ra, abase + v * t.a_vstep);
-  const uint32_t bbase = t.b_off + (uint32_t)k0 * t.ldb_b;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) st.b[i] = load_brow<C::BV>(t.rb, bbase + i * t.ldb_b);
+  for (int q = 0; q < C::QA; ++q) {
+    const int par = q & 1;  // the instruction index parity equals q's (QA is even)
+    const uint32_t off = (k0 + (int32_t)t.a_kc[par] < t.k) ? t.a_off[par] + q * t.a_qstep + (uint32_t)k0 * 2 : kOOB;
+    load_to_lds(t.ra, stage + (w * C::QA + q) * 1024, off);
+  }
 }
 
-// Registers -> LDS stage buffer (B transposed to [n][k]).
 template <int BM, int BN>
-__device__ inline void stage_store(const Stage<BM, BN>& st, uint16_t* lds_stage) {
+__device__ inline void stage_issue_b(const TileAddr<BM, BN>& t, uint32_t stage, int32_t k0) {
   using C = TileCfg<BM, BN>;
-  const int t = threadIdx.x;
-  uint16_t* la = lds_stage;
-  uint16_t* lb = lds_stage + C::A_ELEMS;
-  const int chunk = t & 7;
+  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t sb = stage + C::A_BYTES;
+  const uint32_t kb = (uint32_t)k0 * t.ldb_b;
 #pragma unroll
-  for (int v = 0; v < C::AV; ++v) {
-    const int r = v * 32 + (t >> 3);
-    st16(la + r * kKP + chunk * 8, st.a[v]);
+  for (int q = 0; q < C::QB; ++q) {
+    const int par = q & 1;  // B_RPI is even, so swz_b depends on q only through its parity
+    load_to_lds(t.rb, sb + (w * C::QB + q) * 1024, t.b_off[par] + (q & ~1) * t.b_qstep + kb);
   }
-  const int kb = (t & 7) * 8;
-  const int nb = (t >> 3) * C::BV;
-#pragma unroll
-  for (int j = 0; j < C::BV; ++j) {
-    u32x4 out;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = brow_word<C::BV>(st.b[2 * q], j >> 1);
-      const uint32_t hi = brow_word<C::BV>(st.b[2 * q + 1], j >> 1);
-      out[q] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    st16(lb + (nb + j) * kKP + kb, out);
+}
+
+// Per-lane LDS read offsets (bytes, within a stage) of the MFMA fragments.
+template <int BM, int BN>
+struct FragAddr {
+  uint32_t a[4];         // A fragment of sub-step kk (add fm * 32 rows * 128 B)
+  uint32_t b[TileCfg<BM, BN>::FN];  // B: row (h*8 + s/4), chunk for block fn (add kk*16 rows)
+};
+
+template <int BM, int BN>
+__device__ inline FragAddr<BM, BN> frag_addr() {
+  using C = TileCfg<BM, BN>;
+  FragAddr<BM, BN> f;
+  const uint32_t l = lane_id();
+  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t wm = (wave >> 1) * (BM / 2);
+  const uint32_t wn = (wave & 1) * (BN / 2);
+  // A: row wm + fm*32 + l%32, logical chunk 2*kk + l/32.
+  const uint32_t row = wm + (l & 31);
+  for (int kk = 0; kk < 4; ++kk) f.a[kk] = row * 128 + (((2 * kk) | (l >> 5)) ^ swz_a(row)) * 16;
+  // B: group g = l/16 (h = g/2), source lane s = l%16 points at row
+  // kk*16 + h*8 + s/4 (+4 for the second read), columns
+  // wn + fn*32 + (g%2)*16 + 4*(s%4) .. +3.
+  const uint32_t g = l >> 4, s = l & 15;
+  const uint32_t brow = (g >> 1) * 8 + (s >> 2);
+  for (int fn = 0; fn < C::FN; ++fn) {
+    const uint32_t col = wn + fn * 32 + (g & 1) * 16 + 4 * (s & 3);
+    const uint32_t chunk = (col >> 3) ^ swz_b(brow);
+    f.b[fn] = C::A_BYTES + brow * (BN * 2) + chunk * 16 + (col & 4) * 2;
   }
+  return f;
 }
 
 template <int BM, int BN>
@@ -194,14 +231,18 @@ struct Frags {
 };
 
 template <int BM, int BN>
-__device__ inline void load_frags(Frags<BM, BN>& f, const uint16_t* la, const uint16_t* lb, int kk) {
+__device__ inline void load_frags(Frags<BM, BN>& f, const uint8_t* stage, const FragAddr<BM, BN>& fa, int kk) {
   using C = TileCfg<BM, BN>;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)
-    f.a[fm] = *reinterpret_cast<const bf16x8*>(la + fm * 32 * kKP + kk * 16);
+    f.a[fm] = *OVL_LDS(const bf16x8, stage + fa.a[kk] + fm * 32 * 128);
 #pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn)
-    f.b[fn] = *reinterpret_cast<const bf16x8*>(lb + fn * 32 * kKP + kk * 16);
+  for (int fn = 0; fn < C::FN; ++fn) {
+    const uint8_t* p = stage + fa.b[fn] + kk * 16 * (BN * 2);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(OVL_LDS(s16x4, p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(OVL_LDS(s16x4, p + 4 * (BN * 2)));
+    f.b[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
 }
 
 template <int BM, int BN>
@@ -224,33 +265,42 @@ __device__ inline uint32_t opaque(uint32_t x) {
 
 #define OVL_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
+// Inside one scheduling region: alternate one MFMA with one LDS read, n
+// times, then let the remaining MFMAs follow.
+template <int N>
+__device__ inline void interleave_mfma_ds_read() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+}
+
 // MFMA over one LDS stage (4 sub-steps of K=16), fragments double-buffered
 // so that the LDS reads of sub-step kk+1 are in flight during the MFMAs of
-// kk.  The scheduling fences keep that pipeline shape.  When `next` is not
-// null, the next stage's registers are written to it during the last
-// sub-step, under the MFMAs.
-template <int BM, int BN>
-__device__ inline void stage_compute(Acc<BM, BN>& acc, const uint16_t* lds_stage, const Stage<BM, BN>* st,
-                                     uint16_t* next) {
+// kk (one read after each MFMA).  prefetch_a / prefetch_b issue the next
+// stage's global -> LDS loads under the MFMAs of sub-steps 0 and 1.
+template <int BM, int BN, class PA, class PB>
+__device__ inline void stage_compute(Acc<BM, BN>& acc, const uint8_t* stage, const FragAddr<BM, BN>& fa,
+                                     PA prefetch_a, PB prefetch_b) {
   using C = TileCfg<BM, BN>;
-  const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
-  const int wm = (wave >> 1) * (BM / 2);
-  const int wn = (wave & 1) * (BN / 2);
-  const uint16_t* la = lds_stage + (wm + (lane & 31)) * kKP + (lane >> 5) * 8;
-  const uint16_t* lb = lds_stage + C::A_ELEMS + (wn + (lane & 31)) * kKP + (lane >> 5) * 8;
+  constexpr int kReads = C::FM + 2 * C::FN;  // LDS reads per sub-step
   Frags<BM, BN> f0, f1;
-  load_frags(f0, la, lb, 0);
+  load_frags(f0, stage, fa, 0);
   OVL_SCHED_FENCE();
-  load_frags(f1, la, lb, 1);
+  prefetch_a();
+  load_frags(f1, stage, fa, 1);
   mfma_frags(acc, f0);
+  interleave_mfma_ds_read<kReads>();
   OVL_SCHED_FENCE();
-  load_frags(f0, la, lb, 2);
+  prefetch_b();
+  load_frags(f0, stage, fa, 2);
   mfma_frags(acc, f1);
+  interleave_mfma_ds_read<kReads>();
   OVL_SCHED_FENCE();
-  load_frags(f1, la, lb, 3);
+  load_frags(f1, stage, fa, 3);
   mfma_frags(acc, f0);
-  if (next) stage_store(*st, next);
+  interleave_mfma_ds_read<kReads>();
   OVL_SCHED_FENCE();
   mfma_frags(acc, f1);
   OVL_SCHED_FENCE();
@@ -267,28 +317,40 @@ __device__ inline void acc_zero(Acc<BM, BN>& acc) {
       for (int r = 0; r < 16; ++r) acc.v[fm][fn][r] = 0.f;
 }
 
-// The K loop of one tile.  before_step(k0) runs before the global loads of
-// the K-step at k0 are issued (the consumer's flag wait goes there), in
-// every wave.  Ends with a workgroup barrier, so LDS may be reused at once.
+// The K loop of one tile.  before_step(k0) runs before the loads of the
+// K-step at k0 are issued (the consumer's flag wait goes there), in every
+// wave.  Ends with a workgroup barrier, so LDS may be reused at once.
 template <int BM, int BN, class BeforeStep>
 __device__ inline void gemm_tile(Acc<BM, BN>& acc, const Operands& op, int64_t m0, uint16_t* lds,
                                  BeforeStep before_step) {
   using C = TileCfg<BM, BN>;
+  uint8_t* l8 = reinterpret_cast<uint8_t*>(lds);
   acc_zero(acc);
   const TileAddr<BM, BN> ta = tile_addr<BM, BN>(op, m0);
+  const FragAddr<BM, BN> fa = frag_addr<BM, BN>();
   const int32_t steps = (int32_t)((op.k + kBK - 1) / kBK);
-  Stage<BM, BN> st;
+  const uint32_t lbase = lds_addr(l8);
   before_step(0);
-  stage_load(st, ta, 0);
-  stage_store(st, lds);
+  stage_issue_a(ta, lbase, 0);
+  stage_issue_b(ta, lbase, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads have landed in LDS
   __syncthreads();
   for (int32_t s = 0; s < steps; ++s) {
     const bool more = s + 1 < steps;
-    if (more) {
-      before_step((int64_t)(s + 1) * kBK);
-      stage_load(st, ta, (s + 1) * kBK);
-    }
-    stage_compute(acc, lds + (s & 1) * C::STAGE_ELEMS, &st, more ? lds + ((s + 1) & 1) * C::STAGE_ELEMS : nullptr);
+    const int32_t k1 = (s + 1) * kBK;
+    const uint32_t next = lbase + ((s + 1) & 1) * C::STAGE_BYTES;
+    stage_compute(
+        acc, l8 + (s & 1) * C::STAGE_BYTES, fa,
+        [&] {
+          if (more) {
+            before_step((int64_t)k1);
+            stage_issue_a(ta, next, k1);
+          }
+        },
+        [&] {
+          if (more) stage_issue_b(ta, next, k1);
+        });
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 }
