@@ -188,9 +188,12 @@ __device__ void a2a_produce(const A2aArgs& a, const Geometry* g, int w, int P) {
     }
     const int need = g->chunk_base[pos + 1] - g->chunk_base[pos];
     const int64_t old = wg_arrive(a.counters + s);
-    if (threadIdx.x == 0 && old + 1 == need)
+    if (threadIdx.x == 0 && old + 1 == need) {
+      // Last chunk of the slice: acquire the other arrivals, then publish.
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       __hip_atomic_store(a.flags + (int64_t)s * a.flag_stride, a.epoch, __ATOMIC_RELEASE,
                          __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -281,7 +284,9 @@ extern "C" ovl_status a2a_dispatch_grouped_gemm_run(const a2a_desc* d, const voi
                                                     int32_t* recv_src, int32_t* recv_count, float* y,
                                                     int64_t* flags, void* workspace, int64_t epoch,
                                                     const ovl_opts* opts, hipStream_t stream) {
-  if (!d || !x || !topk_idx || !recv_x || !recv_src || !recv_count || !flags || !workspace) return OVL_EINVAL;
+  if (!d || !recv_count || !flags || !workspace) return OVL_EINVAL;
+  const bool empty = d->tokens == 0;  // nothing to read or write but counts and flags
+  if (!empty && (!x || !topk_idx || !recv_x || !recv_src)) return OVL_EINVAL;
   if (d->ranks < 1 || d->rank < 0 || d->rank >= d->ranks) return OVL_EINVAL;
   if (d->ranks > kA2aMaxRanks || d->experts_per_rank > kA2aMaxExperts) return OVL_EUNSUPPORTED;
   if (d->experts_per_rank < 1 || d->topk < 1 || d->topk > 8 || d->tokens < 0 ||
@@ -298,13 +303,13 @@ extern "C" ovl_status a2a_dispatch_grouped_gemm_run(const a2a_desc* d, const voi
   const uint32_t mode = opts ? opts->mode : OVL_MODE_FUSED;
   if (mode != OVL_MODE_FUSED && mode != OVL_MODE_GEMM_ONLY && mode != OVL_MODE_COPY_ONLY) return OVL_EINVAL;
   const bool gemm = mode != OVL_MODE_COPY_ONLY;
-  if (gemm && (!w || !y)) return OVL_EINVAL;
+  if (gemm && !empty && (!w || !y)) return OVL_EINVAL;
   if (!aligned16(recv_x) || !aligned16(workspace) || (gemm && (!aligned16(w) || !aligned16(y))) ||
       (reinterpret_cast<uintptr_t>(flags) & 7u) || (reinterpret_cast<uintptr_t>(recv_src) & 3u) ||
       (reinterpret_cast<uintptr_t>(recv_count) & 3u))
     return OVL_EALIGN;
   for (int s = 0; s < d->ranks; ++s) {
-    if (mode == OVL_MODE_GEMM_ONLY) break;
+    if (mode == OVL_MODE_GEMM_ONLY || empty) break;
     if (!x[s] || !topk_idx[s]) return OVL_EINVAL;
     if (!aligned16(x[s]) || (reinterpret_cast<uintptr_t>(topk_idx[s]) & 3u)) return OVL_EALIGN;
   }
@@ -314,7 +319,7 @@ extern "C" ovl_status a2a_dispatch_grouped_gemm_run(const a2a_desc* d, const voi
 
   A2aArgs a = {};
   for (int s = 0; s < d->ranks; ++s) {
-    if (mode == OVL_MODE_GEMM_ONLY) break;
+    if (mode == OVL_MODE_GEMM_ONLY || empty) break;
     a.x[s] = static_cast<const uint16_t*>(x[s]);
     a.topk[s] = topk_idx[s];
   }

@@ -49,30 +49,34 @@ enum { kModeFused = 0, kModeBarrier = 1, kModeGemmOnly = 2 };
 // ---------------------------------------------------------------- producer
 
 // Copies rows x cols bf16 (cols a multiple of 8) between two row-major
-// matrices of row pitch ld, 16 bytes per lane, 8 vectors in flight per lane.
+// matrices of row pitch ld, 16 bytes per lane and 16 vectors in flight per
+// lane; the (row, vector) position advances incrementally, without a
+// division per vector.
 __device__ inline void copy_block(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int64_t rows,
                                   int64_t cols, int64_t ld) {
-  constexpr int U = 8;
+  constexpr int U = 16;
   const uint32_t vpr = (uint32_t)(cols / 8);
   const uint32_t total = (uint32_t)(rows * vpr);
+  const uint32_t step_r = kThreads / vpr, step_c = kThreads % vpr;
+  uint32_t r = threadIdx.x / vpr, c = threadIdx.x % vpr;
   for (uint32_t base = 0; base < total; base += kThreads * U) {
     u32x4 v[U];
+    uint32_t rr[U], cc[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const uint32_t idx = base + j * kThreads + threadIdx.x;
-      if (idx < total) {
-        const uint32_t r = idx / vpr, c = idx - r * vpr;
-        v[j] = ld16_nt(src + r * ld + c * 8);
+      rr[j] = r;
+      cc[j] = c;
+      if (base + j * kThreads + threadIdx.x < total) v[j] = ld16_nt(src + r * ld + c * 8);
+      c += step_c;
+      r += step_r;
+      if (c >= vpr) {
+        c -= vpr;
+        ++r;
       }
     }
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const uint32_t idx = base + j * kThreads + threadIdx.x;
-      if (idx < total) {
-        const uint32_t r = idx / vpr, c = idx - r * vpr;
-        st16(dst + r * ld + c * 8, v[j]);
-      }
-    }
+    for (int j = 0; j < U; ++j)
+      if (base + j * kThreads + threadIdx.x < total) st16(dst + rr[j] * ld + cc[j] * 8, v[j]);
   }
 }
 
@@ -202,6 +206,7 @@ __device__ void consume(const AgArgs& a, int cidx, uint16_t* lds) {
     int last_batch = -1;
     auto before_step = [&](int64_t k0) {
       if (MODE != kModeFused || own || timed_out) return;
+      if (threadIdx.x >= 64) return;  // wave 0 waits for the workgroup (see gemm_tile)
       const int bt = (int)(k0 / a.batch_cols);
       if (bt == last_batch) return;
       last_batch = bt;

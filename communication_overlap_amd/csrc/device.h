@@ -65,25 +65,38 @@ __device__ inline bool wave_wait(const int64_t* flag, int64_t epoch, uint64_t sp
   return ok;
 }
 
+// Waits until this wave's outstanding memory operations have completed
+// (stores included: they have reached the L2 of this die).
+__device__ inline void wave_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Workgroup-level publish: every thread calls this after its own stores of
-// the unit.  Each wave releases its stores at agent scope (waits for them and
-// writes back its L2), the workgroup barrier orders all waves before thread
-// 0, and thread 0 stores the epoch with release semantics.
+// the unit.  Each wave drains its stores, the workgroup barrier orders all of
+// them before thread 0, and thread 0 issues one agent-scope release fence
+// (which writes this die's L2 back, so that the other dies see the data)
+// followed by the flag store.  One writeback per unit rather than one per
+// wave keeps the release cheap; the barrier carries the other waves' stores
+// into thread 0's release (scope inclusion: workgroup scope, then agent).
 __device__ inline void wg_publish(int64_t* flag, int64_t epoch) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  wave_drain();
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
-// Workgroup-level arrival on a counter: like wg_publish, but thread 0 adds 1
-// to `counter` (release) and returns the value it observed before the add
-// (only thread 0's return value is meaningful).
+// Workgroup-level arrival on a counter, with the same release as
+// wg_publish; thread 0 adds 1 and returns the value it observed before the
+// add, having acquired the earlier arrivals (only thread 0's value is
+// meaningful).
 __device__ inline int64_t wg_arrive(int64_t* counter) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  wave_drain();
   __syncthreads();
   int64_t old = 0;
-  if (threadIdx.x == 0)
-    old = __hip_atomic_fetch_add(counter, (int64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    old = __hip_atomic_fetch_add(counter, (int64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   return old;
 }
 

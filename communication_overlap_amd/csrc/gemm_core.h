@@ -317,9 +317,11 @@ __device__ inline void acc_zero(Acc<BM, BN>& acc) {
       for (int r = 0; r < 16; ++r) acc.v[fm][fn][r] = 0.f;
 }
 
-// The K loop of one tile.  before_step(k0) runs before the loads of the
-// K-step at k0 are issued (the consumer's flag wait goes there), in every
-// wave.  Ends with a workgroup barrier, so LDS may be reused at once.
+// The K loop of one tile.  before_step(k0) is where a consumer waits for
+// the data of the K-step at k0: every wave calls it, before a workgroup
+// barrier that precedes the first load of that step, one step ahead of the
+// loads (so a wave that acquires there orders the whole workgroup's loads).
+// Ends with a workgroup barrier, so LDS may be reused at once.
 template <int BM, int BN, class BeforeStep>
 __device__ inline void gemm_tile(Acc<BM, BN>& acc, const Operands& op, int64_t m0, uint16_t* lds,
                                  BeforeStep before_step) {
@@ -331,8 +333,10 @@ __device__ inline void gemm_tile(Acc<BM, BN>& acc, const Operands& op, int64_t m
   const int32_t steps = (int32_t)((op.k + kBK - 1) / kBK);
   const uint32_t lbase = lds_addr(l8);
   before_step(0);
+  __syncthreads();
   stage_issue_a(ta, lbase, 0);
   stage_issue_b(ta, lbase, 0);
+  if (steps > 1) before_step(kBK);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads have landed in LDS
   __syncthreads();
   for (int32_t s = 0; s < steps; ++s) {
@@ -342,14 +346,12 @@ __device__ inline void gemm_tile(Acc<BM, BN>& acc, const Operands& op, int64_t m
     stage_compute(
         acc, l8 + (s & 1) * C::STAGE_BYTES, fa,
         [&] {
-          if (more) {
-            before_step((int64_t)k1);
-            stage_issue_a(ta, next, k1);
-          }
+          if (more) stage_issue_a(ta, next, k1);
         },
         [&] {
           if (more) stage_issue_b(ta, next, k1);
         });
+    if (s + 2 < steps) before_step((int64_t)(s + 2) * kBK);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }

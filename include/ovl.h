@@ -254,7 +254,9 @@ size_t a2a_workspace_bytes(const a2a_desc* desc);
  * w:        bf16 [experts_per_rank][hidden][n].
  * recv_x:   bf16 [R][cap][hidden];  recv_src: int32 [R][cap] source token ids;
  * recv_count: int32 [R][experts_per_rank];  y: fp32 [R][cap][n].
- * flags:    a2a_flags_bytes(desc) bytes, slot s = slice from source s. */
+ * flags:    a2a_flags_bytes(desc) bytes, slot s = slice from source s.
+ * With tokens = 0 the row buffers (x, topk_idx, w, recv_x, recv_src, y) may
+ * be NULL; counts are zeroed and every slice flag is still set. */
 ovl_status a2a_dispatch_grouped_gemm_run(const a2a_desc* desc, const void* const* x,
                                          const int32_t* const* topk_idx, const void* w,
                                          void* recv_x, int32_t* recv_src, int32_t* recv_count,
