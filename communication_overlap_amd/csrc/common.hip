@@ -113,6 +113,7 @@ extern "C" ovl_status ovl_flags_reset(int64_t* flags, size_t flag_bytes, void* w
   st = zero_async(workspace, ws_bytes, stream);
   if (st) return st;
   if (flags) epoch_forget(flags);
+  if (workspace) epoch_forget(workspace);
   return OVL_OK;
 }
 

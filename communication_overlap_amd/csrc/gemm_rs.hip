@@ -1,14 +1,23 @@
 // GEMM -> ReduceScatter with tile-level overlap ("Triton-distributed
 // Semantics", Kernel Design Patterns, "GEMM and ReduceScatter Overlapping").
 //
-// One persistent launch of consumer-style GEMM workgroups.  The local
-// product's rows split into R blocks; tiles of the blocks destined for peers
-// come first, starting at block rank+1 (the mirror of the all-gather's
-// swizzle), and the own block comes last.
-//   - Peer tile: the fp32 tile is stored to that peer's partial buffer, then
-//     its out flag is published (put + signal).
-//   - Own tile: every wave waits (acquire) on the tile's in flag of each
-//     peer, then writes acc + P_q for q != rank in ascending q, in fp32.
+// One persistent launch of GEMM workgroups.  The local product's rows split
+// into R blocks; tiles of the blocks destined for peers come first, starting
+// at block rank+1 (the mirror of the all-gather's swizzle), and the own
+// block comes last.
+//   - Peer tile: the fp32 tile is stored to that peer's partial buffer and
+//     its out flag is published (put + signal).  Then the workgroup runs one
+//     reduce job: the own block's tile rows are split evenly over all peer
+//     tiles, and job j sums, for its share of rows, the peers' partials
+//     (after their in flags) in ascending peer order, S = P_a + P_b + ...,
+//     into `out`, and publishes a job flag in the workspace.  This spreads
+//     the reading of the R-1 partials over the whole launch instead of
+//     leaving it to the few workgroups that finish the own block.
+//   - Own tile: wave 0 waits for the jobs that cover the tile, then every
+//     lane writes out = acc + S.  The job flags live in the workspace and are
+//     used in every mode, so the workspace too needs a new epoch per run.
+// Every output element is therefore acc + (((P_a + P_b) + ...)) in fp32, in
+// this fixed order, whatever the timing.
 #include <algorithm>
 
 #include "device.h"
@@ -31,6 +40,7 @@ struct RsArgs {
   float* out;
   int64_t* out_flags;
   const int64_t* in_flags;
+  int64_t* job_flags;  // [jobs] in the workspace
   ErrRec* err;
   int64_t m, n, k, bm;  // bm = rows per block
   int64_t flag_stride;  // int64 slots
@@ -39,15 +49,63 @@ struct RsArgs {
   int32_t ranks, rank;
   int32_t tr, tc;       // row / column tiles per block
   int32_t workers;
-  int32_t wait_in;      // 0: do not wait on in_flags (GEMM-only timing)
+  int32_t sync;         // 0: no in/out flag traffic (measurement of the work alone)
 };
 
-template <int MODE_WAIT>
+// Own-row space: own tile t owns rows [t*256, t*256 + 256) of it (tile row
+// trow*256 + r of the block, columns of tile column tcol).  Job j of J covers
+// [j*OR/J, (j+1)*OR/J), OR = tiles_per_block * 256.
+__device__ inline int64_t job_begin(int64_t j, int64_t J, int64_t OR) { return j * OR / J; }
+__device__ inline int64_t job_of_row(int64_t q, int64_t J, int64_t OR) { return ((q + 1) * J - 1) / OR; }
+
+__device__ void reduce_job(const RsArgs& a, int64_t j, int64_t J, bool& timed_out) {
+  const int tpb = a.tr * a.tc;
+  const int64_t OR = (int64_t)tpb * kRsTile;
+  const int64_t q0 = job_begin(j, J, OR), q1 = job_begin(j + 1, J, OR);
+  // Wait for every peer's partial of the own tiles this job touches.
+  if (a.sync && threadIdx.x < 64 && !timed_out) {
+    for (int64_t t = q0 / kRsTile; t <= (q1 - 1) / kRsTile && !timed_out; ++t)
+      for (int p = 0; p < a.ranks && !timed_out; ++p) {
+        if (p == a.rank) continue;
+        const int64_t idx = (int64_t)p * tpb + t;
+        if (!wave_wait(a.in_flags + idx * a.flag_stride, a.epoch, a.spin_limit, a.err, kSiteRsIn, idx))
+          timed_out = true;
+      }
+  }
+  __syncthreads();
+  // 64 lanes of 16 bytes cover one 256-column row; 4 rows per pass.
+  const int lane = threadIdx.x & 63, rsub = threadIdx.x >> 6;
+  for (int64_t q = q0 + rsub; q < q1; q += 4) {
+    const int64_t t = q / kRsTile;
+    const int64_t row = (t / a.tc) * kRsTile + (q % kRsTile);
+    const int64_t col = (t % a.tc) * kRsTile + lane * 4;
+    if (row >= a.bm || col >= a.n) continue;
+    const int64_t off = row * a.n + col;
+    f32x4 acc4;
+    bool first = true;
+    for (int p = 0; p < a.ranks; ++p) {
+      if (p == a.rank) continue;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(a.peer_in[p] + off);
+      if (first) {
+        acc4 = v;
+        first = false;
+      } else {
+        acc4 += v;
+      }
+    }
+    *reinterpret_cast<f32x4*>(a.out + off) = acc4;
+  }
+  wg_publish(a.job_flags + j, a.epoch);
+}
+
+template <int SYNC>
 __global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
   constexpr int BM = kRsTile, BN = kRsTile;
   const int tpb = a.tr * a.tc;
   const int64_t total = (int64_t)a.ranks * tpb;
+  const int64_t J = (int64_t)(a.ranks - 1) * tpb;  // reduce jobs = peer tiles
+  const int64_t OR = (int64_t)tpb * kRsTile;
   const int Cn = a.workers;
   const int groups = (Cn % kRsXcds == 0) ? kRsXcds : 1;
   const int per = Cn / groups;
@@ -77,27 +135,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs a) {
     gemm_tile<BM, BN>(acc, op, m0, lds, [](int64_t) {});
 
     if (blk != a.rank) {
-      float* dst = a.peer_out[blk];
-      acc_store<BM, BN>(acc, dst, a.n, m0, op.n0, a.bm, a.n);
-      wg_publish(a.out_flags + ((int64_t)blk * tpb + t) * a.flag_stride, a.epoch);
+      acc_store<BM, BN>(acc, a.peer_out[blk], a.n, m0, op.n0, a.bm, a.n);
+      if (SYNC) wg_publish(a.out_flags + ((int64_t)blk * tpb + t) * a.flag_stride, a.epoch);
+      reduce_job(a, j, J, timed_out);  // j < J: peer tiles come first
     } else {
-      if (MODE_WAIT) {
-        for (int p = 0; p < a.ranks && !timed_out; ++p) {
-          if (p == a.rank) continue;
-          const int64_t idx = (int64_t)p * tpb + t;
-          if (!wave_wait(a.in_flags + idx * a.flag_stride, a.epoch, a.spin_limit, a.err, kSiteRsIn, idx))
-            timed_out = true;
+      if (J > 0) {
+        if (threadIdx.x < 64 && !timed_out) {
+          const int64_t j0 = job_of_row((int64_t)t * kRsTile, J, OR);
+          const int64_t j1 = job_of_row((int64_t)t * kRsTile + kRsTile - 1, J, OR);
+          for (int64_t jj = j0; jj <= j1 && !timed_out; ++jj)
+            if (!wave_wait(a.job_flags + jj, a.epoch, a.spin_limit, a.err, kSiteRsJob, jj)) timed_out = true;
         }
+        __syncthreads();
+        const OutTile o = out_tile(a.out, a.n, m0, op.n0, a.bm, a.n);
+        acc_foreach(acc, [&](int row, int col, float v) {
+          const uint32_t off = out_off(o, row, col);
+          bstoref(o.r, off, v + bloadf(o.r, off));
+        });
+      } else {
+        acc_store<BM, BN>(acc, a.out, a.n, m0, op.n0, a.bm, a.n);
       }
-      const OutTile o = out_tile(a.out, a.n, m0, op.n0, a.bm, a.n);
-      rsrc_t rin[kRsMaxRanks];
-      for (int p = 0; p < a.ranks; ++p) rin[p] = make_rsrc(p == a.rank ? a.out : a.peer_in[p], a.bm * a.n * 4);
-      acc_foreach(acc, [&](int row, int col, float v) {
-        const uint32_t off = out_off(o, row, col);
-        for (int p = 0; p < a.ranks; ++p)
-          if (p != a.rank) v += bloadf(rin[p], off);
-        bstoref(o.r, off, v);
-      });
     }
   }
 }
@@ -117,7 +174,13 @@ extern "C" size_t gemm_rs_flags_bytes(const gemm_rs_desc* d) {
   return (size_t)(d->ranks * tpb * d->flag_stride);
 }
 
-extern "C" size_t gemm_rs_workspace_bytes(const gemm_rs_desc* d) { return d ? 256 : 0; }
+// Error record, then one int64 flag per reduce job (one per peer tile).
+extern "C" size_t gemm_rs_workspace_bytes(const gemm_rs_desc* d) {
+  if (!d || d->ranks < 1 || d->m < 1 || d->n < 1 || d->m % d->ranks) return 0;
+  const int64_t bm = d->m / d->ranks;
+  const int64_t tpb = ceil_div(bm, kRsTile) * ceil_div(d->n, kRsTile);
+  return OVL_ERROR_RECORD_BYTES + 8 * (size_t)((d->ranks - 1) * tpb);
+}
 
 extern "C" ovl_status gemm_rs_run(const gemm_rs_desc* d, const void* a, const void* b, float* const* peer_out,
                                   const float* const* peer_in, float* out, int64_t* out_flags,
@@ -162,6 +225,7 @@ extern "C" ovl_status gemm_rs_run(const gemm_rs_desc* d, const void* a, const vo
   r.out_flags = out_flags;
   r.in_flags = in_flags;
   r.err = static_cast<ErrRec*>(workspace);
+  r.job_flags = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(workspace) + OVL_ERROR_RECORD_BYTES);
   r.m = d->m;
   r.n = d->n;
   r.k = d->k;
@@ -173,7 +237,7 @@ extern "C" ovl_status gemm_rs_run(const gemm_rs_desc* d, const void* a, const vo
   r.rank = d->rank;
   r.tr = (int32_t)ceil_div(r.bm, kRsTile);
   r.tc = (int32_t)ceil_div(d->n, kRsTile);
-  r.wait_in = mode == OVL_MODE_FUSED;
+  r.sync = mode == OVL_MODE_FUSED;
 
   const int lds = rs_lds_bytes();
   const void* fn = (mode == OVL_MODE_FUSED) ? reinterpret_cast<const void*>(&gemm_rs_kernel<1>)
@@ -188,12 +252,14 @@ extern "C" ovl_status gemm_rs_run(const gemm_rs_desc* d, const void* a, const vo
   int64_t workers = std::min<int64_t>(total, (int64_t)std::max(occ, 1) * di.cus);
   if (workers > kRsXcds) workers -= workers % kRsXcds;
   r.workers = (int32_t)workers;
-  if (d->ranks > 1) {
+  st = epoch_check(workspace, epoch);
+  if (st) return st;
+  if (d->ranks > 1 && mode == OVL_MODE_FUSED) {
     st = epoch_accept(out_flags, epoch);
     if (st) return st;
-  } else if (epoch < 1) {
-    return OVL_EEPOCH;
   }
+  st = epoch_accept(workspace, epoch);
+  if (st) return st;
   if (mode == OVL_MODE_FUSED)
     hipLaunchKernelGGL(gemm_rs_kernel<1>, dim3(workers), dim3(kThreads), lds, stream, r);
   else

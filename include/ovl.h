@@ -182,7 +182,7 @@ ovl_status ag_gemm_run(ag_gemm_plan_t plan, const void* const* shards, const voi
  * p != rank is a partial destined for rank p: each tile of it is stored to
  * peer_out[p] and signalled in out_flags (put + signal).  For its own block
  * the rank waits for every peer's partial tile (in_flags) and writes
- *   out = L[rank block] + sum over p != rank, ascending, of peer_in[p]
+ *   out = L[rank block] + (sum over p != rank, ascending, of peer_in[p])
  * in fp32.  Tiles of peer blocks are computed first, starting at block
  * rank+1; the own block comes last.
  *
@@ -210,6 +210,15 @@ size_t gemm_rs_workspace_bytes(const gemm_rs_desc* desc);
  *           their in_flags slot reaches `epoch`.
  * out:      fp32 [m/R][n].
  * out_flags: written (epoch) per sent tile.  in_flags: read only.
+ * workspace: gemm_rs_workspace_bytes(desc) bytes: besides the error record
+ *           it holds one flag per peer tile, so successive runs on one
+ *           workspace need increasing epochs too (ovl_flags_reset restarts).
+ * The reduction of the peers' partials is spread over the workgroups that
+ * computed peer tiles: each sums, in ascending peer order, the partials of a
+ * contiguous share of the own block's rows into `out`, and the own block's
+ * tiles then add their accumulators, so out = acc + ((P_a + P_b) + ...).
+ * Modes: FUSED, or GEMM_ONLY (same work and result, without in/out flag
+ * traffic).
  * Errors as for ag_gemm_run; EUNSUPPORTED if tile_m/tile_n are not 256, if
  * m, n or k exceeds 2^20, or if A, B or the local product exceeds 1 GiB. */
 ovl_status gemm_rs_run(const gemm_rs_desc* desc, const void* a, const void* b,
@@ -276,8 +285,10 @@ ovl_status ovl_flags_reset(int64_t* flags, size_t flag_bytes, void* workspace, s
                            hipStream_t stream);
 
 /* Waits for `stream`, then returns the status recorded on the device in
- * `workspace` (OVL_OK or OVL_ETIMEOUT).  detail (HOST, may be NULL) receives
- * {site, flag index, observed value, awaited value}. */
+ * `workspace` (OVL_OK or OVL_ETIMEOUT; the first wait to give up wins).
+ * detail (HOST, may be NULL) receives {site, flag index, observed value,
+ * awaited value}; sites: 1 AG-GEMM unit flag, 2 AG-GEMM barrier mode,
+ * 3 GEMM-RS in flag, 4 dispatch slice flag, 5 GEMM-RS reduce-job flag. */
 ovl_status ovl_check(const void* workspace, int64_t* detail, hipStream_t stream);
 
 const char* ovl_strerror(ovl_status status);
