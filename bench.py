@@ -30,6 +30,24 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, published
 METRIC = "fused AG-GEMM TFLOP/s (% bf16 MFMA peak) + overlap eff. vs copy+GEMM serial"
 
+# HBM bytes per launch of the fused 8192x3584x4096 kernel, from two rocprofv3
+# --pmc passes (FETCH_SIZE x 2.00 + WRITE_SIZE x 1.00, the factors a plain
+# 256 MiB copy reads on the same counters), and the hash of the kernel
+# sources they were taken on; reported only while the sources are unchanged.
+TRAFFIC_BYTES = (352453 * 2.0 + 180240 * 1.0) * 1024
+TRAFFIC_SOURCES_SHA = "38eaa3f1c85ceb8a"
+KERNEL_SOURCES = ("communication_overlap_amd/csrc/ag_gemm.hip", "communication_overlap_amd/csrc/gemm_core.h",
+                  "communication_overlap_amd/csrc/device.h")
+
+
+def kernel_sources_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -213,7 +231,10 @@ def main():
                    "tiles_per_flag": 1},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": (TRAFFIC_BYTES if kernel_sources_sha() == TRAFFIC_SOURCES_SHA else None),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-scaled)",
+                     "algorithmic_flops_per_launch": cfg.flops(),
                      "kernel": "ag_gemm_kernel<256,256,fused>", "avg_launch_us": round(kern_us, 2)},
         "overlap": overlap,
         "side": extra,
