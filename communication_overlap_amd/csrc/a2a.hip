@@ -252,7 +252,7 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
 template <int MODE>  // 0 fused, 2 GEMM only
 __global__ __launch_bounds__(kThreads, 1) void a2a_fused_kernel(A2aArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
-  Geometry* g = reinterpret_cast<Geometry*>(lds + 2 * TileCfg<kGbm, kGbn>::STAGE_ELEMS);
+  Geometry* g = reinterpret_cast<Geometry*>(reinterpret_cast<uint8_t*>(lds) + TileCfg<kGbm, kGbn>::LDS_BYTES);
   build_geometry(a, g);
   if ((int)blockIdx.x < a.producers) {
     a2a_produce(a, g, blockIdx.x, a.producers);

@@ -2,10 +2,11 @@
 // ("Triton-distributed Semantics", Kernel Design Patterns, "AllGather and
 // GEMM Overlapping"; Producer-Consumer Model; Threadblock Swizzling).
 //
-// One persistent launch.  Workgroups [0, P) are producers: they take flag
-// units in the caller's producer order, copy each unit's rows and K-range
-// from its shard into the gathered buffer with 16-byte vectors, and publish
-// the unit's flag (agent-scope release).  Workgroups [P, P + C) are
+// One persistent launch.  All workgroups first copy, together, the units the
+// first round of consumer tiles needs; then workgroups [0, P) are producers:
+// they take the remaining flag units in the caller's producer order, copy
+// each unit's rows and K-range from its shard into the gathered buffer with
+// 16-byte vectors, and publish the unit's flag (agent-scope release).  Workgroups [P, P + C) are
 // consumers: each computes output tiles in arrival order; before the K-step
 // that enters a new K-batch it waits (wave-level acquire) on every unit that
 // covers the tile's rows in that batch, then loads the A tile from the
@@ -80,24 +81,60 @@ __device__ inline void copy_block(const uint16_t* __restrict__ src, uint16_t* __
   }
 }
 
-__device__ inline void produce(const AgArgs& a, int w, int P) {
+// What every workgroup knows of the schedule (tables in LDS, built by
+// build_schedule): the row tiles in consumer order, each row tile's position
+// in it, and the bootstrap: the panels (sp = shard * panels + panel) that the
+// first round of consumer tiles reads, whose units all workgroups move
+// together before anything else.
+struct Sched {
+  int* sorted;         // [tiles_m] row tiles in consumer order
+  int* pos;            // [tiles_m] position of each row tile in `sorted`
+  int* boot;           // [n_boot] bootstrap panels, ascending
+  int* bidx;           // [ranks * panels] index in `boot`, or -1
+  uint32_t* present;   // bit i * batches + bt: unit (boot[i], bt) occurs in the producer order
+  int n_boot;
+  int rows1;           // row-tile positions [0, rows1) are read by the first round
+};
+
+constexpr int kBootBits = 2048 * 32;  // presence bitmap: n_boot * batches <= this
+
+// Copies one flag unit into the gathered buffer and publishes its flag.
+__device__ inline void move_unit(const AgArgs& a, int u) {
+  const int bt = u % a.batches;
+  const int sp = u / a.batches;
+  const int p = sp % a.panels;
+  const int s = sp / a.panels;
+  const int64_t r0 = (int64_t)p * a.unit_rows;
+  const int64_t rows = min((int64_t)a.unit_rows, a.shard_m - r0);
+  const int64_t c0 = (int64_t)bt * a.batch_cols;
+  const int64_t cols = min((int64_t)a.batch_cols, a.k - c0);
+  copy_block(a.shards[s] + r0 * a.k + c0, a.g + ((int64_t)s * a.shard_m + r0) * a.k + c0, rows, cols, a.k);
+  wg_publish(a.flags + (int64_t)u * a.flag_stride, a.epoch);
+}
+
+// Moves the units at producer-order positions w, w + P, ..., skipping the
+// bootstrap panels' units when sc is given (those were moved already).
+__device__ inline void produce(const AgArgs& a, int w, int P, const Sched* sc) {
   for (int i = w; i < a.num_units; i += P) {
     const int u = a.order ? a.order[i] : i;
     if (u < 0 || u >= a.num_units) continue;  // not a unit index: nothing to move
-    const int bt = u % a.batches;
-    const int sp = u / a.batches;
-    const int p = sp % a.panels;
-    const int s = sp / a.panels;
-    const int64_t r0 = (int64_t)p * a.unit_rows;
-    const int64_t rows = min((int64_t)a.unit_rows, a.shard_m - r0);
-    const int64_t c0 = (int64_t)bt * a.batch_cols;
-    const int64_t cols = min((int64_t)a.batch_cols, a.k - c0);
-    copy_block(a.shards[s] + r0 * a.k + c0, a.g + ((int64_t)s * a.shard_m + r0) * a.k + c0, rows, cols, a.k);
-    wg_publish(a.flags + (int64_t)u * a.flag_stride, a.epoch);
+    if (sc && sc->bidx[u / a.batches] >= 0) continue;
+    move_unit(a, u);
   }
 }
 
-__global__ __launch_bounds__(kThreads) void ag_produce_kernel(AgArgs a) { produce(a, blockIdx.x, gridDim.x); }
+// Bootstrap: workgroup w of G moves the bootstrap units number w, w + G, ...
+// (every K-batch of every bootstrap panel, panel-major) that occur in the
+// producer order; a unit the order omits stays unmoved.
+__device__ inline void produce_boot(const AgArgs& a, int w, int G, const Sched& sc) {
+  const int items = sc.n_boot * a.batches;
+  for (int i = w; i < items; i += G)
+    if ((sc.present[i >> 5] >> (i & 31)) & 1u) move_unit(a, sc.boot[i / a.batches] * a.batches + i % a.batches);
+}
+
+__global__ __launch_bounds__(kThreads) void ag_produce_kernel(AgArgs a) {
+  produce(a, blockIdx.x, gridDim.x, nullptr);
+}
 
 // ---------------------------------------------------------------- consumer order
 
@@ -108,16 +145,44 @@ __device__ inline bool row_tile_own(const AgArgs& a, int BM, int rt) {
   return lo >= (int64_t)a.rank * a.shard_m && hi <= (int64_t)(a.rank + 1) * a.shard_m;
 }
 
-// Fills sorted[0 .. tiles_m) with the row tiles in consumer order: own tiles
-// first (ascending), then the others by the latest producer-order position
-// among the first-K-batch units covering their rows (ties by index).
-__device__ void build_consumer_order(const AgArgs& a, int BM, int* key, int* sorted) {
+// True when a consumer of the first round reads panel sp from the gathered
+// buffer: some row tile that the panel's rows fall in is in the first round
+// and is not an own tile (own tiles read the own shard directly).
+__device__ inline bool panel_is_boot(const AgArgs& a, int BM, const int* pos, int rows1, int sp) {
+  const int p = sp % a.panels, s = sp / a.panels;
+  const int64_t r_lo = (int64_t)s * a.shard_m + (int64_t)p * a.unit_rows;
+  const int64_t r_hi = min(r_lo + a.unit_rows, (int64_t)(s + 1) * a.shard_m);
+  for (int rt = (int)(r_lo / BM); rt <= (int)((r_hi - 1) / BM); ++rt)
+    if (pos[rt] < rows1 && !row_tile_own(a, BM, rt)) return true;
+  return false;
+}
+
+// LDS the schedule tables take: the consumer order sits after the GEMM
+// stages (consumers read it throughout); the tables only the bootstrap and
+// the producers use alias the start of the stage area, which consumers
+// overwrite once the bootstrap is done.
+constexpr int kOrderBytes = kMaxRowTiles * (int)sizeof(int);
+constexpr int kBootTabBytes = (3 * kMaxRowTiles + kBootBits / 32) * (int)sizeof(int);
+
+// Builds the schedule tables in LDS at `tab` (identical in every
+// workgroup).  The consumer order puts the own row tiles first (ascending),
+// then the others by the latest producer-order position among the
+// first-K-batch units that cover their rows (ties by index).  The bootstrap
+// is left empty when `with_boot` is false or the panels outnumber the
+// table, and keeps only as many panels as the presence bitmap holds.
+__device__ Sched build_schedule(const AgArgs& a, int BM, int* sorted, int* tab, bool with_boot) {
+  __shared__ int s_nboot;
+  __shared__ int s_wave[kThreads / 64];
+  int* key = tab;  // reused as bidx once the order is known
+  int* pos = tab + kMaxRowTiles;
+  int* boot = pos + kMaxRowTiles;
+  uint32_t* present = reinterpret_cast<uint32_t*>(boot + kMaxRowTiles);
   const int T = a.tiles_m;
-  for (int rt = threadIdx.x; rt < T; rt += kThreads) key[rt] = row_tile_own(a, BM, rt) ? -1 : 0;
+  for (int rt = threadIdx.x; rt < T; rt += blockDim.x) key[rt] = row_tile_own(a, BM, rt) ? -1 : 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < a.num_units; i += kThreads) {
+  for (int i = threadIdx.x; i < a.num_units; i += blockDim.x) {
     const int u = a.order ? a.order[i] : i;
-    if (u < 0 || u >= a.num_units || u % a.batches) continue;
+    if (u < 0 || u >= a.num_units || u % a.batches != 0) continue;
     const int sp = u / a.batches;
     const int p = sp % a.panels, s = sp / a.panels;
     const int64_t r_lo = (int64_t)s * a.shard_m + (int64_t)p * a.unit_rows;
@@ -126,7 +191,7 @@ __device__ void build_consumer_order(const AgArgs& a, int BM, int* key, int* sor
       if (key[rt] >= 0) atomicMax(&key[rt], i);
   }
   __syncthreads();
-  for (int rt = threadIdx.x; rt < T; rt += kThreads) {
+  for (int rt = threadIdx.x; rt < T; rt += blockDim.x) {
     const int k0 = key[rt];
     int rank = 0;
     for (int q = 0; q < T; ++q) {
@@ -134,18 +199,69 @@ __device__ void build_consumer_order(const AgArgs& a, int BM, int* key, int* sor
       rank += (kq < k0) || (kq == k0 && q < rt);
     }
     sorted[rank] = rt;
+    pos[rt] = rank;
+  }
+  const int64_t round1 = min((int64_t)a.consumers, (int64_t)a.tiles_m * a.tiles_n);
+  const int rows1 = (int)((round1 + a.tiles_n - 1) / a.tiles_n);
+  const int SP = a.ranks * a.panels;
+  const bool boot_on = with_boot && SP <= kMaxRowTiles;
+  if (threadIdx.x == 0) s_nboot = 0;
+  __syncthreads();  // key is no longer needed: it becomes bidx
+  int* bidx = key;
+  if (boot_on) {
+    // Ordered compaction of the bootstrap panels: a ballot prefix per wave,
+    // then the waves in order, so every workgroup builds the same list.
+    const int wv = threadIdx.x / 64, ln = lane_id();
+    const int cap = kBootBits / a.batches;  // panels whose presence bits fit
+    for (int base = 0; base < SP; base += blockDim.x) {
+      const int sp = base + threadIdx.x;
+      const bool b = sp < SP && panel_is_boot(a, BM, pos, rows1, sp);
+      const uint64_t m = __ballot(b);
+      if (ln == 0) s_wave[wv] = __popcll(m);
+      __syncthreads();
+      int off = s_nboot;
+      for (int q = 0; q < wv; ++q) off += s_wave[q];
+      off += __popcll(m & ((1ull << ln) - 1));
+      if (sp < SP) bidx[sp] = (b && off < cap) ? off : -1;
+      if (b && off < cap) boot[off] = sp;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        int t = 0;
+        for (int q = 0; q < kThreads / 64; ++q) t += s_wave[q];
+        s_nboot = min(s_nboot + t, cap);
+      }
+      __syncthreads();
+    }
+    const int words = (s_nboot * a.batches + 31) / 32;
+    for (int i = threadIdx.x; i < words; i += blockDim.x) present[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.num_units; i += blockDim.x) {
+      const int u = a.order ? a.order[i] : i;
+      if (u < 0 || u >= a.num_units) continue;
+      const int bi = bidx[u / a.batches];
+      if (bi < 0) continue;
+      const int bit = bi * a.batches + u % a.batches;
+      atomicOr(&present[bit >> 5], 1u << (bit & 31));
+    }
+  } else {
+    for (int sp = threadIdx.x; sp < min(SP, kMaxRowTiles); sp += blockDim.x) bidx[sp] = -1;
   }
   __syncthreads();
+  Sched sc;
+  sc.sorted = sorted;
+  sc.pos = pos;
+  sc.boot = boot;
+  sc.bidx = bidx;
+  sc.present = present;
+  sc.n_boot = s_nboot;
+  sc.rows1 = rows1;
+  return sc;
 }
 
 // ---------------------------------------------------------------- consumer
 
 template <int BM, int BN, int MODE>
-__device__ void consume(const AgArgs& a, int cidx, uint16_t* lds) {
-  using C = TileCfg<BM, BN>;
-  int* key = reinterpret_cast<int*>(lds + 2 * C::STAGE_ELEMS);
-  int* sorted = key + kMaxRowTiles;
-  build_consumer_order(a, BM, key, sorted);
+__device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* lds) {
 
   bool timed_out = false;
   if (MODE == kModeBarrier) {
@@ -230,19 +346,30 @@ __device__ void consume(const AgArgs& a, int cidx, uint16_t* lds) {
   }
 }
 
+// Fused launch.  Every workgroup derives the schedule from the producer
+// order.  In FUSED and BARRIER modes all workgroups first move, together, the
+// units the first round of consumer tiles reads (the bootstrap: the whole
+// chip copies what is needed first); then producers move the remaining units
+// in the caller's order while consumers compute.
 template <int BM, int BN, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void ag_gemm_kernel(AgArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
+  using C = TileCfg<BM, BN>;
+  static_assert(kBootTabBytes <= C::LDS_BYTES, "bootstrap tables alias the stage area");
+  int* sorted = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(lds) + C::LDS_BYTES);
+  const Sched sc = build_schedule(a, BM, sorted, reinterpret_cast<int*>(lds), MODE != kModeGemmOnly);
+  if (MODE != kModeGemmOnly) produce_boot(a, blockIdx.x, gridDim.x, sc);
   if ((int)blockIdx.x < a.producers) {
-    produce(a, blockIdx.x, a.producers);
+    produce(a, blockIdx.x, a.producers, &sc);
     return;
   }
-  consume<BM, BN, MODE>(a, (int)blockIdx.x - a.producers, lds);
+  __syncthreads();  // every read of the bootstrap tables is done: the stages may be written
+  consume<BM, BN, MODE>(a, (int)blockIdx.x - a.producers, sc.sorted, lds);
 }
 
 template <int BM, int BN>
 constexpr int ag_lds_bytes() {
-  return TileCfg<BM, BN>::LDS_BYTES + 2 * kMaxRowTiles * (int)sizeof(int);
+  return TileCfg<BM, BN>::LDS_BYTES + kOrderBytes;
 }
 
 }  // namespace ovl

@@ -2,14 +2,15 @@
 //
 // One workgroup of 4 wavefronts computes a BM x BN output tile; the waves
 // form a 2 x 2 grid, each owning a (BM/2) x (BN/2) sub-tile made of 32 x 32
-// blocks computed with v_mfma_f32_32x32x16_bf16.  K advances in steps of 64
-// through a two-stage LDS ring.
+// blocks computed with v_mfma_f32_32x32x16_bf16.  K advances in steps of BK
+// through a ring of NS LDS stages (BK = 32: 4 stages, the loads of a step
+// issued three steps ahead; BK = 64: 2 stages, one step ahead).
 //
 // Both operands travel global -> LDS with buffer loads that write LDS
 // directly (16 bytes a lane; lane i of an instruction lands at byte 16*i of
 // a 1 KiB LDS block), so staging costs neither registers nor LDS-write
 // instructions:
-//   - A (row-major, K contiguous) is kept as [row][k] (128 B per row);
+//   - A (row-major, K contiguous) is kept as [row][k] (2*BK bytes per row);
 //   - B (row-major, N contiguous) is kept as [k][n] and its MFMA fragments
 //     are read with ds_read_b64_tr_b16, which transposes 4 x 4 blocks of
 //     16-bit elements across each group of 16 lanes: source lane s of a
@@ -33,7 +34,6 @@
 
 namespace ovl {
 
-constexpr int kBK = 64;                 // K per pipeline stage
 constexpr uint32_t kOOB = 0x80000000u;  // an offset past every buffer (operands are < 1 GiB)
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -83,25 +83,37 @@ __device__ inline void load_to_lds(const u32x4& srd, uint32_t lds_block, uint32_
                : "memory", "m0");
 }
 
-// Chunk permutations.  A row r (8 chunks of 16 B): physical chunk p holds
-// logical chunk p ^ swz_a(r).  B row k (BN/8 chunks): p holds p ^ swz_b(k).
-__device__ inline uint32_t swz_a(uint32_t r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Chunk permutations.  An A row r of BK bf16 (BK/8 chunks of 16 B):
+// physical chunk p holds logical chunk p ^ swz_a<BK>(r).  A B row k (BN/8
+// chunks): p holds p ^ swz_b(k).  Each is chosen so that the fragment reads
+// (16 consecutive rows at one logical chunk for A; 4 rows x 2 chunks per
+// 16-lane group for B) hit distinct banks under 32- and 64-bank LDS layouts.
+template <int BK>
+__device__ inline uint32_t swz_a(uint32_t r);
+template <>
+__device__ inline uint32_t swz_a<64>(uint32_t r) { return (r & 7) ^ ((r >> 3) & 1); }
+template <>
+__device__ inline uint32_t swz_a<32>(uint32_t r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 __device__ inline uint32_t swz_b(uint32_t k) { return (0xCA60u >> ((k & 3) * 4)) & 15; }  // 0, 6, 10, 12
 
-template <int BM, int BN>
+template <int BM, int BN, int BK = 64>
 struct TileCfg {
   static_assert(BM % 64 == 0 && BN % 128 == 0 && BN <= 256 && BM <= 256, "tile shape");
+  static_assert(BK == 32 || BK == 64, "K step");
+  static constexpr int NS = BK == 32 ? 4 : 2;     // LDS stages
   static constexpr int FM = BM / 64;             // 32-row blocks per wave
   static constexpr int FN = BN / 64;             // 32-col blocks per wave
-  static constexpr int A_BYTES = BM * kBK * 2;
-  static constexpr int B_BYTES = BN * kBK * 2;
+  static constexpr int KK = BK / 16;             // MFMA sub-steps per stage
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int B_BYTES = BN * BK * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int STAGE_ELEMS = STAGE_BYTES / 2;  // in bf16
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-  static constexpr int QA = BM / 32;             // A load instructions per wave per stage
-  static constexpr int QB = BN / 32;             // B load instructions per wave per stage
+  static constexpr int LDS_BYTES = NS * STAGE_BYTES;
+  static constexpr int A_RPI = 1024 / (BK * 2);  // A rows per load instruction
+  static constexpr int QA = BM / A_RPI / 4;      // A load instructions per wave per stage
   static constexpr int B_LPR = BN / 8;           // lanes per B row in one instruction
   static constexpr int B_RPI = 64 / B_LPR;       // B rows per instruction
+  static constexpr int QB = BK / B_RPI / 4;      // B load instructions per wave per stage
+  static constexpr int LPS = QA + QB;            // load instructions per wave per stage
 };
 
 template <int BM, int BN>
@@ -123,41 +135,43 @@ struct Operands {
 };
 
 // Per-tile, per-lane addressing of the global -> LDS loads.
-template <int BM, int BN>
+template <int BM, int BN, int BK>
 struct TileAddr {
   u32x4 ra, rb;
-  uint32_t a_off[2];   // lane offset of A instruction q = 0 / 1 at k0 = 0 (bytes), before the row step
-  uint32_t a_kc[2];    // lane's K column (elements) for even / odd instructions
-  uint32_t a_qstep;    // bytes between consecutive A instructions (8 rows)
-  uint32_t b_off[2];   // lane offset of B instruction parity 0 / 1 at k0 = 0, or kOOB past N
+  uint32_t a_off[2];   // lane offset of A instructions with index parity 0 / 1 at k0 = 0 (bytes)
+  uint32_t a_kc[2];    // lane's K column (elements) for those instructions
+  uint32_t a_qstep;    // bytes between consecutive A instructions
+  uint32_t b_off[2];   // lane offset of B instructions with index parity 0 / 1 at k0 = 0, or kOOB past N
   uint32_t b_qstep;    // bytes between consecutive B instructions
   uint32_t ldb_b;
   int32_t k;
 };
 
-template <int BM, int BN>
-__device__ inline TileAddr<BM, BN> tile_addr(const Operands& op, int64_t m0) {
-  using C = TileCfg<BM, BN>;
-  TileAddr<BM, BN> t;
+template <int BM, int BN, int BK>
+__device__ inline TileAddr<BM, BN, BK> tile_addr(const Operands& op, int64_t m0) {
+  using C = TileCfg<BM, BN, BK>;
+  TileAddr<BM, BN, BK> t;
   const uint32_t l = lane_id();
   const uint32_t w = threadIdx.x >> 6;
   t.ra = make_srd(op.a + m0 * op.lda, (op.m_valid - m0) * op.lda * 2);
   t.rb = make_srd(op.b + op.n0, op.k * op.ldb * 2 - op.n0 * 2);
   t.k = (int32_t)op.k;
-  // A: instruction iq = w*QA + q covers tile rows iq*8 .. iq*8+7; lane l
-  // fills row iq*8 + l/8, physical chunk l%8.
+  // A: instruction iq = w*QA + q covers tile rows iq*A_RPI .. +A_RPI-1; lane
+  // l fills row iq*A_RPI + l/CPR, physical chunk l%CPR (CPR = BK/8 chunks).
+  constexpr uint32_t CPR = BK / 8;
   const uint32_t lda_b = (uint32_t)(op.lda * 2);
-  for (int par = 0; par < 2; ++par) {
-    const uint32_t lc = (l & 7) ^ (l >> 3) ^ (uint32_t)par;  // swz_a of row iq*8 + l/8 for iq parity par
+  for (uint32_t par = 0; par < 2; ++par) {
+    const uint32_t row = (w * C::QA + par) * C::A_RPI + l / CPR;
+    const uint32_t lc = (l % CPR) ^ swz_a<BK>(row);
     t.a_kc[par] = lc * 8;
-    t.a_off[par] = (w * C::QA * 8 + (l >> 3)) * lda_b + lc * 16;
+    t.a_off[par] = row * lda_b + lc * 16;
   }
-  t.a_qstep = 8 * lda_b;
-  // B: instruction iq = w*QB + q covers k rows iq*RPI .. +RPI-1; lane l
-  // fills row iq*RPI + l/LPR, physical chunk l%LPR.
+  t.a_qstep = C::A_RPI * lda_b;
+  // B: instruction iq = w*QB + q covers k rows iq*B_RPI .. +B_RPI-1; lane l
+  // fills row iq*B_RPI + l/LPR, physical chunk l%LPR.
   t.ldb_b = (uint32_t)(op.ldb * 2);
-  for (int par = 0; par < 2; ++par) {
-    const uint32_t row = (w * C::QB + par) * C::B_RPI + l / C::B_LPR;  // row of instruction q = par
+  for (uint32_t par = 0; par < 2; ++par) {
+    const uint32_t row = (w * C::QB + par) * C::B_RPI + l / C::B_LPR;
     const uint32_t lc = (l % C::B_LPR) ^ swz_b(row);
     const bool nvalid = op.n0 + (int64_t)lc * 8 < op.n_valid;
     t.b_off[par] = nvalid ? row * t.ldb_b + lc * 16 : kOOB;
@@ -168,49 +182,85 @@ __device__ inline TileAddr<BM, BN> tile_addr(const Operands& op, int64_t m0) {
 
 // Issues this wave's share of the global -> LDS loads of the K-step at k0:
 // the A part and the B part separately, so that each can sit under MFMAs.
-template <int BM, int BN>
-__device__ inline void stage_issue_a(const TileAddr<BM, BN>& t, uint32_t stage, int32_t k0) {
-  using C = TileCfg<BM, BN>;
+// The swizzle of an instruction's rows depends on the instruction index only
+// through its parity (even QA / QB and row counts), hence the two variants.
+template <int BM, int BN, int BK>
+__device__ inline void stage_issue_a(const TileAddr<BM, BN, BK>& t, uint32_t stage, int32_t k0) {
+  using C = TileCfg<BM, BN, BK>;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int q = 0; q < C::QA; ++q) {
-    const int par = q & 1;  // the instruction index parity equals q's (QA is even)
-    const uint32_t off = (k0 + (int32_t)t.a_kc[par] < t.k) ? t.a_off[par] + q * t.a_qstep + (uint32_t)k0 * 2 : kOOB;
+    const int par = q & 1;
+    const uint32_t off =
+        (k0 + (int32_t)t.a_kc[par] < t.k) ? t.a_off[par] + (q & ~1) * t.a_qstep + (uint32_t)k0 * 2 : kOOB;
     load_to_lds(t.ra, stage + (w * C::QA + q) * 1024, off);
   }
 }
 
-template <int BM, int BN>
-__device__ inline void stage_issue_b(const TileAddr<BM, BN>& t, uint32_t stage, int32_t k0) {
-  using C = TileCfg<BM, BN>;
+template <int BM, int BN, int BK>
+__device__ inline void stage_issue_b(const TileAddr<BM, BN, BK>& t, uint32_t stage, int32_t k0) {
+  using C = TileCfg<BM, BN, BK>;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t sb = stage + C::A_BYTES;
   const uint32_t kb = (uint32_t)k0 * t.ldb_b;
 #pragma unroll
   for (int q = 0; q < C::QB; ++q) {
-    const int par = q & 1;  // B_RPI is even, so swz_b depends on q only through its parity
+    const int par = q & 1;
     load_to_lds(t.rb, sb + (w * C::QB + q) * 1024, t.b_off[par] + (q & ~1) * t.b_qstep + kb);
   }
 }
 
-// Per-lane LDS read offsets (bytes, within a stage) of the MFMA fragments.
-template <int BM, int BN>
-struct FragAddr {
-  uint32_t a[4];         // A fragment of sub-step kk (add fm * 32 rows * 128 B)
-  uint32_t b[TileCfg<BM, BN>::FN];  // B: row (h*8 + s/4), chunk for block fn (add kk*16 rows)
+// One load instruction of a stage: q < QA is A instruction q, otherwise B
+// instruction q - QA.
+template <int BM, int BN, int BK, int Q>
+__device__ inline void stage_issue_one(const TileAddr<BM, BN, BK>& t, uint32_t stage, int32_t k0) {
+  using C = TileCfg<BM, BN, BK>;
+  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if constexpr (Q < C::QA) {
+    constexpr int par = Q & 1;
+    const uint32_t off =
+        (k0 + (int32_t)t.a_kc[par] < t.k) ? t.a_off[par] + (Q & ~1) * t.a_qstep + (uint32_t)k0 * 2 : kOOB;
+    load_to_lds(t.ra, stage + (w * C::QA + Q) * 1024, off);
+  } else {
+    constexpr int q = Q - C::QA, par = q & 1;
+    load_to_lds(t.rb, stage + C::A_BYTES + (w * C::QB + q) * 1024,
+                t.b_off[par] + (q & ~1) * t.b_qstep + (uint32_t)k0 * t.ldb_b);
+  }
+}
+
+// The loads of one stage, to be spread over the MFMA groups of the step
+// before (on == false: nothing to load).
+template <int BM, int BN, int BK>
+struct Prefetch {
+  const TileAddr<BM, BN, BK>* t;
+  uint32_t slot;
+  int32_t k0;
+  bool on;
+  template <int Q>
+  __device__ inline void issue() const {
+    if (on) stage_issue_one<BM, BN, BK, Q>(*t, slot, k0);
+  }
 };
 
-template <int BM, int BN>
-__device__ inline FragAddr<BM, BN> frag_addr() {
-  using C = TileCfg<BM, BN>;
-  FragAddr<BM, BN> f;
+// Per-lane LDS read offsets (bytes, within a stage) of the MFMA fragments.
+template <int BM, int BN, int BK>
+struct FragAddr {
+  uint32_t a[BK / 16];               // A fragment of sub-step kk (add fm * 32 rows)
+  uint32_t b[TileCfg<BM, BN, BK>::FN];  // B: row (h*8 + s/4), chunk for block fn (add kk*16 rows)
+};
+
+template <int BM, int BN, int BK>
+__device__ inline FragAddr<BM, BN, BK> frag_addr() {
+  using C = TileCfg<BM, BN, BK>;
+  FragAddr<BM, BN, BK> f;
   const uint32_t l = lane_id();
   const uint32_t wave = threadIdx.x >> 6;
   const uint32_t wm = (wave >> 1) * (BM / 2);
   const uint32_t wn = (wave & 1) * (BN / 2);
-  // A: row wm + fm*32 + l%32, logical chunk 2*kk + l/32.
+  // A: row wm + fm*32 + l%32, logical chunk 2*kk + l/32 (the swizzle of a
+  // row depends on it modulo 16 only, so fm*32 does not change it).
   const uint32_t row = wm + (l & 31);
-  for (int kk = 0; kk < 4; ++kk) f.a[kk] = row * 128 + (((2 * kk) | (l >> 5)) ^ swz_a(row)) * 16;
+  for (int kk = 0; kk < C::KK; ++kk) f.a[kk] = row * (BK * 2) + (((2 * kk) | (l >> 5)) ^ swz_a<BK>(row)) * 16;
   // B: group g = l/16 (h = g/2), source lane s = l%16 points at row
   // kk*16 + h*8 + s/4 (+4 for the second read), columns
   // wn + fn*32 + (g%2)*16 + 4*(s%4) .. +3.
@@ -224,25 +274,53 @@ __device__ inline FragAddr<BM, BN> frag_addr() {
   return f;
 }
 
+// MFMA operands of one sub-step: A fragments, and B fragments as the two
+// 4-element halves that two transposing LDS reads produce.
 template <int BM, int BN>
 struct Frags {
   bf16x8 a[TileCfg<BM, BN>::FM];
-  bf16x8 b[TileCfg<BM, BN>::FN];
+  s16x4 blo[TileCfg<BM, BN>::FN];
+  s16x4 bhi[TileCfg<BM, BN>::FN];
 };
 
 template <int BM, int BN>
-__device__ inline void load_frags(Frags<BM, BN>& f, const uint8_t* stage, const FragAddr<BM, BN>& fa, int kk) {
-  using C = TileCfg<BM, BN>;
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm)
-    f.a[fm] = *OVL_LDS(const bf16x8, stage + fa.a[kk] + fm * 32 * 128);
-#pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn) {
-    const uint8_t* p = stage + fa.b[fn] + kk * 16 * (BN * 2);
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(OVL_LDS(s16x4, p));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(OVL_LDS(s16x4, p + 4 * (BN * 2)));
-    f.b[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+__device__ inline bf16x8 bfrag(const Frags<BM, BN>& f, int fn) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(f.blo[fn], f.bhi[fn], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Read R of the fragments of sub-step kk, in the order the next sub-step
+// needs them: the low and high halves of each B fragment first (the first
+// MFMA group uses them all), then A fragment R - 2*FN.
+template <int BM, int BN, int BK, int R>
+__device__ inline void load_piece(Frags<BM, BN>& f, const uint8_t* stage, const FragAddr<BM, BN, BK>& fa, int kk) {
+  using C = TileCfg<BM, BN, BK>;
+  if constexpr (R >= 2 * C::FN) {
+    constexpr int fm = R - 2 * C::FN;
+    f.a[fm] = *OVL_LDS(const bf16x8, stage + fa.a[kk] + fm * 32 * (BK * 2));
+  } else {
+    constexpr int fn = R / 2;
+    constexpr int hi = R & 1;
+    const uint8_t* p = stage + fa.b[fn] + kk * 16 * (BN * 2) + hi * 4 * (BN * 2);
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(OVL_LDS(s16x4, p));
+    if (hi)
+      f.bhi[fn] = v;
+    else
+      f.blo[fn] = v;
   }
+}
+
+template <int BM, int BN, int BK, int R0, int R1>
+__device__ inline void load_pieces(Frags<BM, BN>& f, const uint8_t* stage, const FragAddr<BM, BN, BK>& fa, int kk) {
+  if constexpr (R0 < R1) {
+    load_piece<BM, BN, BK, R0>(f, stage, fa, kk);
+    load_pieces<BM, BN, BK, R0 + 1, R1>(f, stage, fa, kk);
+  }
+}
+
+template <int BM, int BN, int BK>
+__device__ inline void load_frags(Frags<BM, BN>& f, const uint8_t* stage, const FragAddr<BM, BN, BK>& fa, int kk) {
+  using C = TileCfg<BM, BN, BK>;
+  load_pieces<BM, BN, BK, 0, C::FM + 2 * C::FN>(f, stage, fa, kk);
 }
 
 template <int BM, int BN>
@@ -252,7 +330,7 @@ __device__ inline void mfma_frags(Acc<BM, BN>& acc, const Frags<BM, BN>& f) {
   for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn)
-      acc.v[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[fm], f.b[fn], acc.v[fm][fn], 0, 0, 0);
+      acc.v[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[fm], bfrag(f, fn), acc.v[fm][fn], 0, 0, 0);
 }
 
 // Keeps the compiler from treating x as loop-invariant (the value is
@@ -276,34 +354,88 @@ __device__ inline void interleave_mfma_ds_read() {
   }
 }
 
-// MFMA over one LDS stage (4 sub-steps of K=16), fragments double-buffered
-// so that the LDS reads of sub-step kk+1 are in flight during the MFMAs of
-// kk (one read after each MFMA).  prefetch_a / prefetch_b issue the next
-// stage's global -> LDS loads under the MFMAs of sub-steps 0 and 1.
-template <int BM, int BN, class PA, class PB>
-__device__ inline void stage_compute(Acc<BM, BN>& acc, const uint8_t* stage, const FragAddr<BM, BN>& fa,
-                                     PA prefetch_a, PB prefetch_b) {
-  using C = TileCfg<BM, BN>;
-  constexpr int kReads = C::FM + 2 * C::FN;  // LDS reads per sub-step
+// Issues loads [Q0, Q1) of the prefetch, in order.
+template <int Q0, int Q1, class P>
+__device__ inline void issue_range(const P& p) {
+  if constexpr (Q0 < Q1) {
+    p.template issue<Q0>();
+    issue_range<Q0 + 1, Q1>(p);
+  }
+}
+
+// One MFMA group (the FN blocks of A-fragment row fm = G % FM) of sub-step
+// KKI, on fragments `cur`, with this group's share of the next sub-step's
+// fragment reads into `nxt` interleaved (one read after each MFMA), followed
+// by a burst of a later stage's global loads where it is due.
+template <int BM, int BN, int BK, int KKI, int G, class P>
+__device__ inline void mfma_group(Acc<BM, BN>& acc, const Frags<BM, BN>& cur, Frags<BM, BN>& nxt,
+                                  const uint8_t* stage, const FragAddr<BM, BN, BK>& fa, const P& pf) {
+  using C = TileCfg<BM, BN, BK>;
+  constexpr int fm = G % C::FM;
+  constexpr int reads = C::FM + 2 * C::FN;  // fragment reads per sub-step
+  constexpr int per = (reads + C::FM - 1) / C::FM;
+  constexpr int r0 = fm * per < reads ? fm * per : reads;
+  constexpr int r1 = (fm + 1) * per < reads ? (fm + 1) * per : reads;
+  constexpr int rd = KKI + 1 < C::KK ? r1 - r0 : 0;
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn)
+    acc.v[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[fm], bfrag(cur, fn), acc.v[fm][fn], 0, 0, 0);
+  if constexpr (KKI + 1 < C::KK) load_pieces<BM, BN, BK, r0, r1>(nxt, stage, fa, KKI + 1);
+#pragma unroll
+  for (int i = 0; i < C::FN; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if (i < rd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+  OVL_SCHED_FENCE();
+  // The next stage's loads go in two bursts, A after the first group of
+  // sub-step KK/4 and B after the first group of sub-step KK/2 (measured:
+  // bursts in mid-step beat bursts at the step start and one load per group).
+  if constexpr (G == (C::KK / 4) * C::FM + (C::KK == 2 ? C::FM / 2 : 0)) issue_range<0, C::QA>(pf);
+  if constexpr (G == (C::KK / 2) * C::FM) issue_range<C::QA, C::LPS>(pf);
+  OVL_SCHED_FENCE();
+}
+
+template <int BM, int BN, int BK, int KKI, int G0, int N, class P>
+__device__ inline void mfma_groups(Acc<BM, BN>& acc, const Frags<BM, BN>& cur, Frags<BM, BN>& nxt,
+                                   const uint8_t* stage, const FragAddr<BM, BN, BK>& fa, const P& pf) {
+  if constexpr (N > 0) {
+    mfma_group<BM, BN, BK, KKI, G0>(acc, cur, nxt, stage, fa, pf);
+    mfma_groups<BM, BN, BK, KKI, G0 + 1, N - 1>(acc, cur, nxt, stage, fa, pf);
+  }
+}
+
+// MFMA over one LDS stage (BK/16 sub-steps of K = 16), fragments
+// double-buffered so that the LDS reads of sub-step kk+1 are in flight
+// during the MFMAs of kk (one read after each MFMA), with the global -> LDS
+// loads of a later stage in two bursts in mid-step.
+template <int BM, int BN, int BK, class P>
+__device__ inline void stage_compute(Acc<BM, BN>& acc, const uint8_t* stage, const FragAddr<BM, BN, BK>& fa,
+                                     const P& pf) {
+  using C = TileCfg<BM, BN, BK>;
   Frags<BM, BN> f0, f1;
   load_frags(f0, stage, fa, 0);
   OVL_SCHED_FENCE();
-  prefetch_a();
-  load_frags(f1, stage, fa, 1);
-  mfma_frags(acc, f0);
-  interleave_mfma_ds_read<kReads>();
-  OVL_SCHED_FENCE();
-  prefetch_b();
-  load_frags(f0, stage, fa, 2);
-  mfma_frags(acc, f1);
-  interleave_mfma_ds_read<kReads>();
-  OVL_SCHED_FENCE();
-  load_frags(f1, stage, fa, 3);
-  mfma_frags(acc, f0);
-  interleave_mfma_ds_read<kReads>();
-  OVL_SCHED_FENCE();
-  mfma_frags(acc, f1);
-  OVL_SCHED_FENCE();
+  mfma_groups<BM, BN, BK, 0, 0, C::FM>(acc, f0, f1, stage, fa, pf);
+  if constexpr (C::KK == 4) {
+    mfma_groups<BM, BN, BK, 1, C::FM, C::FM>(acc, f1, f0, stage, fa, pf);
+    mfma_groups<BM, BN, BK, 2, 2 * C::FM, C::FM>(acc, f0, f1, stage, fa, pf);
+    mfma_groups<BM, BN, BK, 3, 3 * C::FM, C::FM>(acc, f1, f0, stage, fa, pf);
+  } else {
+    mfma_groups<BM, BN, BK, 1, C::FM, C::FM>(acc, f1, f0, stage, fa, pf);
+  }
+}
+
+// Waits until at most n of this wave's asm-issued stage loads are in flight
+// (n a multiple of the loads per stage, at most 2 stages' worth).
+template <int LPS>
+__device__ inline void wait_stage_loads(int pending_stages) {
+  if (pending_stages >= 2) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPS) : "memory");
+  } else if (pending_stages == 1) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
 }
 
 template <int BM, int BN>
@@ -319,40 +451,38 @@ __device__ inline void acc_zero(Acc<BM, BN>& acc) {
 
 // The K loop of one tile.  before_step(k0) is where a consumer waits for
 // the data of the K-step at k0: every wave calls it, before a workgroup
-// barrier that precedes the first load of that step, one step ahead of the
-// loads (so a wave that acquires there orders the whole workgroup's loads).
-// Ends with a workgroup barrier, so LDS may be reused at once.
-template <int BM, int BN, class BeforeStep>
+// barrier that precedes the first load of that step (so a wave that acquires
+// there orders the whole workgroup's loads).  Ends with a workgroup
+// barrier, so LDS may be reused at once.
+template <int BM, int BN, int BK = 64, class BeforeStep>
 __device__ inline void gemm_tile(Acc<BM, BN>& acc, const Operands& op, int64_t m0, uint16_t* lds,
                                  BeforeStep before_step) {
-  using C = TileCfg<BM, BN>;
+  using C = TileCfg<BM, BN, BK>;
+  constexpr int NS = C::NS;
+  static_assert(NS - 2 <= 2, "wait_stage_loads covers up to two pending stages");
   uint8_t* l8 = reinterpret_cast<uint8_t*>(lds);
   acc_zero(acc);
-  const TileAddr<BM, BN> ta = tile_addr<BM, BN>(op, m0);
-  const FragAddr<BM, BN> fa = frag_addr<BM, BN>();
-  const int32_t steps = (int32_t)((op.k + kBK - 1) / kBK);
+  const TileAddr<BM, BN, BK> ta = tile_addr<BM, BN, BK>(op, m0);
+  const FragAddr<BM, BN, BK> fa = frag_addr<BM, BN, BK>();
+  const int32_t steps = (int32_t)((op.k + BK - 1) / BK);
   const uint32_t lbase = lds_addr(l8);
-  before_step(0);
+  // Prologue: the first NS-1 stages.
+  for (int32_t i = 0; i < NS - 1 && i < steps; ++i) before_step((int64_t)i * BK);
   __syncthreads();
-  stage_issue_a(ta, lbase, 0);
-  stage_issue_b(ta, lbase, 0);
-  if (steps > 1) before_step(kBK);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads have landed in LDS
+  for (int32_t i = 0; i < NS - 1 && i < steps; ++i) {
+    stage_issue_a(ta, lbase + i * C::STAGE_BYTES, i * BK);
+    stage_issue_b(ta, lbase + i * C::STAGE_BYTES, i * BK);
+  }
+  if (NS - 1 < steps) before_step((int64_t)(NS - 1) * BK);
+  wait_stage_loads<C::LPS>(min(NS - 2, steps - 1));  // stage 0 has landed
   __syncthreads();
   for (int32_t s = 0; s < steps; ++s) {
-    const bool more = s + 1 < steps;
-    const int32_t k1 = (s + 1) * kBK;
-    const uint32_t next = lbase + ((s + 1) & 1) * C::STAGE_BYTES;
-    stage_compute(
-        acc, l8 + (s & 1) * C::STAGE_BYTES, fa,
-        [&] {
-          if (more) stage_issue_a(ta, next, k1);
-        },
-        [&] {
-          if (more) stage_issue_b(ta, next, k1);
-        });
-    if (s + 2 < steps) before_step((int64_t)(s + 2) * kBK);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int32_t nxt = s + NS - 1;  // stage issued during this step
+    const Prefetch<BM, BN, BK> pf{&ta, lbase + (uint32_t)(nxt % NS) * C::STAGE_BYTES, nxt * BK, nxt < steps};
+    stage_compute<BM, BN, BK>(acc, l8 + (s % NS) * C::STAGE_BYTES, fa, pf);
+    if (s + NS < steps) before_step((int64_t)(s + NS) * BK);
+    // Stage s+1 must have landed; the stages issued after it may stay in flight.
+    wait_stage_loads<C::LPS>(max(0, min(s + NS - 1, steps - 1) - (s + 1)));
     __syncthreads();
   }
 }
