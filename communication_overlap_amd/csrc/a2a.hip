@@ -244,7 +244,7 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
     op.k = a.hidden;
     const int64_t m0 = seg0 + (int64_t)mt * kGbm;
     Acc<kGbm, kGbn> acc;
-    gemm_tile<kGbm, kGbn>(acc, op, m0, lds, [](int64_t) {});
+    gemm_tile<kGbm, kGbn>(acc, op, m0, lds, [](int64_t, int64_t) {});
     acc_store<kGbm, kGbn>(acc, a.y + (int64_t)s * a.cap * a.n, a.n, m0, op.n0, seg_end, a.n);
   }
 }

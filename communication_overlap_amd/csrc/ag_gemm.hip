@@ -320,24 +320,31 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
     }
 
     int last_batch = -1;
-    auto before_step = [&](int64_t k0) {
+    // Waits for every K-batch the step's columns [k0, k1) reach that no
+    // earlier step has waited for (steps advance in K order; a step may
+    // straddle a batch boundary when the batch width is not a multiple of
+    // the K-step).
+    auto before_step = [&](int64_t k0, int64_t k1) {
       if (MODE != kModeFused || own || timed_out) return;
       if (threadIdx.x >= 64) return;  // wave 0 waits for the workgroup (see gemm_tile)
-      const int bt = (int)(k0 / a.batch_cols);
-      if (bt == last_batch) return;
-      last_batch = bt;
+      const int bt_hi = (int)((k1 - 1) / a.batch_cols);
+      if (bt_hi <= last_batch) return;
       const int s_lo = (int)(m0 / a.shard_m), s_hi = (int)((m_end - 1) / a.shard_m);
-      for (int s = s_lo; s <= s_hi && !timed_out; ++s) {
-        const int64_t lo = max(m0, (int64_t)s * a.shard_m) - (int64_t)s * a.shard_m;
-        const int64_t hi = min(m_end, (int64_t)(s + 1) * a.shard_m) - (int64_t)s * a.shard_m;
-        for (int p = (int)(lo / a.unit_rows); p <= (int)((hi - 1) / a.unit_rows); ++p) {
-          const int64_t u = ((int64_t)s * a.panels + p) * a.batches + bt;
-          if (!wave_wait(a.flags + u * a.flag_stride, a.epoch, a.spin_limit, a.err, kSiteAgUnit, u)) {
-            timed_out = true;
-            break;
+      for (int bt = last_batch + 1; bt <= bt_hi && !timed_out; ++bt) {
+        for (int s = s_lo; s <= s_hi && !timed_out; ++s) {
+          const int64_t lo = max(m0, (int64_t)s * a.shard_m) - (int64_t)s * a.shard_m;
+          const int64_t hi = min(m_end, (int64_t)(s + 1) * a.shard_m) - (int64_t)s * a.shard_m;
+          for (int p = (int)(lo / a.unit_rows); p <= (int)((hi - 1) / a.unit_rows); ++p) {
+            const int64_t u = ((int64_t)s * a.panels + p) * a.batches + bt;
+            if (!wave_poll(a.flags + u * a.flag_stride, a.epoch, a.spin_limit, a.err, kSiteAgUnit, u)) {
+              timed_out = true;
+              break;
+            }
           }
         }
       }
+      last_batch = bt_hi;
+      wave_acquire();  // one acquire for all the units polled
     };
 
     Acc<BM, BN> acc;

@@ -26,7 +26,7 @@ struct ErrRec {
 };
 static_assert(sizeof(ErrRec) == 64, "error record size");
 
-enum : int32_t { kSiteAgUnit = 1, kSiteAgBarrier = 2, kSiteRsIn = 3, kSiteA2aSlice = 4, kSiteRsJob = 5 };
+enum : int32_t { kSiteAgUnit = 1, kSiteAgBarrier = 2, kSiteRsIn = 3, kSiteA2aSlice = 4, kSiteRsOwn = 5 };
 
 __device__ inline void report_error(ErrRec* e, int32_t code, int32_t site, int64_t index,
                                     int64_t observed, int64_t expected) {
@@ -40,28 +40,35 @@ __device__ inline void report_error(ErrRec* e, int32_t code, int32_t site, int64
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
 
-// Wave-level acquire wait: every lane of the calling wavefront polls `flag`
-// (one load per poll, uniform address) with relaxed agent-scope loads until
-// it holds a value >= epoch, then issues one agent-scope acquire fence, so
-// that every load the wave issues afterwards sees the producer's data.
-// Returns false (after recording OVL_ETIMEOUT) if spin_limit polls pass.
-__device__ inline bool wave_wait(const int64_t* flag, int64_t epoch, uint64_t spin_limit,
+// Wave-level poll: every lane of the calling wavefront polls `flag` (one
+// load per poll, uniform address) with relaxed agent-scope loads until it
+// holds a value >= epoch.  Returns false (after recording OVL_ETIMEOUT) if
+// spin_limit polls pass.  The caller follows one or more polls with
+// wave_acquire() before it reads what the flags guard.
+__device__ inline bool wave_poll(const int64_t* flag, int64_t epoch, uint64_t spin_limit,
                                  ErrRec* err, int32_t site, int64_t index) {
   int64_t v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint64_t polls = 0;
-  bool ok = true;
   while (__builtin_amdgcn_readfirstlane((int)(v < epoch))) {
     if (++polls > spin_limit) {
-      ok = false;
-      break;
+      if (lane_id() == 0) report_error(err, -6 /* OVL_ETIMEOUT */, site, index, v, epoch);
+      return false;
     }
     __builtin_amdgcn_s_sleep(2);
     v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (!ok) {
-    if (lane_id() == 0) report_error(err, -6 /* OVL_ETIMEOUT */, site, index, v, epoch);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
+}
+
+// Agent-scope acquire fence: every load the wave issues afterwards sees what
+// the producers released before the flag values its polls observed.
+__device__ inline void wave_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// Wave-level acquire wait on one flag: wave_poll, then wave_acquire.
+__device__ inline bool wave_wait(const int64_t* flag, int64_t epoch, uint64_t spin_limit,
+                                 ErrRec* err, int32_t site, int64_t index) {
+  const bool ok = wave_poll(flag, epoch, spin_limit, err, site, index);
+  wave_acquire();
   return ok;
 }
 

@@ -49,8 +49,9 @@ __device__ inline rsrc_t make_rsrc(const void* base, int64_t bytes) {
 __device__ inline float bloadf(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
+template <int AUX = 0>
 __device__ inline void bstoref(rsrc_t r, uint32_t off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, AUX);
 }
 
 // Buffer descriptor as four scalar words, for the inline-asm loads below
@@ -449,11 +450,11 @@ __device__ inline void acc_zero(Acc<BM, BN>& acc) {
       for (int r = 0; r < 16; ++r) acc.v[fm][fn][r] = 0.f;
 }
 
-// The K loop of one tile.  before_step(k0) is where a consumer waits for
-// the data of the K-step at k0: every wave calls it, before a workgroup
-// barrier that precedes the first load of that step (so a wave that acquires
-// there orders the whole workgroup's loads).  Ends with a workgroup
-// barrier, so LDS may be reused at once.
+// The K loop of one tile.  before_step(k0, k1) is where a consumer waits
+// for the data of the K-step that reads columns [k0, k1) of A: every wave
+// calls it, before a workgroup barrier that precedes the first load of that
+// step (so a wave that acquires there orders the whole workgroup's loads).
+// Ends with a workgroup barrier, so LDS may be reused at once.
 template <int BM, int BN, int BK = 64, class BeforeStep>
 __device__ inline void gemm_tile(Acc<BM, BN>& acc, const Operands& op, int64_t m0, uint16_t* lds,
                                  BeforeStep before_step) {
@@ -467,20 +468,21 @@ __device__ inline void gemm_tile(Acc<BM, BN>& acc, const Operands& op, int64_t m
   const int32_t steps = (int32_t)((op.k + BK - 1) / BK);
   const uint32_t lbase = lds_addr(l8);
   // Prologue: the first NS-1 stages.
-  for (int32_t i = 0; i < NS - 1 && i < steps; ++i) before_step((int64_t)i * BK);
+  auto step_cols = [&](int32_t i) { before_step((int64_t)i * BK, min((int64_t)(i + 1) * BK, op.k)); };
+  for (int32_t i = 0; i < NS - 1 && i < steps; ++i) step_cols(i);
   __syncthreads();
   for (int32_t i = 0; i < NS - 1 && i < steps; ++i) {
     stage_issue_a(ta, lbase + i * C::STAGE_BYTES, i * BK);
     stage_issue_b(ta, lbase + i * C::STAGE_BYTES, i * BK);
   }
-  if (NS - 1 < steps) before_step((int64_t)(NS - 1) * BK);
+  if (NS - 1 < steps) step_cols(NS - 1);
   wait_stage_loads<C::LPS>(min(NS - 2, steps - 1));  // stage 0 has landed
   __syncthreads();
   for (int32_t s = 0; s < steps; ++s) {
     const int32_t nxt = s + NS - 1;  // stage issued during this step
     const Prefetch<BM, BN, BK> pf{&ta, lbase + (uint32_t)(nxt % NS) * C::STAGE_BYTES, nxt * BK, nxt < steps};
     stage_compute<BM, BN, BK>(acc, l8 + (s % NS) * C::STAGE_BYTES, fa, pf);
-    if (s + NS < steps) before_step((int64_t)(s + NS) * BK);
+    if (s + NS < steps) step_cols(s + NS);
     // Stage s+1 must have landed; the stages issued after it may stay in flight.
     wait_stage_loads<C::LPS>(max(0, min(s + NS - 1, steps - 1) - (s + 1)));
     __syncthreads();
@@ -536,11 +538,14 @@ __device__ inline uint32_t out_off(const OutTile& o, int row, int col) {
 }
 
 // Stores the tile to fp32 C (row pitch ldc) at (m0, n0), clipped to m_valid x n_valid.
-template <int BM, int BN>
+// AUX is the buffer store's cache-policy operand (0: default).  Each store
+// instruction writes 128 contiguous bytes of two rows (measured faster than
+// computing the blocks transposed for 16-byte stores: 32-byte row pieces).
+template <int BM, int BN, int AUX = 0>
 __device__ inline void acc_store(const Acc<BM, BN>& acc, float* c, int64_t ldc, int64_t m0, int64_t n0,
                                  int64_t m_valid, int64_t n_valid) {
   const OutTile o = out_tile(c, ldc, m0, n0, m_valid, n_valid);
-  acc_foreach(acc, [&](int row, int col, float v) { bstoref(o.r, out_off(o, row, col), v); });
+  acc_foreach(acc, [&](int row, int col, float v) { bstoref<AUX>(o.r, out_off(o, row, col), v); });
 }
 
 }  // namespace ovl

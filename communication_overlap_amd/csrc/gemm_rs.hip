@@ -2,21 +2,20 @@
 // Semantics", Kernel Design Patterns, "GEMM and ReduceScatter Overlapping").
 //
 // One persistent launch of GEMM workgroups.  The local product's rows split
-// into R blocks; tiles of the blocks destined for peers come first, starting
-// at block rank+1 (the mirror of the all-gather's swizzle), and the own
-// block comes last.
+// into R blocks.  The own block's tiles come first, then the blocks destined
+// for peers, starting at block rank+1 (the mirror of the all-gather's
+// swizzle).
+//   - Own tile: the fp32 accumulator is stored to `out` and an own-tile flag
+//     in the workspace is published.
 //   - Peer tile: the fp32 tile is stored to that peer's partial buffer and
 //     its out flag is published (put + signal).  Then the workgroup runs one
 //     reduce job: the own block's tile rows are split evenly over all peer
-//     tiles, and job j sums, for its share of rows, the peers' partials
-//     (after their in flags) in ascending peer order, S = P_a + P_b + ...,
-//     into `out`, and publishes a job flag in the workspace.  This spreads
-//     the reading of the R-1 partials over the whole launch instead of
-//     leaving it to the few workgroups that finish the own block.
-//   - Own tile: wave 0 waits for the jobs that cover the tile, then every
-//     lane writes out = acc + S.  The job flags live in the workspace and are
-//     used in every mode, so the workspace too needs a new epoch per run.
-// Every output element is therefore acc + (((P_a + P_b) + ...)) in fp32, in
+//     tiles, and job j, for its share of rows, waits for the own tiles and
+//     the peers' partials it covers (own-tile flags, in flags), sums the
+//     partials in ascending peer order, S = P_a + P_b + ..., and writes
+//     out = acc + S over the stored accumulator.  This spreads the reading of
+//     the R-1 partials over the whole launch, and nothing waits at its end.
+// Every output element is therefore acc + ((P_a + P_b) + ...) in fp32, in
 // this fixed order, whatever the timing.
 #include <algorithm>
 
@@ -40,7 +39,7 @@ struct RsArgs {
   float* out;
   int64_t* out_flags;
   const int64_t* in_flags;
-  int64_t* job_flags;  // [jobs] in the workspace
+  int64_t* own_flags;  // [tiles per block] in the workspace
   ErrRec* err;
   int64_t m, n, k, bm;  // bm = rows per block
   int64_t flag_stride;  // int64 slots
@@ -56,46 +55,78 @@ struct RsArgs {
 // trow*256 + r of the block, columns of tile column tcol).  Job j of J covers
 // [j*OR/J, (j+1)*OR/J), OR = tiles_per_block * 256.
 __device__ inline int64_t job_begin(int64_t j, int64_t J, int64_t OR) { return j * OR / J; }
-__device__ inline int64_t job_of_row(int64_t q, int64_t J, int64_t OR) { return ((q + 1) * J - 1) / OR; }
 
 __device__ void reduce_job(const RsArgs& a, int64_t j, int64_t J, bool& timed_out) {
   const int tpb = a.tr * a.tc;
   const int64_t OR = (int64_t)tpb * kRsTile;
   const int64_t q0 = job_begin(j, J, OR), q1 = job_begin(j + 1, J, OR);
-  // Wait for every peer's partial of the own tiles this job touches.
-  if (a.sync && threadIdx.x < 64 && !timed_out) {
-    for (int64_t t = q0 / kRsTile; t <= (q1 - 1) / kRsTile && !timed_out; ++t)
+  if (q0 >= q1) return;
+  // Wave 0 waits for the own tiles this job touches and, with flags on, for
+  // every peer's partial of them; the barrier hands the acquire to the
+  // other waves.
+  // All flags are polled first, then one acquire covers them.
+  if (threadIdx.x < 64 && !timed_out) {
+    for (int64_t t = q0 / kRsTile; t <= (q1 - 1) / kRsTile && !timed_out; ++t) {
+      if (!wave_poll(a.own_flags + t, a.epoch, a.spin_limit, a.err, kSiteRsOwn, t)) {
+        timed_out = true;
+        break;
+      }
+      if (!a.sync) continue;
       for (int p = 0; p < a.ranks && !timed_out; ++p) {
         if (p == a.rank) continue;
         const int64_t idx = (int64_t)p * tpb + t;
-        if (!wave_wait(a.in_flags + idx * a.flag_stride, a.epoch, a.spin_limit, a.err, kSiteRsIn, idx))
+        if (!wave_poll(a.in_flags + idx * a.flag_stride, a.epoch, a.spin_limit, a.err, kSiteRsIn, idx))
           timed_out = true;
       }
+    }
+    wave_acquire();
   }
   __syncthreads();
-  // 64 lanes of 16 bytes cover one 256-column row; 4 rows per pass.
+  // 64 lanes of 16 bytes cover one 256-column row; each wave takes two rows
+  // per pass and issues all of their loads (accumulator and R-1 partials)
+  // before the first add.
+  constexpr int U = 2;
   const int lane = threadIdx.x & 63, rsub = threadIdx.x >> 6;
-  for (int64_t q = q0 + rsub; q < q1; q += 4) {
-    const int64_t t = q / kRsTile;
-    const int64_t row = (t / a.tc) * kRsTile + (q % kRsTile);
-    const int64_t col = (t % a.tc) * kRsTile + lane * 4;
-    if (row >= a.bm || col >= a.n) continue;
-    const int64_t off = row * a.n + col;
-    f32x4 acc4;
-    bool first = true;
-    for (int p = 0; p < a.ranks; ++p) {
-      if (p == a.rank) continue;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.peer_in[p] + off);
-      if (first) {
-        acc4 = v;
-        first = false;
-      } else {
-        acc4 += v;
-      }
+  for (int64_t q = q0 + rsub; q < q1; q += 4 * U) {
+    int64_t off[U];
+    bool ok[U];
+    f32x4 acc[U], v[U][kRsMaxRanks];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t qq = q + 4 * u;
+      const int64_t t = qq / kRsTile;
+      const int64_t row = (t / a.tc) * kRsTile + (qq % kRsTile);
+      const int64_t col = (t % a.tc) * kRsTile + lane * 4;
+      ok[u] = qq < q1 && row < a.bm && col < a.n;
+      off[u] = ok[u] ? row * a.n + col : 0;
     }
-    *reinterpret_cast<f32x4*>(a.out + off) = acc4;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!ok[u]) continue;
+      acc[u] = *reinterpret_cast<const f32x4*>(a.out + off[u]);
+#pragma unroll
+      for (int p = 0; p < kRsMaxRanks; ++p)
+        if (p < a.ranks && p != a.rank)
+          v[u][p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.peer_in[p] + off[u]));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!ok[u]) continue;
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+      bool first = true;
+#pragma unroll
+      for (int p = 0; p < kRsMaxRanks; ++p) {
+        if (p >= a.ranks || p == a.rank) continue;
+        if (first) {
+          sum = v[u][p];
+          first = false;
+        } else {
+          sum += v[u][p];
+        }
+      }
+      *reinterpret_cast<f32x4*>(a.out + off[u]) = acc[u] + sum;
+    }
   }
-  wg_publish(a.job_flags + j, a.epoch);
 }
 
 template <int SYNC>
@@ -105,7 +136,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs a) {
   const int tpb = a.tr * a.tc;
   const int64_t total = (int64_t)a.ranks * tpb;
   const int64_t J = (int64_t)(a.ranks - 1) * tpb;  // reduce jobs = peer tiles
-  const int64_t OR = (int64_t)tpb * kRsTile;
   const int Cn = a.workers;
   const int groups = (Cn % kRsXcds == 0) ? kRsXcds : 1;
   const int per = Cn / groups;
@@ -116,8 +146,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs a) {
   for (int64_t w = 0;; ++w) {
     const int64_t j = w * Cn + (int64_t)x * per + q;
     if (j >= total) break;
-    const int blk = (int)((a.rank + 1 + j / tpb) % a.ranks);
-    const int t = (int)(j % tpb);
+    // Own tiles first, then peer tile pj of block rank+1+pj/tpb.
+    const int64_t pj = j - tpb;
+    const int blk = pj < 0 ? a.rank : (int)((a.rank + 1 + pj / tpb) % a.ranks);
+    const int t = (int)(pj < 0 ? j : pj % tpb);
     const int trow = t / a.tc, tcol = t % a.tc;
 
     Operands op;
@@ -132,29 +164,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs a) {
     const int64_t m0 = (int64_t)trow * BM;
 
     Acc<BM, BN> acc;
-    gemm_tile<BM, BN>(acc, op, m0, lds, [](int64_t) {});
+    gemm_tile<BM, BN>(acc, op, m0, lds, [](int64_t, int64_t) {});
 
     if (blk != a.rank) {
       acc_store<BM, BN>(acc, a.peer_out[blk], a.n, m0, op.n0, a.bm, a.n);
       if (SYNC) wg_publish(a.out_flags + ((int64_t)blk * tpb + t) * a.flag_stride, a.epoch);
-      reduce_job(a, j, J, timed_out);  // j < J: peer tiles come first
+      reduce_job(a, pj, J, timed_out);
     } else {
-      if (J > 0) {
-        if (threadIdx.x < 64 && !timed_out) {
-          const int64_t j0 = job_of_row((int64_t)t * kRsTile, J, OR);
-          const int64_t j1 = job_of_row((int64_t)t * kRsTile + kRsTile - 1, J, OR);
-          for (int64_t jj = j0; jj <= j1 && !timed_out; ++jj)
-            if (!wave_wait(a.job_flags + jj, a.epoch, a.spin_limit, a.err, kSiteRsJob, jj)) timed_out = true;
-        }
-        __syncthreads();
-        const OutTile o = out_tile(a.out, a.n, m0, op.n0, a.bm, a.n);
-        acc_foreach(acc, [&](int row, int col, float v) {
-          const uint32_t off = out_off(o, row, col);
-          bstoref(o.r, off, v + bloadf(o.r, off));
-        });
-      } else {
-        acc_store<BM, BN>(acc, a.out, a.n, m0, op.n0, a.bm, a.n);
-      }
+      acc_store<BM, BN>(acc, a.out, a.n, m0, op.n0, a.bm, a.n);
+      if (J > 0) wg_publish(a.own_flags + t, a.epoch);
     }
   }
 }
@@ -174,12 +192,12 @@ extern "C" size_t gemm_rs_flags_bytes(const gemm_rs_desc* d) {
   return (size_t)(d->ranks * tpb * d->flag_stride);
 }
 
-// Error record, then one int64 flag per reduce job (one per peer tile).
+// Error record, then one int64 flag per own tile.
 extern "C" size_t gemm_rs_workspace_bytes(const gemm_rs_desc* d) {
   if (!d || d->ranks < 1 || d->m < 1 || d->n < 1 || d->m % d->ranks) return 0;
   const int64_t bm = d->m / d->ranks;
   const int64_t tpb = ceil_div(bm, kRsTile) * ceil_div(d->n, kRsTile);
-  return OVL_ERROR_RECORD_BYTES + 8 * (size_t)((d->ranks - 1) * tpb);
+  return OVL_ERROR_RECORD_BYTES + 8 * (size_t)tpb;
 }
 
 extern "C" ovl_status gemm_rs_run(const gemm_rs_desc* d, const void* a, const void* b, float* const* peer_out,
@@ -225,7 +243,7 @@ extern "C" ovl_status gemm_rs_run(const gemm_rs_desc* d, const void* a, const vo
   r.out_flags = out_flags;
   r.in_flags = in_flags;
   r.err = static_cast<ErrRec*>(workspace);
-  r.job_flags = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(workspace) + OVL_ERROR_RECORD_BYTES);
+  r.own_flags = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(workspace) + OVL_ERROR_RECORD_BYTES);
   r.m = d->m;
   r.n = d->n;
   r.k = d->k;

@@ -183,8 +183,8 @@ ovl_status ag_gemm_run(ag_gemm_plan_t plan, const void* const* shards, const voi
  * peer_out[p] and signalled in out_flags (put + signal).  For its own block
  * the rank waits for every peer's partial tile (in_flags) and writes
  *   out = L[rank block] + (sum over p != rank, ascending, of peer_in[p])
- * in fp32.  Tiles of peer blocks are computed first, starting at block
- * rank+1; the own block comes last.
+ * in fp32.  The own block's tiles are computed first, then the peer
+ * blocks, starting at block rank+1.
  *
  * Flag layout (both buffers): R rows of tiles_per_block slots, tile t of
  * block p at byte (p * tiles_per_block + t) * flag_stride, with
@@ -211,12 +211,13 @@ size_t gemm_rs_workspace_bytes(const gemm_rs_desc* desc);
  * out:      fp32 [m/R][n].
  * out_flags: written (epoch) per sent tile.  in_flags: read only.
  * workspace: gemm_rs_workspace_bytes(desc) bytes: besides the error record
- *           it holds one flag per peer tile, so successive runs on one
+ *           it holds one flag per own tile, so successive runs on one
  *           workspace need increasing epochs too (ovl_flags_reset restarts).
- * The reduction of the peers' partials is spread over the workgroups that
- * computed peer tiles: each sums, in ascending peer order, the partials of a
- * contiguous share of the own block's rows into `out`, and the own block's
- * tiles then add their accumulators, so out = acc + ((P_a + P_b) + ...).
+ * The own block's tiles store their accumulators to `out` first; the
+ * reduction of the peers' partials is spread over the workgroups that
+ * computed peer tiles: each takes a contiguous share of the own block's
+ * rows, sums the partials in ascending peer order and adds the stored
+ * accumulator, so out = acc + ((P_a + P_b) + ...).
  * Modes: FUSED, or GEMM_ONLY (same work and result, without in/out flag
  * traffic).
  * Errors as for ag_gemm_run; EUNSUPPORTED if tile_m/tile_n are not 256, if
@@ -288,7 +289,7 @@ ovl_status ovl_flags_reset(int64_t* flags, size_t flag_bytes, void* workspace, s
  * `workspace` (OVL_OK or OVL_ETIMEOUT; the first wait to give up wins).
  * detail (HOST, may be NULL) receives {site, flag index, observed value,
  * awaited value}; sites: 1 AG-GEMM unit flag, 2 AG-GEMM barrier mode,
- * 3 GEMM-RS in flag, 4 dispatch slice flag, 5 GEMM-RS reduce-job flag. */
+ * 3 GEMM-RS in flag, 4 dispatch slice flag, 5 GEMM-RS own-tile flag. */
 ovl_status ovl_check(const void* workspace, int64_t* detail, hipStream_t stream);
 
 const char* ovl_strerror(ovl_status status);

@@ -170,7 +170,7 @@ def test_flag_and_workspace_sizes():
     o = ovl()
     d = o.gemm_rs_desc(8, 0, 8192, 4096, 1792)
     assert o.gemm_rs_flags_bytes(d) == 8 * 64 * 8
-    assert o.gemm_rs_workspace_bytes(d) == o.ERROR_RECORD_BYTES + 8 * 7 * 64
+    assert o.gemm_rs_workspace_bytes(d) == o.ERROR_RECORD_BYTES + 8 * 64
     ad = o.a2a_desc(8, 0, 4096, 4096, 1408, 2, 64, 8, 128)
     assert o.a2a_flags_bytes(ad) == 8 * 128
     assert o.a2a_workspace_bytes(ad) >= o.ERROR_RECORD_BYTES + 8 * 8

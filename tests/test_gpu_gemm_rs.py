@@ -96,10 +96,9 @@ def test_withheld_partial_times_out():
     v[3, 2] = 0  # peer 3 never sent tile 2 of this rank's block
     st, det = case.run(1, spin_limit=2000)
     assert st == o.OVL_ETIMEOUT
-    # Either the reduce job that needs the withheld partial gave up first
-    # (site 3: in flag 3*tpb + 2), or the own tile waiting on that job did
-    # (site 5: a job flag).
-    assert (det[0] == 3 and det[1] == 3 * case.tpb + 2) or det[0] == 5, det
+    # The reduce job that needs the withheld partial gives up (site 3: in
+    # flag 3*tpb + 2, observed 0, awaited 1).
+    assert det == (3, 3 * case.tpb + 2, 0, 1), det
 
 
 def test_full_size_sampled():
