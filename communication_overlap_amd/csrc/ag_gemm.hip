@@ -43,7 +43,15 @@ struct AgArgs {
   int32_t num_units;
   int32_t producers, consumers;
   int32_t tiles_m, tiles_n;
+  // Split K: each output tile is computed as `splits` column ranges of A
+  // (split_cols wide); each range's fp32 product goes to partial[s] and the
+  // last range to arrive (counters[tile]) sums them in range order into C.
+  int32_t splits, split_cols;
+  float* partial;     // [splits][m][n]
+  int64_t* counters;  // [tiles], zero between launches
 };
+
+constexpr int kMaxSplits = 8;
 
 enum { kModeFused = 0, kModeBarrier = 1, kModeGemmOnly = 2 };
 
@@ -201,7 +209,8 @@ __device__ Sched build_schedule(const AgArgs& a, int BM, int* sorted, int* tab, 
     sorted[rank] = rt;
     pos[rt] = rank;
   }
-  const int64_t round1 = min((int64_t)a.consumers, (int64_t)a.tiles_m * a.tiles_n);
+  const int64_t round1 =
+      min((int64_t)a.tiles_m * a.tiles_n, ((int64_t)a.consumers + a.splits - 1) / a.splits);  // tiles
   const int rows1 = (int)((round1 + a.tiles_n - 1) / a.tiles_n);
   const int SP = a.ranks * a.panels;
   const bool boot_on = with_boot && SP <= kMaxRowTiles;
@@ -260,7 +269,44 @@ __device__ Sched build_schedule(const AgArgs& a, int BM, int* sorted, int* tab, 
 
 // ---------------------------------------------------------------- consumer
 
-template <int BM, int BN, int MODE>
+// Last range of a split tile: C[rows, cols] = ((P_0 + P_1) + ...) over the
+// partial products in range order, 16 bytes per lane, four row groups of
+// every partial loaded before the first add.
+template <int BM, int BN>
+__device__ void reduce_splits(const AgArgs& a, int64_t m0, int64_t n0) {
+  constexpr int VPR = BN / 4;           // 16-byte vectors per tile row
+  constexpr int RPP = kThreads / VPR;   // rows per pass
+  constexpr int U = 4;
+  const int64_t rows = min((int64_t)BM, a.m - m0);
+  const int64_t cols = min((int64_t)BN, a.n - n0);
+  const int vc = threadIdx.x % VPR, r0 = threadIdx.x / VPR;
+  if (vc * 4 >= cols) return;  // n is a multiple of 8: a vector is all in or all out
+  const int64_t slice = a.m * a.n;
+  for (int64_t r = r0; r < rows; r += RPP * U) {
+    f32x4 v[U][kMaxSplits];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = r + (int64_t)u * RPP;
+      if (row >= rows) continue;
+      const float* src = a.partial + (m0 + row) * a.n + n0 + vc * 4;
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplits; ++sp)
+        if (sp < a.splits) v[u][sp] = *reinterpret_cast<const f32x4*>(src + sp * slice);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = r + (int64_t)u * RPP;
+      if (row >= rows) continue;
+      f32x4 sum = v[u][0];
+#pragma unroll
+      for (int sp = 1; sp < kMaxSplits; ++sp)
+        if (sp < a.splits) sum += v[u][sp];
+      *reinterpret_cast<f32x4*>(a.c + (m0 + row) * a.n + n0 + vc * 4) = sum;
+    }
+  }
+}
+
+template <int BM, int BN, int NS, int MODE>
 __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* lds) {
 
   bool timed_out = false;
@@ -281,45 +327,50 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
 
-  // Tiles in consumer order are dealt out in rounds of C; inside a round,
-  // consecutive tiles go to consumers on the same die (workgroup ids are
-  // dispatched round-robin over the dies), so that tiles sharing A rows or
-  // B columns share an L2.
+  // Work items (tile, K range) in consumer order are dealt out in rounds of
+  // C; inside a round, consecutive items go to consumers on the same die
+  // (workgroup ids are dispatched round-robin over the dies), so that items
+  // sharing A rows or B columns share an L2.
   const int Cn = a.consumers;
   const int groups = (Cn % kXcds == 0) ? kXcds : 1;
   const int per = Cn / groups;
   const int x = cidx % groups, q = cidx / groups;
-  const int64_t total = (int64_t)a.tiles_m * a.tiles_n;
+  const int64_t items = (int64_t)a.tiles_m * a.tiles_n * a.splits;
   const int own_lo = a.rank;  // shard index of the own rank
+  __shared__ int s_last;
 
   for (int64_t w = 0;; ++w) {
     const int64_t j = w * Cn + (int64_t)x * per + q;
-    if (j >= total) break;
-    const int rt = sorted[j / a.tiles_n];
-    const int nt = (int)(j % a.tiles_n);
+    if (j >= items) break;
+    const int64_t tl = j / a.splits;
+    const int sp = (int)(j % a.splits);
+    const int rt = sorted[tl / a.tiles_n];
+    const int nt = (int)(tl % a.tiles_n);
     const int64_t m0 = (int64_t)rt * BM, n0 = (int64_t)nt * BN;
+    const int64_t k_lo = (int64_t)sp * a.split_cols;
+    const int64_t k_hi = min(a.k, k_lo + a.split_cols);
     const int64_t m_end = min(m0 + BM, a.m);
     const bool own = row_tile_own(a, BM, rt);
 
-    Operands op;
-    op.b = a.b;
+    Operands op;  // A and B shifted to the item's K range
+    op.b = a.b + k_lo * a.n;
     op.ldb = a.n;
     op.n0 = n0;
     op.n_valid = a.n;
-    op.k = a.k;
+    op.k = k_hi - k_lo;
     op.lda = a.k;
     int64_t m0_op;
     if (own) {
-      op.a = a.shards[own_lo];
+      op.a = a.shards[own_lo] + k_lo;
       op.m_valid = a.shard_m;
       m0_op = m0 - (int64_t)a.rank * a.shard_m;
     } else {
-      op.a = a.g;
+      op.a = a.g + k_lo;
       op.m_valid = a.m;
       m0_op = m0;
     }
 
-    int last_batch = -1;
+    int last_batch = (int)(k_lo / a.batch_cols) - 1;
     // Waits for every K-batch the step's columns [k0, k1) reach that no
     // earlier step has waited for (steps advance in K order; a step may
     // straddle a batch boundary when the batch width is not a multiple of
@@ -327,7 +378,7 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
     auto before_step = [&](int64_t k0, int64_t k1) {
       if (MODE != kModeFused || own || timed_out) return;
       if (threadIdx.x >= 64) return;  // wave 0 waits for the workgroup (see gemm_tile)
-      const int bt_hi = (int)((k1 - 1) / a.batch_cols);
+      const int bt_hi = (int)((k_lo + k1 - 1) / a.batch_cols);
       if (bt_hi <= last_batch) return;
       const int s_lo = (int)(m0 / a.shard_m), s_hi = (int)((m_end - 1) / a.shard_m);
       for (int bt = last_batch + 1; bt <= bt_hi && !timed_out; ++bt) {
@@ -348,8 +399,23 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
     };
 
     Acc<BM, BN> acc;
-    gemm_tile<BM, BN>(acc, op, m0_op, lds, before_step);
-    acc_store<BM, BN>(acc, a.c, a.n, m0, n0, a.m, a.n);
+    gemm_tile<BM, BN, 64, NS>(acc, op, m0_op, lds, before_step);
+    if (a.splits == 1) {
+      acc_store<BM, BN>(acc, a.c, a.n, m0, n0, a.m, a.n);
+      continue;
+    }
+    acc_store<BM, BN>(acc, a.partial + (int64_t)sp * a.m * a.n, a.n, m0, n0, a.m, a.n);
+    const int64_t before = wg_arrive(a.counters + tl);  // releases this range's partial
+    if (threadIdx.x == 0) {
+      const bool last = before == a.splits - 1;
+      if (last) {
+        wave_acquire();  // the other ranges' partials
+        __hip_atomic_store(a.counters + tl, (int64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      s_last = last;
+    }
+    __syncthreads();
+    if (s_last) reduce_splits<BM, BN>(a, m0, n0);
   }
 }
 
@@ -358,10 +424,10 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
 // units the first round of consumer tiles reads (the bootstrap: the whole
 // chip copies what is needed first); then producers move the remaining units
 // in the caller's order while consumers compute.
-template <int BM, int BN, int MODE>
+template <int BM, int BN, int NS, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void ag_gemm_kernel(AgArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
-  using C = TileCfg<BM, BN>;
+  using C = TileCfg<BM, BN, 64, NS>;
   static_assert(kBootTabBytes <= C::LDS_BYTES, "bootstrap tables alias the stage area");
   int* sorted = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(lds) + C::LDS_BYTES);
   const Sched sc = build_schedule(a, BM, sorted, reinterpret_cast<int*>(lds), MODE != kModeGemmOnly);
@@ -371,12 +437,12 @@ __global__ __launch_bounds__(kThreads, 1) void ag_gemm_kernel(AgArgs a) {
     return;
   }
   __syncthreads();  // every read of the bootstrap tables is done: the stages may be written
-  consume<BM, BN, MODE>(a, (int)blockIdx.x - a.producers, sc.sorted, lds);
+  consume<BM, BN, NS, MODE>(a, (int)blockIdx.x - a.producers, sc.sorted, lds);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NS>
 constexpr int ag_lds_bytes() {
-  return TileCfg<BM, BN>::LDS_BYTES + kOrderBytes;
+  return TileCfg<BM, BN, 64, NS>::LDS_BYTES + kOrderBytes;
 }
 
 }  // namespace ovl
@@ -390,41 +456,55 @@ struct ag_gemm_plan_s {
   int64_t num_units;
   int bm, bn;
   int tiles_m, tiles_n;
+  int splits, split_cols;  // K split (1: none)
 };
 
 namespace {
 
-template <int BM, int BN, int MODE>
+template <int BM, int BN, int NS, int MODE>
 ovl_status launch_fused(const AgArgs& a, hipStream_t stream) {
-  const void* fn = reinterpret_cast<const void*>(&ag_gemm_kernel<BM, BN, MODE>);
-  const int lds = ag_lds_bytes<BM, BN>();
+  const void* fn = reinterpret_cast<const void*>(&ag_gemm_kernel<BM, BN, NS, MODE>);
+  const int lds = ag_lds_bytes<BM, BN, NS>();
   ovl_status st = allow_lds(fn, lds);
   if (st) return st;
-  hipLaunchKernelGGL((ag_gemm_kernel<BM, BN, MODE>), dim3(a.producers + a.consumers), dim3(kThreads), lds,
+  hipLaunchKernelGGL((ag_gemm_kernel<BM, BN, NS, MODE>), dim3(a.producers + a.consumers), dim3(kThreads), lds,
                      stream, a);
   OVL_HIP_TRY(hipGetLastError());
   return OVL_OK;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NS>
 ovl_status occupancy(int* out) {
-  const int lds = ag_lds_bytes<BM, BN>();
-  ovl_status st = allow_lds(reinterpret_cast<const void*>(&ag_gemm_kernel<BM, BN, kModeFused>), lds);
+  const int lds = ag_lds_bytes<BM, BN, NS>();
+  ovl_status st = allow_lds(reinterpret_cast<const void*>(&ag_gemm_kernel<BM, BN, NS, kModeFused>), lds);
   if (st) return st;
-  OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(out, ag_gemm_kernel<BM, BN, kModeFused>, kThreads,
-                                                           lds));
+  OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(out, ag_gemm_kernel<BM, BN, NS, kModeFused>,
+                                                           kThreads, lds));
   return OVL_OK;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NS>
 ovl_status dispatch_mode(const AgArgs& a, uint32_t mode, hipStream_t stream) {
   switch (mode) {
-    case OVL_MODE_FUSED: return launch_fused<BM, BN, kModeFused>(a, stream);
-    case OVL_MODE_BARRIER: return launch_fused<BM, BN, kModeBarrier>(a, stream);
-    case OVL_MODE_GEMM_ONLY: return launch_fused<BM, BN, kModeGemmOnly>(a, stream);
+    case OVL_MODE_FUSED: return launch_fused<BM, BN, NS, kModeFused>(a, stream);
+    case OVL_MODE_BARRIER: return launch_fused<BM, BN, NS, kModeBarrier>(a, stream);
+    case OVL_MODE_GEMM_ONLY: return launch_fused<BM, BN, NS, kModeGemmOnly>(a, stream);
     default: return OVL_EINVAL;
   }
 }
+
+// The three tile configurations: 256x256 with a 2-stage ring; 128x128 with
+// a 2-stage ring; 128x128 with a 4-stage ring for split-K plans (skinny,
+// bandwidth-bound: more of B in flight per workgroup).
+enum TileKind { kBig = 0, kSmall = 1, kSplit = 2 };
+
+inline TileKind tile_kind(const ag_gemm_plan_s* p) {
+  return p->bm == 256 ? kBig : (p->splits > 1 ? kSplit : kSmall);
+}
+
+// Compute units the plan assumes (MI355X); a device with fewer runs the
+// same work items in more rounds.
+constexpr int kPlanCus = 256;
 
 }  // namespace
 
@@ -473,6 +553,19 @@ extern "C" ovl_status ag_gemm_plan(const ag_gemm_desc* d, ag_gemm_plan_t* out) {
     delete p;
     return OVL_EUNSUPPORTED;
   }
+  // Split K when the 128x128 tiles fill less than half of the consumers and
+  // K is long: each range at least 4 K-steps of 64, at most kMaxSplits.
+  p->splits = 1;
+  p->split_cols = (int32_t)d->k;
+  const int64_t tiles = (int64_t)p->tiles_m * p->tiles_n;
+  const int64_t consumers = kPlanCus - std::max(kXcds, kPlanCus / 8);
+  if (p->bm == 128) {
+    const int64_t s = std::min<int64_t>({consumers / tiles, ceil_div(d->k, 256), kMaxSplits});
+    if (s >= 2) {
+      p->split_cols = (int32_t)(ceil_div(ceil_div(d->k, s), 64) * 64);
+      p->splits = (int)ceil_div(d->k, p->split_cols);
+    }
+  }
   *out = p;
   return OVL_OK;
 }
@@ -519,7 +612,20 @@ extern "C" size_t ag_gemm_flags_bytes(ag_gemm_plan_t p) {
   return p ? (size_t)p->num_units * (size_t)p->d.flag_stride : 0;
 }
 
-extern "C" size_t ag_gemm_workspace_bytes(ag_gemm_plan_t p) { return p ? 256 : 0; }
+// Error record (256 bytes reserved); with a K split, one arrival counter per
+// tile (padded to 256 bytes), then the fp32 partial products [splits][m][n].
+static size_t ag_counters_offset() { return 256; }
+static size_t ag_partial_offset(const ag_gemm_plan_s* p) {
+  return ag_counters_offset() + (size_t)ceil_div((int64_t)p->tiles_m * p->tiles_n * 8, 256) * 256;
+}
+
+extern "C" size_t ag_gemm_workspace_bytes(ag_gemm_plan_t p) {
+  if (!p) return 0;
+  if (p->splits == 1) return 256;
+  return ag_partial_offset(p) + (size_t)p->splits * p->m * p->d.n * 4;
+}
+
+extern "C" int32_t ag_gemm_splits(ag_gemm_plan_t p) { return p ? p->splits : 0; }
 
 extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, const void* b, void* gathered,
                                   float* c, int64_t* flags, void* workspace, int64_t epoch,
@@ -575,6 +681,11 @@ extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, c
   a.num_units = (int32_t)p->num_units;
   a.tiles_m = p->tiles_m;
   a.tiles_n = p->tiles_n;
+  a.splits = p->splits;
+  a.split_cols = p->split_cols;
+  a.counters = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(workspace) + ag_counters_offset());
+  a.partial = p->splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ag_partial_offset(p))
+                            : nullptr;
 
   const int64_t tiles = (int64_t)p->tiles_m * p->tiles_n;
   const uint32_t req_prod = opts ? opts->producers : 0;
@@ -592,7 +703,9 @@ extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, c
   }
 
   int occ = 0;
-  st = (p->bm == 256) ? occupancy<256, 256>(&occ) : occupancy<128, 128>(&occ);
+  const TileKind kind = tile_kind(p);
+  st = kind == kBig ? occupancy<256, 256, 2>(&occ)
+                    : (kind == kSmall ? occupancy<128, 128, 2>(&occ) : occupancy<128, 128, 4>(&occ));
   if (st) return st;
   const int64_t resident = (int64_t)std::max(occ, 1) * di.cus;
   int P = 0;
@@ -601,7 +714,7 @@ extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, c
     P = (int)std::min<int64_t>(P, a.num_units);
     if (P >= resident) return OVL_EINVAL;
   }
-  int64_t Cn = std::min<int64_t>(tiles, resident - P);
+  int64_t Cn = std::min<int64_t>(tiles * p->splits, resident - P);
   if (Cn > kXcds) Cn -= Cn % kXcds;  // keep whole die groups
   a.producers = P;
   a.consumers = (int32_t)Cn;
@@ -609,5 +722,7 @@ extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, c
     st = epoch_accept(flags, epoch);
     if (st) return st;
   }
-  return (p->bm == 256) ? dispatch_mode<256, 256>(a, mode, stream) : dispatch_mode<128, 128>(a, mode, stream);
+  return kind == kBig ? dispatch_mode<256, 256, 2>(a, mode, stream)
+                      : (kind == kSmall ? dispatch_mode<128, 128, 2>(a, mode, stream)
+                                        : dispatch_mode<128, 128, 4>(a, mode, stream));
 }

@@ -97,11 +97,13 @@ template <>
 __device__ inline uint32_t swz_a<32>(uint32_t r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 __device__ inline uint32_t swz_b(uint32_t k) { return (0xCA60u >> ((k & 3) * 4)) & 15; }  // 0, 6, 10, 12
 
-template <int BM, int BN, int BK = 64>
+// NSTAGES: LDS ring depth (0: 4 for BK 32, 2 for BK 64).  Deeper rings keep
+// more loads in flight for bandwidth-bound (skinny) tiles.
+template <int BM, int BN, int BK = 64, int NSTAGES = 0>
 struct TileCfg {
   static_assert(BM % 64 == 0 && BN % 128 == 0 && BN <= 256 && BM <= 256, "tile shape");
   static_assert(BK == 32 || BK == 64, "K step");
-  static constexpr int NS = BK == 32 ? 4 : 2;     // LDS stages
+  static constexpr int NS = NSTAGES ? NSTAGES : (BK == 32 ? 4 : 2);  // LDS stages
   static constexpr int FM = BM / 64;             // 32-row blocks per wave
   static constexpr int FN = BN / 64;             // 32-col blocks per wave
   static constexpr int KK = BK / 16;             // MFMA sub-steps per stage
@@ -455,10 +457,10 @@ __device__ inline void acc_zero(Acc<BM, BN>& acc) {
 // calls it, before a workgroup barrier that precedes the first load of that
 // step (so a wave that acquires there orders the whole workgroup's loads).
 // Ends with a workgroup barrier, so LDS may be reused at once.
-template <int BM, int BN, int BK = 64, class BeforeStep>
+template <int BM, int BN, int BK = 64, int NSTAGES = 0, class BeforeStep>
 __device__ inline void gemm_tile(Acc<BM, BN>& acc, const Operands& op, int64_t m0, uint16_t* lds,
                                  BeforeStep before_step) {
-  using C = TileCfg<BM, BN, BK>;
+  using C = TileCfg<BM, BN, BK, NSTAGES>;
   constexpr int NS = C::NS;
   static_assert(NS - 2 <= 2, "wait_stage_loads covers up to two pending stages");
   uint8_t* l8 = reinterpret_cast<uint8_t*>(lds);

@@ -33,7 +33,7 @@ ERROR_RECORD_BYTES = 64
 
 EXPORTS = (
     "ag_gemm_plan", "ag_gemm_plan_destroy", "ag_gemm_num_units", "ag_gemm_flags_bytes",
-    "ag_gemm_workspace_bytes", "ag_gemm_run",
+    "ag_gemm_workspace_bytes", "ag_gemm_splits", "ag_gemm_run",
     "gemm_rs_flags_bytes", "gemm_rs_workspace_bytes", "gemm_rs_run",
     "a2a_flags_bytes", "a2a_workspace_bytes", "a2a_dispatch_grouped_gemm_run",
     "ovl_flags_reset", "ovl_check", "ovl_strerror", "ovl_copy",
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
     L.ag_gemm_flags_bytes.restype = c_size_t
     L.ag_gemm_workspace_bytes.argtypes = [c_void_p]
     L.ag_gemm_workspace_bytes.restype = c_size_t
+    L.ag_gemm_splits.argtypes = [c_void_p]
+    L.ag_gemm_splits.restype = c_int32
     L.ag_gemm_run.argtypes = [c_void_p, POINTER(c_void_p), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                               c_int64, c_void_p, POINTER(Opts), c_void_p]
     L.ag_gemm_run.restype = st
@@ -188,6 +190,10 @@ class AgGemmPlan:
     @property
     def workspace_bytes(self) -> int:
         return lib().ag_gemm_workspace_bytes(self.handle)
+
+    @property
+    def splits(self) -> int:
+        return lib().ag_gemm_splits(self.handle)
 
 
 def ag_gemm_plan(*args, **kw) -> AgGemmPlan:

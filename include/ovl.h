@@ -143,6 +143,17 @@ size_t ag_gemm_workspace_bytes(ag_gemm_plan_t plan);  /* >= OVL_ERROR_RECORD_BYT
 int32_t ag_gemm_row_tiles(ag_gemm_plan_t plan);
 int32_t ag_gemm_tile_rows(ag_gemm_plan_t plan);
 
+/* K split of the plan (1 = none).  When few output tiles would leave most
+ * compute units idle (skinny, bandwidth-bound shapes), each tile is computed
+ * as `splits` ranges of K by different workgroups; every range stores its
+ * fp32 product in the workspace and the last range to finish sums them in
+ * range order, C = ((P_0 + P_1) + ...), so the result does not depend on
+ * timing or producer order.  The workspace then holds one arrival counter
+ * per tile (each returned to zero by its tile's last range) and the
+ * partial products; after a run that ended in an error, reset the workspace
+ * (ovl_flags_reset) before the next. */
+int32_t ag_gemm_splits(ag_gemm_plan_t plan);
+
 /* The order in which consumers take rows of output tiles for a given
  * producer order (HOST int32 [num_units] permutation, or NULL = ascending):
  * writes ag_gemm_row_tiles(plan) row-tile indices to `out` (HOST).  Rows of

@@ -174,3 +174,21 @@ def test_flag_and_workspace_sizes():
     ad = o.a2a_desc(8, 0, 4096, 4096, 1408, 2, 64, 8, 128)
     assert o.a2a_flags_bytes(ad) == 8 * 128
     assert o.a2a_workspace_bytes(ad) >= o.ERROR_RECORD_BYTES + 8 * 8
+
+
+@pytest.mark.parametrize("name,tpf,splits", [
+    ("ag_r2_128x256x256", 0, 1),            # K too short to split
+    ("ag_r8_8192x3584x4096", 1, 1),         # enough 256x256 tiles
+    ("ag_r8_skinny_128x7168x8192", 4, 4),   # 56 tiles of 128x128: K in 4 ranges
+])
+def test_split_k_plan(name, tpf, splits):
+    cfg = synth.CONFIGS[name]
+    p = ovl().ag_gemm_plan(cfg.ranks, 0, cfg.shard_m, cfg.k, cfg.n, cfg.tile_m, cfg.tile_n, tpf, 8)
+    assert p.splits == splits
+    if splits > 1:
+        m = cfg.ranks * cfg.shard_m
+        tiles = -(-m // 128) * -(-cfg.n // 128)
+        counters = -(-tiles * 8 // 256) * 256
+        assert p.workspace_bytes == 256 + counters + splits * m * cfg.n * 4
+    else:
+        assert p.workspace_bytes == 256

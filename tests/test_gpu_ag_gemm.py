@@ -104,6 +104,50 @@ def test_ragged_shapes_match_oracle(shape):
     _full_check(case)
 
 
+# ------------------------------------------------------------------ split K
+
+def _counters_are_zero(case):
+    tiles = -(-case.cfg.m // 128) * -(-case.cfg.n // 128)  # split plans use 128x128 tiles
+    cnt = host(case.ws)[256: 256 + 8 * tiles].view(np.int64)
+    return not cnt.any()
+
+
+@pytest.mark.parametrize("mode", [0, 3, 2])
+def test_split_k_small_integers_bit_exact(mode):
+    # 64 x 256 output in two 128x128 tiles, K = 2048 in 8 ranges of 256.
+    cfg = _small("splitk", 4, 16, 2048, 256, 16, 128, seed=11)
+    case = AgCase(cfg, "smallint", tiles_per_flag=2)
+    assert case.plan.splits == 8
+    _, c_ref = oracle.ag_gemm(case.shards, case.b)
+    if mode == 2:  # GEMM only: the gathered operand must already be there
+        assert case.run(1, case.order(1, "units"), mode=1)[0] == 0
+    for epoch in (2, 3):
+        st, det = case.run(epoch, case.order(epoch, "units"), mode=mode)
+        assert st == 0, det
+        assert np.array_equal(host(case.c), c_ref.astype(np.float32))
+        assert _counters_are_zero(case)
+    if mode != 2:
+        case.check_gathered_and_flags(3)
+
+
+def test_split_k_ragged_orders_and_modes_agree():
+    # 150 x 200 output (2 x 2 tiles of 128, ragged), K = 1000 in ranges of
+    # 256, 256, 256, 232; flag batches of 120 columns straddle the ranges.
+    cfg = _small("splitk_ragged", 3, 50, 1000, 200, 50, 40, seed=12)
+    case = AgCase(cfg, tiles_per_flag=3)
+    assert case.plan.splits == 4
+    first = None
+    for epoch in range(1, 5):
+        st, det = case.run(epoch, case.order(epoch, "units"), mode=0 if epoch < 4 else 3)
+        assert st == 0, det
+        case.check_gathered_and_flags(epoch)
+        assert _counters_are_zero(case)
+        c = host(case.c).copy()
+        if first is None:
+            first = _full_check(case).copy()
+        assert np.array_equal(c.view(np.uint32), first.view(np.uint32)), "C bits changed with producer order"
+
+
 def test_epochs_reuse_flags_without_reset():
     case = AgCase(synth.CONFIGS["ag_r2_128x256x256"], tiles_per_flag=2, flag_stride=128)
     first = None
