@@ -235,7 +235,7 @@ def main():
                      "traffic": (TRAFFIC_BYTES if kernel_sources_sha() == TRAFFIC_SOURCES_SHA else None),
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-scaled)",
                      "algorithmic_flops_per_launch": cfg.flops(),
-                     "kernel": "ag_gemm_kernel<256,256,fused>", "avg_launch_us": round(kern_us, 2)},
+                     "kernel": "ag_gemm_kernel<256, 256, 2, 0> (fused)", "avg_launch_us": round(kern_us, 2)},
         "overlap": overlap,
         "side": extra,
     }
@@ -296,6 +296,52 @@ def side_workloads(reps, flush):
     res[cfg.name] = {"fused_us": t, "gemm_only_us": g,
                      "TFLOPs": cfg.flops() / (t["median_us"] * 1e-6) / 1e12,
                      "pct_of_bf16_peak": 100 * cfg.flops() / (t["median_us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
+
+    # All-to-all dispatch -> grouped expert GEMM (rank 0 receives the most rows).
+    cfg = synth.CONFIGS["a2a_r8_t4096_h4096_e64"]
+    log(f"[bench] side {cfg.name}")
+    x, topk, w = synth.dispatch_inputs(cfg)
+    R, cap, E = cfg.ranks, cfg.cap, cfg.experts_per_rank
+    desc = ovl.a2a_desc(R, cfg.rank, cfg.tokens, cfg.hidden, cfg.n, cfg.topk, cfg.num_experts, E, 8)
+    fb = ovl.a2a_flags_bytes(desc)
+    d_x = [dev(v) for v in x]
+    d_topk = [dev(t) for t in topk]
+    d_w = dev(w)
+    recv_x = torch.zeros(R, cap, cfg.hidden, dtype=torch.int16, device="cuda")
+    recv_src = torch.zeros(R, cap, dtype=torch.int32, device="cuda")
+    recv_count = torch.zeros(R, E, dtype=torch.int32, device="cuda")
+    y = torch.zeros(R, cap, cfg.n, dtype=torch.float32, device="cuda")
+    flags = torch.zeros(fb, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(ovl.a2a_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    ovl.ovl_flags_reset(flags, fb, ws, ws.numel())
+    ep = [0]
+
+    def a2a(mode=0):
+        ep[0] += 1
+        ovl.a2a_dispatch_grouped_gemm_run(desc, d_x, d_topk, d_w, recv_x, recv_src, recv_count, y, flags, ws,
+                                          ep[0], mode=mode)
+
+    a2a()
+    t = timed_reps(a2a, reps, flush)
+    disp = timed_reps(lambda: a2a(ovl.MODE_COPY_ONLY), reps, flush)
+    g = timed_reps(lambda: a2a(ovl.MODE_GEMM_ONLY), reps, flush)
+    ovl.ovl_check(ws)
+    rows = int(recv_count.sum().item())
+    lo = cfg.rank * E
+    uniq = sum(int(((tk >= lo) & (tk < lo + E)).any(axis=1).sum()) for tk in topk)
+    d_bytes = uniq * cfg.hidden * 2 + rows * (cfg.hidden * 2 + 4)  # token reads; row + source writes
+    flops = 2.0 * rows * cfg.hidden * cfg.n
+    res[cfg.name] = {"fused_us": t, "dispatch_only_us": disp, "gemm_only_us": g,
+                     "routed_rows": rows, "unique_tokens": uniq,
+                     "dispatch_bytes": d_bytes, "grouped_gemm_flops": flops,
+                     "dispatch_GBps": d_bytes / (disp["median_us"] * 1e-6) / 1e9,
+                     "dispatch_pct_of_hbm_peak": 100 * d_bytes / (disp["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                     "gemm_only_TFLOPs": flops / (g["median_us"] * 1e-6) / 1e12,
+                     "fused_TFLOPs": flops / (t["median_us"] * 1e-6) / 1e12,
+                     "fused_pct_of_bf16_peak": 100 * flops / (t["median_us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                     "fused_over_dispatch_plus_gemm": t["median_us"] / (disp["median_us"] + g["median_us"]),
+                     "fused_over_gemm_only": t["median_us"] / g["median_us"]}
+    del recv_x, y
 
     # Plain copy, for the HBM reference point.
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")

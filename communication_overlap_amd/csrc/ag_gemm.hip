@@ -58,24 +58,30 @@ enum { kModeFused = 0, kModeBarrier = 1, kModeGemmOnly = 2 };
 // ---------------------------------------------------------------- producer
 
 // Copies rows x cols bf16 (cols a multiple of 8) between two row-major
-// matrices of row pitch ld, 16 bytes per lane and 16 vectors in flight per
+// matrices of row pitch ld, 16 bytes per lane, in blocks of U vectors per
 // lane; the (row, vector) position advances incrementally, without a
-// division per vector.
+// division per vector.  The loads of block i+1 are issued before the stores
+// of block i, so that a lane always has a block in flight (vector memory
+// counters complete in order: waiting for the loads does not wait for the
+// stores issued after them).
 __device__ inline void copy_block(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int64_t rows,
                                   int64_t cols, int64_t ld) {
-  constexpr int U = 16;
+  constexpr int U = 8;
   const uint32_t vpr = (uint32_t)(cols / 8);
   const uint32_t total = (uint32_t)(rows * vpr);
   const uint32_t step_r = kThreads / vpr, step_c = kThreads % vpr;
-  uint32_t r = threadIdx.x / vpr, c = threadIdx.x % vpr;
-  for (uint32_t base = 0; base < total; base += kThreads * U) {
+  uint32_t r = threadIdx.x / vpr, c = threadIdx.x % vpr;  // next vector to load
+  const uint32_t blocks = (total + kThreads * U - 1) / (kThreads * U);
+  struct Blk {
     u32x4 v[U];
-    uint32_t rr[U], cc[U];
+    uint32_t off[U];  // element offset, or ~0u past the end
+  };
+  auto load = [&](uint32_t bi, Blk& b) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      rr[j] = r;
-      cc[j] = c;
-      if (base + j * kThreads + threadIdx.x < total) v[j] = ld16_nt(src + r * ld + c * 8);
+      const bool in = bi * kThreads * U + j * kThreads + threadIdx.x < total;
+      b.off[j] = in ? r * (uint32_t)ld + c * 8 : ~0u;
+      if (in) b.v[j] = ld16_nt(src + b.off[j]);
       c += step_c;
       r += step_r;
       if (c >= vpr) {
@@ -83,9 +89,20 @@ __device__ inline void copy_block(const uint16_t* __restrict__ src, uint16_t* __
         ++r;
       }
     }
+  };
+  auto store = [&](const Blk& b) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
-      if (base + j * kThreads + threadIdx.x < total) st16(dst + rr[j] * ld + cc[j] * 8, v[j]);
+      if (b.off[j] != ~0u) st16(dst + b.off[j], b.v[j]);
+  };
+  Blk x, y;
+  if (blocks > 0) load(0, x);
+  for (uint32_t bi = 0; bi < blocks; bi += 2) {
+    if (bi + 1 < blocks) load(bi + 1, y);
+    store(x);
+    if (bi + 1 >= blocks) break;
+    if (bi + 2 < blocks) load(bi + 2, x);
+    store(y);
   }
 }
 
@@ -124,9 +141,9 @@ __device__ inline void move_unit(const AgArgs& a, int u) {
 // bootstrap panels' units when sc is given (those were moved already).
 __device__ inline void produce(const AgArgs& a, int w, int P, const Sched* sc) {
   for (int i = w; i < a.num_units; i += P) {
-    const int u = a.order ? a.order[i] : i;
+    const int u = uniform(a.order ? a.order[i] : i);
     if (u < 0 || u >= a.num_units) continue;  // not a unit index: nothing to move
-    if (sc && sc->bidx[u / a.batches] >= 0) continue;
+    if (sc && uniform(sc->bidx[u / a.batches]) >= 0) continue;
     move_unit(a, u);
   }
 }
@@ -137,7 +154,8 @@ __device__ inline void produce(const AgArgs& a, int w, int P, const Sched* sc) {
 __device__ inline void produce_boot(const AgArgs& a, int w, int G, const Sched& sc) {
   const int items = sc.n_boot * a.batches;
   for (int i = w; i < items; i += G)
-    if ((sc.present[i >> 5] >> (i & 31)) & 1u) move_unit(a, sc.boot[i / a.batches] * a.batches + i % a.batches);
+    if (uniform((sc.present[i >> 5] >> (i & 31)) & 1u))
+      move_unit(a, uniform(sc.boot[i / a.batches]) * a.batches + i % a.batches);
 }
 
 __global__ __launch_bounds__(kThreads) void ag_produce_kernel(AgArgs a) {
@@ -262,7 +280,7 @@ __device__ Sched build_schedule(const AgArgs& a, int BM, int* sorted, int* tab, 
   sc.boot = boot;
   sc.bidx = bidx;
   sc.present = present;
-  sc.n_boot = s_nboot;
+  sc.n_boot = uniform(s_nboot);
   sc.rows1 = rows1;
   return sc;
 }
@@ -344,7 +362,7 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
     if (j >= items) break;
     const int64_t tl = j / a.splits;
     const int sp = (int)(j % a.splits);
-    const int rt = sorted[tl / a.tiles_n];
+    const int rt = uniform(sorted[tl / a.tiles_n]);
     const int nt = (int)(tl % a.tiles_n);
     const int64_t m0 = (int64_t)rt * BM, n0 = (int64_t)nt * BN;
     const int64_t k_lo = (int64_t)sp * a.split_cols;
@@ -415,7 +433,7 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
       s_last = last;
     }
     __syncthreads();
-    if (s_last) reduce_splits<BM, BN>(a, m0, n0);
+    if (uniform(s_last)) reduce_splits<BM, BN>(a, m0, n0);
   }
 }
 
