@@ -44,11 +44,14 @@ struct AgArgs {
   int32_t producers, consumers;
   int32_t tiles_m, tiles_n;
   // Split K: each output tile is computed as `splits` column ranges of A
-  // (split_cols wide); each range's fp32 product goes to partial[s] and the
-  // last range to arrive (counters[tile]) sums them in range order into C.
-  int32_t splits, split_cols;
+  // (split_cols wide); each range's fp32 product goes to partial[s], and C
+  // is their sum in range order.  With split_sync (every range of the launch
+  // runs in its first round, so the ranges of a tile run at the same time)
+  // the ranges wait for each other on counters[2 * tile] and each sums one
+  // stripe of rows; otherwise the last range to arrive sums the whole tile.
+  int32_t splits, split_cols, split_sync;
   float* partial;     // [splits][m][n]
-  int64_t* counters;  // [tiles], zero between launches
+  int64_t* counters;  // [tiles][2], zero between launches
 };
 
 constexpr int kMaxSplits = 8;
@@ -287,20 +290,20 @@ __device__ Sched build_schedule(const AgArgs& a, int BM, int* sorted, int* tab, 
 
 // ---------------------------------------------------------------- consumer
 
-// Last range of a split tile: C[rows, cols] = ((P_0 + P_1) + ...) over the
+// Tile rows [lo, hi) of a split tile: C = ((P_0 + P_1) + ...) over the
 // partial products in range order, 16 bytes per lane, four row groups of
 // every partial loaded before the first add.
 template <int BM, int BN>
-__device__ void reduce_splits(const AgArgs& a, int64_t m0, int64_t n0) {
+__device__ void reduce_splits(const AgArgs& a, int64_t m0, int64_t n0, int64_t lo, int64_t hi) {
   constexpr int VPR = BN / 4;           // 16-byte vectors per tile row
   constexpr int RPP = kThreads / VPR;   // rows per pass
   constexpr int U = 4;
-  const int64_t rows = min((int64_t)BM, a.m - m0);
+  const int64_t rows = min(hi, a.m - m0);
   const int64_t cols = min((int64_t)BN, a.n - n0);
   const int vc = threadIdx.x % VPR, r0 = threadIdx.x / VPR;
   if (vc * 4 >= cols) return;  // n is a multiple of 8: a vector is all in or all out
   const int64_t slice = a.m * a.n;
-  for (int64_t r = r0; r < rows; r += RPP * U) {
+  for (int64_t r = lo + r0; r < rows; r += RPP * U) {
     f32x4 v[U][kMaxSplits];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -388,32 +391,70 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
       m0_op = m0;
     }
 
-    int last_batch = (int)(k_lo / a.batch_cols) - 1;
-    // Waits for every K-batch the step's columns [k0, k1) reach that no
-    // earlier step has waited for (steps advance in K order; a step may
-    // straddle a batch boundary when the batch width is not a multiple of
-    // the K-step).
-    auto before_step = [&](int64_t k0, int64_t k1) {
+    // Batches (ready, last] of this item's K range are the ones still to be
+    // acquired.  Waiting is done by wave 0 one K-step ahead (see gemm_tile).
+    // One round trip reads every flag of every remaining batch of the item,
+    // lanes in parallel, so that a producer that runs ahead costs one poll
+    // per item instead of one per batch; the item then knows all batches
+    // up to the first missing unit are there.
+    int ready = (int)(k_lo / a.batch_cols) - 1;
+    const int last = (int)((k_hi - 1) / a.batch_cols);
+    const int s_lo = (int)(m0 / a.shard_m), s_hi = (int)((m_end - 1) / a.shard_m);
+    // Calls f(u) for the units of batch bt that cover the tile's rows.
+    auto units_of = [&](int bt, auto f) {
+      for (int s = s_lo; s <= s_hi; ++s) {
+        const int64_t lo = max(m0, (int64_t)s * a.shard_m) - (int64_t)s * a.shard_m;
+        const int64_t hi = min(m_end, (int64_t)(s + 1) * a.shard_m) - (int64_t)s * a.shard_m;
+        for (int p = (int)(lo / a.unit_rows); p <= (int)((hi - 1) / a.unit_rows); ++p)
+          f(((int64_t)s * a.panels + p) * a.batches + bt);
+      }
+    };
+    auto before_step = [&](int64_t, int64_t k1) {
       if (MODE != kModeFused || own || timed_out) return;
       if (threadIdx.x >= 64) return;  // wave 0 waits for the workgroup (see gemm_tile)
-      const int bt_hi = (int)((k_lo + k1 - 1) / a.batch_cols);
-      if (bt_hi <= last_batch) return;
-      const int s_lo = (int)(m0 / a.shard_m), s_hi = (int)((m_end - 1) / a.shard_m);
-      for (int bt = last_batch + 1; bt <= bt_hi && !timed_out; ++bt) {
-        for (int s = s_lo; s <= s_hi && !timed_out; ++s) {
-          const int64_t lo = max(m0, (int64_t)s * a.shard_m) - (int64_t)s * a.shard_m;
-          const int64_t hi = min(m_end, (int64_t)(s + 1) * a.shard_m) - (int64_t)s * a.shard_m;
-          for (int p = (int)(lo / a.unit_rows); p <= (int)((hi - 1) / a.unit_rows); ++p) {
-            const int64_t u = ((int64_t)s * a.panels + p) * a.batches + bt;
-            if (!wave_poll(a.flags + u * a.flag_stride, a.epoch, a.spin_limit, a.err, kSiteAgUnit, u)) {
-              timed_out = true;
-              break;
-            }
-          }
+      const int need = (int)((k_lo + k1 - 1) / a.batch_cols);
+      if (need <= ready) return;
+      const int lane = lane_id();
+      for (uint64_t polls = 0;; ++polls) {
+        int bad = last + 1;  // first batch with a unit not there yet (this lane's share)
+        // Units numbered batch-major; lane l reads units l, l + 64, ...: the
+        // numbering pass only picks this lane's unit, then one load per lane
+        // goes out for all lanes at once.
+        for (int base = 0;; base += 64) {
+          int64_t mine = -1;
+          int mine_bt = 0, i = 0;
+          for (int bt = ready + 1; bt <= last; ++bt)
+            units_of(bt, [&](int64_t u) {
+              if (i == base + lane) {
+                mine = u;
+                mine_bt = bt;
+              }
+              ++i;
+            });
+          if (mine >= 0 &&
+              __hip_atomic_load(a.flags + mine * a.flag_stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.epoch)
+            bad = min(bad, mine_bt);
+          if (base + 64 >= i) break;
         }
+        for (int d = 1; d < 64; d <<= 1) bad = min(bad, __shfl_xor(bad, d, 64));
+        bad = uniform(bad);
+        if (bad > need) {
+          ready = bad - 1;
+          break;
+        }
+        if (polls >= a.spin_limit) {
+          // Name the first missing unit in the error record.
+          for (int bt = ready + 1; bt <= need && !timed_out; ++bt)
+            units_of(bt, [&](int64_t u) {
+              if (!timed_out && !wave_poll(a.flags + u * a.flag_stride, a.epoch, 0, a.err, kSiteAgUnit, u))
+                timed_out = true;
+            });
+          timed_out = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
       }
-      last_batch = bt_hi;
-      wave_acquire();  // one acquire for all the units polled
+      wave_acquire();  // one acquire for all the units seen
     };
 
     Acc<BM, BN> acc;
@@ -423,17 +464,36 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
       continue;
     }
     acc_store<BM, BN>(acc, a.partial + (int64_t)sp * a.m * a.n, a.n, m0, n0, a.m, a.n);
-    const int64_t before = wg_arrive(a.counters + tl);  // releases this range's partial
+    int64_t* cnt = a.counters + 2 * tl;
+    const int64_t before = wg_arrive(cnt);  // releases this range's partial
+    if (a.split_sync) {
+      // Wait for the tile's other ranges, then sum stripe sp of its rows.
+      if (threadIdx.x < 64 && !timed_out) {
+        if (!wave_poll(cnt, a.splits, a.spin_limit, a.err, kSiteAgSplit, tl)) timed_out = true;
+        wave_acquire();
+      }
+      __syncthreads();
+      const int64_t rs = (BM + a.splits - 1) / a.splits;
+      reduce_splits<BM, BN>(a, m0, n0, sp * rs, min((int64_t)BM, (sp + 1) * rs));
+      // The last range out returns both counters to zero for the next launch.
+      const int64_t out = wg_arrive(cnt + 1);
+      if (threadIdx.x == 0 && out == a.splits - 1) {
+        __hip_atomic_store(cnt, (int64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(cnt + 1, (int64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      continue;
+    }
     if (threadIdx.x == 0) {
       const bool last = before == a.splits - 1;
       if (last) {
         wave_acquire();  // the other ranges' partials
-        __hip_atomic_store(a.counters + tl, (int64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(cnt, (int64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       s_last = last;
     }
     __syncthreads();
-    if (uniform(s_last)) reduce_splits<BM, BN>(a, m0, n0);
+    if (uniform(s_last)) reduce_splits<BM, BN>(a, m0, n0, 0, BM);
   }
 }
 
@@ -630,11 +690,12 @@ extern "C" size_t ag_gemm_flags_bytes(ag_gemm_plan_t p) {
   return p ? (size_t)p->num_units * (size_t)p->d.flag_stride : 0;
 }
 
-// Error record (256 bytes reserved); with a K split, one arrival counter per
-// tile (padded to 256 bytes), then the fp32 partial products [splits][m][n].
+// Error record (256 bytes reserved); with a K split, two arrival counters
+// per tile (padded to 256 bytes), then the fp32 partial products
+// [splits][m][n].
 static size_t ag_counters_offset() { return 256; }
 static size_t ag_partial_offset(const ag_gemm_plan_s* p) {
-  return ag_counters_offset() + (size_t)ceil_div((int64_t)p->tiles_m * p->tiles_n * 8, 256) * 256;
+  return ag_counters_offset() + (size_t)ceil_div((int64_t)p->tiles_m * p->tiles_n * 16, 256) * 256;
 }
 
 extern "C" size_t ag_gemm_workspace_bytes(ag_gemm_plan_t p) {
@@ -736,6 +797,7 @@ extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, c
   if (Cn > kXcds) Cn -= Cn % kXcds;  // keep whole die groups
   a.producers = P;
   a.consumers = (int32_t)Cn;
+  a.split_sync = p->splits > 1 && tiles * p->splits <= Cn;  // every range in the first round
   if (needs_copy) {
     st = epoch_accept(flags, epoch);
     if (st) return st;

@@ -26,7 +26,9 @@ struct ErrRec {
 };
 static_assert(sizeof(ErrRec) == 64, "error record size");
 
-enum : int32_t { kSiteAgUnit = 1, kSiteAgBarrier = 2, kSiteRsIn = 3, kSiteA2aSlice = 4, kSiteRsOwn = 5 };
+enum : int32_t {
+  kSiteAgUnit = 1, kSiteAgBarrier = 2, kSiteRsIn = 3, kSiteA2aSlice = 4, kSiteRsOwn = 5, kSiteAgSplit = 6
+};
 
 __device__ inline void report_error(ErrRec* e, int32_t code, int32_t site, int64_t index,
                                     int64_t observed, int64_t expected) {

@@ -64,20 +64,44 @@ __device__ void reduce_job(const RsArgs& a, int64_t j, int64_t J, bool& timed_ou
   // Wave 0 waits for the own tiles this job touches and, with flags on, for
   // every peer's partial of them; the barrier hands the acquire to the
   // other waves.
-  // All flags are polled first, then one acquire covers them.
+  // Every flag the job needs (own tiles, and with flags on every peer's
+  // partial of them) is read in one round trip, lanes in parallel, until all
+  // are set; then one acquire covers them.  Flag i of the job: tile
+  // t0 + i / R, and within it the own-tile flag (peer slot `rank`) or peer
+  // p's in flag.
   if (threadIdx.x < 64 && !timed_out) {
-    for (int64_t t = q0 / kRsTile; t <= (q1 - 1) / kRsTile && !timed_out; ++t) {
-      if (!wave_poll(a.own_flags + t, a.epoch, a.spin_limit, a.err, kSiteRsOwn, t)) {
+    const int64_t t0 = q0 / kRsTile, nt = (q1 - 1) / kRsTile - t0 + 1;
+    const int64_t nflags = nt * (a.sync ? a.ranks : 1);
+    auto flag_at = [&](int64_t i, int64_t* idx, int32_t* site) -> const int64_t* {
+      const int64_t t = t0 + (a.sync ? i / a.ranks : i);
+      const int p = a.sync ? (int)(i % a.ranks) : a.rank;
+      if (p == a.rank) {
+        *idx = t;
+        *site = kSiteRsOwn;
+        return a.own_flags + t;
+      }
+      *idx = (int64_t)p * tpb + t;
+      *site = kSiteRsIn;
+      return a.in_flags + *idx * a.flag_stride;
+    };
+    for (uint64_t polls = 0;; ++polls) {
+      bool missing = false;
+      for (int64_t i = lane_id(); i < nflags; i += 64) {
+        int64_t idx;
+        int32_t site;
+        missing |= __hip_atomic_load(flag_at(i, &idx, &site), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.epoch;
+      }
+      if (!__ballot(missing)) break;
+      if (polls >= a.spin_limit) {
+        for (int64_t i = 0; i < nflags && !timed_out; ++i) {  // name the first missing flag
+          int64_t idx;
+          int32_t site;
+          if (!wave_poll(flag_at(i, &idx, &site), a.epoch, 0, a.err, site, idx)) timed_out = true;
+        }
         timed_out = true;
         break;
       }
-      if (!a.sync) continue;
-      for (int p = 0; p < a.ranks && !timed_out; ++p) {
-        if (p == a.rank) continue;
-        const int64_t idx = (int64_t)p * tpb + t;
-        if (!wave_poll(a.in_flags + idx * a.flag_stride, a.epoch, a.spin_limit, a.err, kSiteRsIn, idx))
-          timed_out = true;
-      }
+      __builtin_amdgcn_s_sleep(2);
     }
     wave_acquire();
   }

@@ -148,10 +148,13 @@ int32_t ag_gemm_tile_rows(ag_gemm_plan_t plan);
  * as `splits` ranges of K by different workgroups; every range stores its
  * fp32 product in the workspace and the last range to finish sums them in
  * range order, C = ((P_0 + P_1) + ...), so the result does not depend on
- * timing or producer order.  The workspace then holds one arrival counter
- * per tile (each returned to zero by its tile's last range) and the
- * partial products; after a run that ended in an error, reset the workspace
- * (ovl_flags_reset) before the next. */
+ * timing or producer order.  When every range runs in the launch's first
+ * round the ranges of a tile wait for each other and each sums a stripe of
+ * the tile's rows; otherwise the last range to finish sums the whole tile.
+ * The workspace then holds two arrival counters per tile (returned to zero
+ * by the tile's last range) and the partial products; after a run that
+ * ended in an error, reset the workspace (ovl_flags_reset) before the
+ * next. */
 int32_t ag_gemm_splits(ag_gemm_plan_t plan);
 
 /* The order in which consumers take rows of output tiles for a given
@@ -300,7 +303,8 @@ ovl_status ovl_flags_reset(int64_t* flags, size_t flag_bytes, void* workspace, s
  * `workspace` (OVL_OK or OVL_ETIMEOUT; the first wait to give up wins).
  * detail (HOST, may be NULL) receives {site, flag index, observed value,
  * awaited value}; sites: 1 AG-GEMM unit flag, 2 AG-GEMM barrier mode,
- * 3 GEMM-RS in flag, 4 dispatch slice flag, 5 GEMM-RS own-tile flag. */
+ * 3 GEMM-RS in flag, 4 dispatch slice flag, 5 GEMM-RS own-tile flag,
+ * 6 AG-GEMM split-K range counter (index = tile). */
 ovl_status ovl_check(const void* workspace, int64_t* detail, hipStream_t stream);
 
 const char* ovl_strerror(ovl_status status);

@@ -188,7 +188,7 @@ def test_split_k_plan(name, tpf, splits):
     if splits > 1:
         m = cfg.ranks * cfg.shard_m
         tiles = -(-m // 128) * -(-cfg.n // 128)
-        counters = -(-tiles * 8 // 256) * 256
+        counters = -(-tiles * 16 // 256) * 256
         assert p.workspace_bytes == 256 + counters + splits * m * cfg.n * 4
     else:
         assert p.workspace_bytes == 256

@@ -108,7 +108,7 @@ def test_ragged_shapes_match_oracle(shape):
 
 def _counters_are_zero(case):
     tiles = -(-case.cfg.m // 128) * -(-case.cfg.n // 128)  # split plans use 128x128 tiles
-    cnt = host(case.ws)[256: 256 + 8 * tiles].view(np.int64)
+    cnt = host(case.ws)[256: 256 + 16 * tiles].view(np.int64)
     return not cnt.any()
 
 
