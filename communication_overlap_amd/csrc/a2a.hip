@@ -20,7 +20,10 @@
 //     m-tile, n-tile) tiles in the same slice order; before the first tile
 //     of a slice they take tickets while its flag is not set (helping the
 //     copy instead of idling), then wait on it, and run the MFMA GEMM of the
-//     expert's rows against that expert's weight.
+//     expert's rows against that expert's weight.  Tiles are expert-major:
+//     an m-tile takes 256 consecutive rows of one expert across slices
+//     (rows gathered through a per-tile row table), so only each expert's
+//     last m-tile is partial.
 #include <algorithm>
 
 #include "device.h"
@@ -34,7 +37,8 @@ namespace {
 constexpr int kA2aMaxRanks = 16;
 constexpr int kA2aMaxExperts = 64;
 constexpr int kChunkRows = 32;
-constexpr int kGbm = 256, kGbn = 128;  // grouped GEMM tile
+constexpr int kGbm = 256, kGbn = 256;  // grouped GEMM tile
+constexpr int kA2aMaxMTiles = 1024;    // m-tiles whose consumer order is sorted in LDS
 constexpr int kA2aXcds = 8;
 
 struct A2aArgs {
@@ -131,40 +135,107 @@ __global__ __launch_bounds__(kThreads) void a2a_layout_kernel(A2aArgs a) {
 // ---------------------------------------------------------------- shared schedule
 
 // Per-run geometry, rebuilt by every workgroup from recv_count.
+//
+// The grouped GEMM runs expert-major: expert e's rows are the rows of its
+// segments in slice order (own slice first), and its m-tiles cut that list
+// into kGbm-row pieces, so a tile may take rows from two slices and only the
+// expert's last m-tile is partial.  M-tiles are taken in the order the data
+// arrives: by the slice position of their last row, then by expert, then by
+// m-tile (n-tiles of one m-tile are consecutive).
 struct Geometry {
   int32_t count[kA2aMaxRanks * kA2aMaxExperts];  // recv_count, by (slice, expert)
   int32_t slice_rows[kA2aMaxRanks];   // by slice
   int32_t chunk_base[kA2aMaxRanks + 1];  // by position in slice order
-  int32_t tile_base[kA2aMaxRanks * kA2aMaxExperts + 1];  // by (order position, expert)
-  int32_t seg_start[kA2aMaxRanks * kA2aMaxExperts];      // by (order position, expert)
+  int32_t seg_start[kA2aMaxRanks * kA2aMaxExperts];  // by (position, expert): segment start in the slice
+  int32_t exp_pre[kA2aMaxExperts * (kA2aMaxRanks + 1)];  // by (expert, position): expert rows before it
+  int32_t mt_base[kA2aMaxExperts + 1];  // m-tiles of experts before e
+  int32_t n_mt;                         // m-tiles in all
+  int32_t mt_order[kA2aMaxMTiles];      // m-tiles in consumer order (e << 20 | mt), if n_mt fits
 };
 
 __device__ inline int slice_at(const A2aArgs& a, int pos) { return (a.rank + pos) % a.ranks; }
 
+// Slice position of expert row r of expert e (rows of earlier positions come first).
+__device__ inline int pos_of_row(const A2aArgs& a, const Geometry* g, int e, int r) {
+  const int32_t* pre = g->exp_pre + e * (kA2aMaxRanks + 1);
+  int pos = 0;
+  while (pos + 1 < a.ranks && uniform(pre[pos + 1]) <= r) ++pos;
+  return pos;
+}
+
 __device__ void build_geometry(const A2aArgs& a, Geometry* g) {
+  __shared__ int32_t s_key[kA2aMaxMTiles];
   for (int i = threadIdx.x; i < a.ranks * a.experts; i += kThreads) g->count[i] = a.recv_count[i];
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int ntn = (int)((a.n + kGbn - 1) / kGbn);
-    int chunks = 0, tiles = 0;
+    int chunks = 0;
     for (int pos = 0; pos < a.ranks; ++pos) {
       const int s = slice_at(a, pos);
       int rows = 0;
       g->chunk_base[pos] = chunks;
       for (int e = 0; e < a.experts; ++e) {
-        const int c = g->count[s * a.experts + e];
         g->seg_start[pos * a.experts + e] = rows;
-        g->tile_base[pos * a.experts + e] = tiles;
-        tiles += ((c + kGbm - 1) / kGbm) * ntn;
-        rows += c;
+        rows += g->count[s * a.experts + e];
       }
       g->slice_rows[s] = rows;
       chunks += (rows + kChunkRows - 1) / kChunkRows;
     }
     g->chunk_base[a.ranks] = chunks;
-    g->tile_base[a.ranks * a.experts] = tiles;
+    int mts = 0;
+    for (int e = 0; e < a.experts; ++e) {
+      int32_t* pre = g->exp_pre + e * (kA2aMaxRanks + 1);
+      int r = 0;
+      for (int pos = 0; pos < a.ranks; ++pos) {
+        pre[pos] = r;
+        r += g->count[slice_at(a, pos) * a.experts + e];
+      }
+      pre[a.ranks] = r;
+      g->mt_base[e] = mts;
+      mts += (r + kGbm - 1) / kGbm;
+    }
+    g->mt_base[a.experts] = mts;
+    g->n_mt = mts;
   }
   __syncthreads();
+  // Consumer order of the m-tiles: a rank sort on (last row's position,
+  // expert, m-tile), identical in every workgroup.
+  const int n_mt = uniform(g->n_mt);
+  if (n_mt <= kA2aMaxMTiles) {
+    for (int q = threadIdx.x; q < n_mt; q += kThreads) {
+      int e = 0;
+      while (g->mt_base[e + 1] <= q) ++e;
+      const int mt = q - g->mt_base[e];
+      const int32_t* pre = g->exp_pre + e * (kA2aMaxRanks + 1);
+      const int last = min((mt + 1) * kGbm, pre[a.ranks]) - 1;
+      int pos = 0;
+      while (pos + 1 < a.ranks && pre[pos + 1] <= last) ++pos;
+      s_key[q] = (pos * kA2aMaxExperts + e) * kA2aMaxMTiles + mt;  // distinct keys
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < n_mt; q += kThreads) {
+      const int32_t k = s_key[q];
+      int rank = 0;
+      for (int o = 0; o < n_mt; ++o) rank += s_key[o] < k;
+      const int e = (k / kA2aMaxMTiles) % kA2aMaxExperts;
+      g->mt_order[rank] = (e << 20) | (k % kA2aMaxMTiles);
+    }
+  }
+  __syncthreads();
+}
+
+// Expert and m-tile of the q-th m-tile in consumer order (expert-major
+// when there are more m-tiles than the order table holds).
+__device__ inline void mtile_at(const A2aArgs& a, const Geometry* g, int q, int* e, int* mt) {
+  if (uniform(g->n_mt) <= kA2aMaxMTiles) {
+    const int v = uniform(g->mt_order[q]);
+    *e = v >> 20;
+    *mt = v & ((1 << 20) - 1);
+    return;
+  }
+  int x = 0;
+  while (uniform(g->mt_base[x + 1]) <= q) ++x;
+  *e = x;
+  *mt = q - uniform(g->mt_base[x]);
 }
 
 // ---------------------------------------------------------------- producer
@@ -319,44 +390,59 @@ __device__ bool wait_slice_helping(const A2aArgs& a, const Geometry* g, int s, i
 template <bool WAIT>
 __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint16_t* lds) {
   __shared__ int sh[2];
+  __shared__ int32_t rowtab[2][kGbm];  // A / y row of each tile row (s * cap + slice row), or -1
   const int ntn = (int)((a.n + kGbn - 1) / kGbn);
-  const int nseg = a.ranks * a.experts;
-  const int total = uniform(g->tile_base[nseg]);
+  const int total = uniform(g->n_mt) * ntn;
   const int Cn = a.consumers;
   const int groups = (Cn % kA2aXcds == 0) ? kA2aXcds : 1;
   const int per = Cn / groups;
   const int x = cidx % groups, q = cidx / groups;
-  int seg = 0;
-  int64_t waited_slice = -1;
+  int waited_hi = -1;  // slice positions [0, waited_hi] are acquired
   bool timed_out = false;
   for (int64_t wv = 0;; ++wv) {
     const int64_t j = wv * Cn + (int64_t)x * per + q;
     if (j >= total) break;
-    while (uniform(g->tile_base[seg + 1]) <= j) ++seg;  // tiles only move forward
-    const int pos = seg / a.experts, e = seg % a.experts;
-    const int s = slice_at(a, pos);
-    const int local = (int)(j - uniform(g->tile_base[seg]));
-    const int mt = local / ntn, nt = local % ntn;
-    const int seg0 = uniform(g->seg_start[seg]);
-    const int seg_end = seg0 + uniform(g->count[s * a.experts + e]);
-
-    if (WAIT && waited_slice != s && !timed_out) {
-      if (!wait_slice_helping(a, g, s, sh)) timed_out = true;
-      waited_slice = s;
+    int e, mt;
+    mtile_at(a, g, (int)(j / ntn), &e, &mt);
+    const int nt = (int)(j % ntn);
+    const int32_t* pre = g->exp_pre + e * (kA2aMaxRanks + 1);
+    const int r0 = mt * kGbm, rows_e = uniform(pre[a.ranks]);
+    const int nrows = min(kGbm, rows_e - r0);
+    const int pos_hi = pos_of_row(a, g, e, r0 + nrows - 1);
+    if (WAIT) {
+      while (waited_hi < pos_hi && !timed_out) {
+        ++waited_hi;
+        if (!wait_slice_helping(a, g, slice_at(a, waited_hi), sh)) timed_out = true;
+      }
     }
+    // Row table of the tile: expert row r0 + i lies in the slice at the
+    // first position whose expert prefix exceeds it.
+    int32_t* tab = rowtab[wv & 1];
+    for (int i = threadIdx.x; i < kGbm; i += kThreads) {
+      int32_t v = -1;
+      if (i < nrows) {
+        const int r = r0 + i;
+        int pos = 0;
+        while (pos + 1 < a.ranks && pre[pos + 1] <= r) ++pos;
+        const int s = slice_at(a, pos);
+        v = s * (int32_t)a.cap + g->seg_start[pos * a.experts + e] + (r - pre[pos]);
+      }
+      tab[i] = v;
+    }
+    __syncthreads();
     Operands op;
-    op.a = a.recv_x + (int64_t)s * a.cap * a.hidden;
+    op.a = a.recv_x;
     op.lda = a.hidden;
-    op.m_valid = seg_end;
+    op.m_valid = (int64_t)a.ranks * a.cap;
+    op.rows = tab;
     op.b = a.w + (int64_t)e * a.hidden * a.n;
     op.ldb = a.n;
     op.n0 = (int64_t)nt * kGbn;
     op.n_valid = a.n;
     op.k = a.hidden;
-    const int64_t m0 = seg0 + (int64_t)mt * kGbm;
     Acc<kGbm, kGbn> acc;
-    gemm_tile<kGbm, kGbn>(acc, op, m0, lds, [](int64_t, int64_t) {});
-    acc_store<kGbm, kGbn>(acc, a.y + (int64_t)s * a.cap * a.n, a.n, m0, op.n0, seg_end, a.n);
+    gemm_tile<kGbm, kGbn, 64, 0, true>(acc, op, 0, lds, [](int64_t, int64_t) {});
+    acc_store_rows<kGbm, kGbn>(acc, a.y, a.n, (int64_t)a.ranks * a.cap, tab, op.n0, a.n);
   }
 }
 
@@ -496,8 +582,9 @@ extern "C" ovl_status a2a_dispatch_grouped_gemm_run(const a2a_desc* d, const voi
   int P = 0;
   if (mode == OVL_MODE_FUSED) {
     // Few dedicated producers: consumers take chunks themselves whenever
-    // the slice they need is behind (measured: 8 producers beat 16 and 32).
-    P = req ? (int)req : kA2aXcds;
+    // the slice they need is behind (measured with 256x256 tiles: 16
+    // producers beat 8 and 64).
+    P = req ? (int)req : 2 * kA2aXcds;
     if (P >= resident) return OVL_EINVAL;
   }
   int64_t Cn = resident - P;

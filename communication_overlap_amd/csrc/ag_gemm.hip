@@ -55,6 +55,10 @@ struct AgArgs {
 };
 
 constexpr int kMaxSplits = 8;
+// Split-K plans run the 128x128 tile with this many LDS stages, and only
+// that configuration carries the split epilogue (the others keep their
+// registers for the main loop).
+constexpr int kSplitStages = 4;
 
 enum { kModeFused = 0, kModeBarrier = 1, kModeGemmOnly = 2 };
 
@@ -291,13 +295,13 @@ __device__ Sched build_schedule(const AgArgs& a, int BM, int* sorted, int* tab, 
 // ---------------------------------------------------------------- consumer
 
 // Tile rows [lo, hi) of a split tile: C = ((P_0 + P_1) + ...) over the
-// partial products in range order, 16 bytes per lane, four row groups of
+// partial products in range order, 16 bytes per lane, two row groups of
 // every partial loaded before the first add.
 template <int BM, int BN>
 __device__ void reduce_splits(const AgArgs& a, int64_t m0, int64_t n0, int64_t lo, int64_t hi) {
   constexpr int VPR = BN / 4;           // 16-byte vectors per tile row
   constexpr int RPP = kThreads / VPR;   // rows per pass
-  constexpr int U = 4;
+  constexpr int U = 2;
   const int64_t rows = min(hi, a.m - m0);
   const int64_t cols = min((int64_t)BN, a.n - n0);
   const int vc = threadIdx.x % VPR, r0 = threadIdx.x / VPR;
@@ -459,7 +463,7 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
 
     Acc<BM, BN> acc;
     gemm_tile<BM, BN, 64, NS>(acc, op, m0_op, lds, before_step);
-    if (a.splits == 1) {
+    if (NS != kSplitStages || a.splits == 1) {
       acc_store<BM, BN>(acc, a.c, a.n, m0, n0, a.m, a.n);
       continue;
     }
@@ -784,7 +788,7 @@ extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, c
   int occ = 0;
   const TileKind kind = tile_kind(p);
   st = kind == kBig ? occupancy<256, 256, 2>(&occ)
-                    : (kind == kSmall ? occupancy<128, 128, 2>(&occ) : occupancy<128, 128, 4>(&occ));
+                    : (kind == kSmall ? occupancy<128, 128, 2>(&occ) : occupancy<128, 128, kSplitStages>(&occ));
   if (st) return st;
   const int64_t resident = (int64_t)std::max(occ, 1) * di.cus;
   int P = 0;
@@ -804,5 +808,5 @@ extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, c
   }
   return kind == kBig ? dispatch_mode<256, 256, 2>(a, mode, stream)
                       : (kind == kSmall ? dispatch_mode<128, 128, 2>(a, mode, stream)
-                                        : dispatch_mode<128, 128, 4>(a, mode, stream));
+                                        : dispatch_mode<128, 128, kSplitStages>(a, mode, stream));
 }

@@ -125,11 +125,14 @@ struct Acc {
 };
 
 // Operand view for one tile: A rows [0, m_valid) at a (row pitch lda),
-// B rows [0, k) at b (row pitch ldb), columns [n0, n_valid) of B.
+// B rows [0, k) at b (row pitch ldb), columns [n0, n_valid) of B.  For a
+// gathered-rows tile (gemm_tile's IND), `rows` is an LDS table of BM
+// entries: tile row i is A row rows[i], or no row (zeros) where rows[i] < 0.
 struct Operands {
   const uint16_t* a;
   int64_t lda;
   int64_t m_valid;  // rows of A that exist, counted from a's row 0
+  const int32_t* rows = nullptr;
   const uint16_t* b;
   int64_t ldb;
   int64_t n0;       // first column of the tile
@@ -137,23 +140,26 @@ struct Operands {
   int64_t k;
 };
 
-// Per-tile, per-lane addressing of the global -> LDS loads.
-template <int BM, int BN, int BK>
+// Per-tile, per-lane addressing of the global -> LDS loads.  IND: A rows
+// come from a row table, so every A instruction keeps its own offset.
+template <int BM, int BN, int BK, bool IND = false>
 struct TileAddr {
   u32x4 ra, rb;
-  uint32_t a_off[2];   // lane offset of A instructions with index parity 0 / 1 at k0 = 0 (bytes)
-  uint32_t a_kc[2];    // lane's K column (elements) for those instructions
-  uint32_t a_qstep;    // bytes between consecutive A instructions
+  // Direct: lane offset of A instructions with index parity 0 / 1 at k0 = 0
+  // (bytes).  IND: lane offset of each A instruction, or kOOB for no row.
+  uint32_t a_off[IND ? TileCfg<BM, BN, BK>::QA : 2];
+  uint32_t a_kc[2];    // lane's K column (elements) for A instructions of index parity 0 / 1
+  uint32_t a_qstep;    // direct: bytes between consecutive A instructions
   uint32_t b_off[2];   // lane offset of B instructions with index parity 0 / 1 at k0 = 0, or kOOB past N
   uint32_t b_qstep;    // bytes between consecutive B instructions
   uint32_t ldb_b;
   int32_t k;
 };
 
-template <int BM, int BN, int BK>
-__device__ inline TileAddr<BM, BN, BK> tile_addr(const Operands& op, int64_t m0) {
+template <int BM, int BN, int BK, bool IND = false>
+__device__ inline TileAddr<BM, BN, BK, IND> tile_addr(const Operands& op, int64_t m0) {
   using C = TileCfg<BM, BN, BK>;
-  TileAddr<BM, BN, BK> t;
+  TileAddr<BM, BN, BK, IND> t;
   const uint32_t l = lane_id();
   const uint32_t w = threadIdx.x >> 6;
   t.ra = make_srd(op.a + m0 * op.lda, (op.m_valid - m0) * op.lda * 2);
@@ -167,9 +173,17 @@ __device__ inline TileAddr<BM, BN, BK> tile_addr(const Operands& op, int64_t m0)
     const uint32_t row = (w * C::QA + par) * C::A_RPI + l / CPR;
     const uint32_t lc = (l % CPR) ^ swz_a<BK>(row);
     t.a_kc[par] = lc * 8;
-    t.a_off[par] = row * lda_b + lc * 16;
+    if constexpr (!IND) t.a_off[par] = row * lda_b + lc * 16;
   }
   t.a_qstep = C::A_RPI * lda_b;
+  if constexpr (IND) {
+#pragma unroll
+    for (int q = 0; q < C::QA; ++q) {
+      const uint32_t row = (w * C::QA + q) * C::A_RPI + l / CPR;
+      const int32_t r = op.rows[row];
+      t.a_off[q] = r >= 0 ? (uint32_t)r * lda_b + (t.a_kc[q & 1] / 8) * 16 : kOOB;
+    }
+  }
   // B: instruction iq = w*QB + q covers k rows iq*B_RPI .. +B_RPI-1; lane l
   // fills row iq*B_RPI + l/LPR, physical chunk l%LPR.
   t.ldb_b = (uint32_t)(op.ldb * 2);
@@ -183,25 +197,32 @@ __device__ inline TileAddr<BM, BN, BK> tile_addr(const Operands& op, int64_t m0)
   return t;
 }
 
+// Buffer offset of A instruction q of the K-step at k0 (kOOB past K, or for
+// a row the table leaves out: kOOB + 2 * k0 is still past every buffer).
+template <int BM, int BN, int BK, bool IND>
+__device__ inline uint32_t a_offset(const TileAddr<BM, BN, BK, IND>& t, int q, int32_t k0) {
+  const int par = q & 1;
+  if (k0 + (int32_t)t.a_kc[par] >= t.k) return kOOB;
+  if constexpr (IND)
+    return t.a_off[q] + (uint32_t)k0 * 2;
+  else
+    return t.a_off[par] + (q & ~1) * t.a_qstep + (uint32_t)k0 * 2;
+}
+
 // Issues this wave's share of the global -> LDS loads of the K-step at k0:
 // the A part and the B part separately, so that each can sit under MFMAs.
 // The swizzle of an instruction's rows depends on the instruction index only
 // through its parity (even QA / QB and row counts), hence the two variants.
-template <int BM, int BN, int BK>
-__device__ inline void stage_issue_a(const TileAddr<BM, BN, BK>& t, uint32_t stage, int32_t k0) {
+template <int BM, int BN, int BK, bool IND>
+__device__ inline void stage_issue_a(const TileAddr<BM, BN, BK, IND>& t, uint32_t stage, int32_t k0) {
   using C = TileCfg<BM, BN, BK>;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int q = 0; q < C::QA; ++q) {
-    const int par = q & 1;
-    const uint32_t off =
-        (k0 + (int32_t)t.a_kc[par] < t.k) ? t.a_off[par] + (q & ~1) * t.a_qstep + (uint32_t)k0 * 2 : kOOB;
-    load_to_lds(t.ra, stage + (w * C::QA + q) * 1024, off);
-  }
+  for (int q = 0; q < C::QA; ++q) load_to_lds(t.ra, stage + (w * C::QA + q) * 1024, a_offset(t, q, k0));
 }
 
-template <int BM, int BN, int BK>
-__device__ inline void stage_issue_b(const TileAddr<BM, BN, BK>& t, uint32_t stage, int32_t k0) {
+template <int BM, int BN, int BK, bool IND>
+__device__ inline void stage_issue_b(const TileAddr<BM, BN, BK, IND>& t, uint32_t stage, int32_t k0) {
   using C = TileCfg<BM, BN, BK>;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t sb = stage + C::A_BYTES;
@@ -215,15 +236,12 @@ __device__ inline void stage_issue_b(const TileAddr<BM, BN, BK>& t, uint32_t sta
 
 // One load instruction of a stage: q < QA is A instruction q, otherwise B
 // instruction q - QA.
-template <int BM, int BN, int BK, int Q>
-__device__ inline void stage_issue_one(const TileAddr<BM, BN, BK>& t, uint32_t stage, int32_t k0) {
+template <int BM, int BN, int BK, bool IND, int Q>
+__device__ inline void stage_issue_one(const TileAddr<BM, BN, BK, IND>& t, uint32_t stage, int32_t k0) {
   using C = TileCfg<BM, BN, BK>;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if constexpr (Q < C::QA) {
-    constexpr int par = Q & 1;
-    const uint32_t off =
-        (k0 + (int32_t)t.a_kc[par] < t.k) ? t.a_off[par] + (Q & ~1) * t.a_qstep + (uint32_t)k0 * 2 : kOOB;
-    load_to_lds(t.ra, stage + (w * C::QA + Q) * 1024, off);
+    load_to_lds(t.ra, stage + (w * C::QA + Q) * 1024, a_offset(t, Q, k0));
   } else {
     constexpr int q = Q - C::QA, par = q & 1;
     load_to_lds(t.rb, stage + C::A_BYTES + (w * C::QB + q) * 1024,
@@ -233,15 +251,15 @@ __device__ inline void stage_issue_one(const TileAddr<BM, BN, BK>& t, uint32_t s
 
 // The loads of one stage, to be spread over the MFMA groups of the step
 // before (on == false: nothing to load).
-template <int BM, int BN, int BK>
+template <int BM, int BN, int BK, bool IND>
 struct Prefetch {
-  const TileAddr<BM, BN, BK>* t;
+  const TileAddr<BM, BN, BK, IND>* t;
   uint32_t slot;
   int32_t k0;
   bool on;
   template <int Q>
   __device__ inline void issue() const {
-    if (on) stage_issue_one<BM, BN, BK, Q>(*t, slot, k0);
+    if (on) stage_issue_one<BM, BN, BK, IND, Q>(*t, slot, k0);
   }
 };
 
@@ -457,7 +475,7 @@ __device__ inline void acc_zero(Acc<BM, BN>& acc) {
 // calls it, before a workgroup barrier that precedes the first load of that
 // step (so a wave that acquires there orders the whole workgroup's loads).
 // Ends with a workgroup barrier, so LDS may be reused at once.
-template <int BM, int BN, int BK = 64, int NSTAGES = 0, class BeforeStep>
+template <int BM, int BN, int BK = 64, int NSTAGES = 0, bool IND = false, class BeforeStep>
 __device__ inline void gemm_tile(Acc<BM, BN>& acc, const Operands& op, int64_t m0, uint16_t* lds,
                                  BeforeStep before_step) {
   using C = TileCfg<BM, BN, BK, NSTAGES>;
@@ -465,7 +483,7 @@ __device__ inline void gemm_tile(Acc<BM, BN>& acc, const Operands& op, int64_t m
   static_assert(NS - 2 <= 2, "wait_stage_loads covers up to two pending stages");
   uint8_t* l8 = reinterpret_cast<uint8_t*>(lds);
   acc_zero(acc);
-  const TileAddr<BM, BN, BK> ta = tile_addr<BM, BN, BK>(op, m0);
+  const TileAddr<BM, BN, BK, IND> ta = tile_addr<BM, BN, BK, IND>(op, m0);
   const FragAddr<BM, BN, BK> fa = frag_addr<BM, BN, BK>();
   const int32_t steps = (int32_t)((op.k + BK - 1) / BK);
   const uint32_t lbase = lds_addr(l8);
@@ -482,7 +500,7 @@ __device__ inline void gemm_tile(Acc<BM, BN>& acc, const Operands& op, int64_t m
   __syncthreads();
   for (int32_t s = 0; s < steps; ++s) {
     const int32_t nxt = s + NS - 1;  // stage issued during this step
-    const Prefetch<BM, BN, BK> pf{&ta, lbase + (uint32_t)(nxt % NS) * C::STAGE_BYTES, nxt * BK, nxt < steps};
+    const Prefetch<BM, BN, BK, IND> pf{&ta, lbase + (uint32_t)(nxt % NS) * C::STAGE_BYTES, nxt * BK, nxt < steps};
     stage_compute<BM, BN, BK>(acc, l8 + (s % NS) * C::STAGE_BYTES, fa, pf);
     if (s + NS < steps) step_cols(s + NS);
     // Stage s+1 must have landed; the stages issued after it may stay in flight.
@@ -548,6 +566,35 @@ __device__ inline void acc_store(const Acc<BM, BN>& acc, float* c, int64_t ldc, 
                                  int64_t m_valid, int64_t n_valid) {
   const OutTile o = out_tile(c, ldc, m0, n0, m_valid, n_valid);
   acc_foreach(acc, [&](int row, int col, float v) { bstoref<AUX>(o.r, out_off(o, row, col), v); });
+}
+
+// Stores the tile through a row table: tile row i goes to row rows[i] of
+// fp32 C (row pitch ldc, c_rows rows; nothing where rows[i] < 0), columns
+// n0 + col clipped to n_valid.
+template <int BM, int BN>
+__device__ inline void acc_store_rows(const Acc<BM, BN>& acc, float* c, int64_t ldc, int64_t c_rows,
+                                      const int32_t* rows, int64_t n0, int64_t n_valid) {
+  using C = TileCfg<BM, BN>;
+  const rsrc_t r = make_rsrc(c, c_rows * ldc * 4);
+  const uint32_t ldc_b = opaque((uint32_t)(ldc * 4));
+  const int64_t n_left = n_valid - n0;
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int wm = (wave >> 1) * (BM / 2);
+  const int wn = (wave & 1) * (BN / 2);
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = wm + fm * 32 + (i & 3) + 8 * (i >> 2) + 4 * (lane >> 5);
+      const int32_t cr = rows[row];
+      const uint32_t rb = cr >= 0 ? (uint32_t)cr * ldc_b + (uint32_t)n0 * 4 : kOOB;
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const int col = wn + fn * 32 + (lane & 31);
+        bstoref(r, (rb != kOOB && col < n_left) ? rb + (uint32_t)col * 4 : kOOB, acc.v[fm][fn][i]);
+      }
+    }
 }
 
 }  // namespace ovl
