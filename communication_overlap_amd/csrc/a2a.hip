@@ -16,14 +16,14 @@
 //     then arrives on its slice's counter, and the workgroup that completes
 //     a slice publishes the slice flag (signal ADD for the arrivals, signal
 //     SET for the flag).  Producer workgroups take tickets until none is
-//     left.  Consumer workgroups walk a flattened list of (slice, expert,
-//     m-tile, n-tile) tiles in the same slice order; before the first tile
-//     of a slice they take tickets while its flag is not set (helping the
-//     copy instead of idling), then wait on it, and run the MFMA GEMM of the
-//     expert's rows against that expert's weight.  Tiles are expert-major:
-//     an m-tile takes 256 consecutive rows of one expert across slices
-//     (rows gathered through a per-tile row table), so only each expert's
-//     last m-tile is partial.
+//     left.  Consumer workgroups run 256x256 tiles of the grouped GEMM,
+//     expert-major: an m-tile takes 256 consecutive rows of one expert's
+//     rows (its segments in slice order, gathered through a per-tile row
+//     table), so only each expert's last m-tile is partial; m-tiles go in
+//     the order their last slice arrives.  Before a tile whose slices are
+//     not all acquired, a consumer takes tickets while the flag it waits
+//     for is not set (helping the copy instead of idling), then waits, and
+//     runs the MFMA GEMM of the rows against that expert's weight.
 #include <algorithm>
 
 #include "device.h"
