@@ -352,14 +352,14 @@ __global__ __launch_bounds__(kThreads) void a2a_produce_kernel(A2aArgs a) {
 
 // ---------------------------------------------------------------- consumer
 
-// Waits for slice s; while its flag is not set and chunks of slices up to
-// s are left, the workgroup copies chunks itself (the first consumers thus
-// copy the first slice together, and no consumer idles while the copy it
-// waits for can be sped up).  Ends with the acquire done by wave 0 and a
-// workgroup barrier.  Returns false on timeout.
+// Waits for slice s; while its flag is not set and chunks are left, the
+// workgroup copies chunks itself, rechecking the flag after each (the first
+// consumers thus copy the first slices together, and no consumer idles
+// while copying work remains: measured better than helping only with the
+// chunks up to s).  Ends with the acquire done by wave 0 and a workgroup
+// barrier.  Returns false on timeout.
 __device__ bool wait_slice_helping(const A2aArgs& a, const Geometry* g, int s, int* sh) {
   const int total = uniform(g->chunk_base[a.ranks]);
-  const int limit = uniform(g->chunk_base[(s - a.rank + a.ranks) % a.ranks + 1]);  // end of s's chunks
   const int64_t* flag = a.flags + (int64_t)s * a.flag_stride;
   bool ok = true;
   for (;;) {
@@ -367,7 +367,7 @@ __device__ bool wait_slice_helping(const A2aArgs& a, const Geometry* g, int s, i
       int st = 2;  // 0 ready, 1 help, 2 wait
       if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= a.epoch)
         st = 0;
-      else if (__hip_atomic_load(a.ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < limit)
+      else if (__hip_atomic_load(a.ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < total)
         st = 1;
       sh[1] = st;
     }
