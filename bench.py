@@ -209,7 +209,19 @@ def main():
 
     extra = {}
     if not args.no_extra:
+        # Flag batching on the same workload: one flag per 256-column K-batch
+        # (the headline setting), per 4 or 16 K-tiles, or per whole panel.
+        batching = {"1": round(fused["median_us"], 1)}
+        for tpf in (4, 16, 0):
+            log(f"[bench] flag batching: tiles_per_flag={tpf}")
+            agb = AgBench(cfg, tiles_per_flag=tpf)
+            agb.run()
+            batching[str(tpf)] = round(timed_reps(lambda: agb.run(ovl.MODE_FUSED), args.reps, flush)["median_us"], 1)
+            agb.check()
+            del agb
         extra = side_workloads(args.reps, flush)
+        extra["ag_flag_batching_fused_us"] = {"by_tiles_per_flag": batching,
+                                              "note": "0 = one flag per 256-row panel (all of K)"}
 
     out = {
         "metric": METRIC,

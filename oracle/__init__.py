@@ -18,3 +18,4 @@ from .bf16 import bf16_to_f64, bf16_to_f32  # noqa: F401
 from .ag_gemm import all_gather, ag_gemm, gemm, gemm_entries, ag_flag_units, expected_flags  # noqa: F401
 from .gemm_rs import gemm_rs, rs_expected_flags  # noqa: F401
 from .dispatch import dispatch_layout, dispatch, grouped_gemm, grouped_gemm_rows  # noqa: F401
+from .combine import combine, combine_positions  # noqa: F401

@@ -17,8 +17,9 @@ from .gen import (  # noqa: F401
     small_int_f32,
     permutation,
     zipf_top2_routing,
+    zipf_topk_gates,
 )
 from .configs import (  # noqa: F401
     CONFIGS, AgGemmCfg, GemmRsCfg, DispatchCfg,
-    ag_inputs, rs_inputs, dispatch_inputs, producer_order,
+    ag_inputs, rs_inputs, dispatch_inputs, combine_inputs, producer_order,
 )

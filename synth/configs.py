@@ -12,7 +12,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .gen import normal_bf16, normal_f32, small_int_bf16, small_int_f32, permutation, stream_key, zipf_top2_routing
+from .gen import (normal_bf16, normal_f32, small_int_bf16, small_int_f32, permutation, stream_key,
+                  zipf_top2_routing, zipf_topk_gates)
 
 
 @dataclass(frozen=True)
@@ -179,3 +180,24 @@ def dispatch_inputs(cfg: DispatchCfg, kind: str = "normal"):
         w = np.stack([normal_bf16(cfg.seed, 6, e, (H, N), cfg.w_sigma) for e in range(cfg.experts_per_rank)])
     topk = [zipf_top2_routing(cfg.seed, s, T, cfg.num_experts, cfg.topk, cfg.zipf) for s in range(R)]
     return x, topk, w
+
+
+# ---------------------------------------------------------------- combine inputs
+
+def combine_inputs(cfg: DispatchCfg, kind: str = "normal"):
+    """(gates, ret_in) for the combine at rank cfg.rank: gates float32
+    [tokens][topk] of this rank's own tokens (routing of source cfg.rank),
+    and for every peer q != rank the rows q returns for those tokens, float32
+    [cap][n] (None at the own rank): what q's experts computed for the
+    tokens it received from this rank, in q's slice order."""
+    R, T, N = cfg.ranks, cfg.tokens, cfg.n
+    cap = cfg.cap
+    gates = zipf_topk_gates(cfg.seed, cfg.rank, T, cfg.num_experts, cfg.topk, cfg.zipf)
+    if kind == "smallint":
+        # dyadic gates (1..4)/4 and small integers: every product and sum exact in fp32
+        gates = (small_int_f32(cfg.seed, 9, cfg.rank, (T, cfg.topk), 1, 4) / 4).astype(np.float32)
+        ret = [None if q == cfg.rank else small_int_f32(cfg.seed, 8, q, (cap, N), -16, 16) for q in range(R)]
+    else:
+        ret = [None if q == cfg.rank else normal_f32(stream_key(cfg.seed, 8, q), cap * N, 1.0).reshape(cap, N)
+               for q in range(R)]
+    return gates, ret

@@ -154,3 +154,17 @@ def zipf_top2_routing(seed: int, source: int, tokens: int, num_experts: int = 64
     keys = logp[None, :] - np.log(-np.log(u))
     order = np.argsort(-keys, axis=1, kind="stable")
     return np.ascontiguousarray(order[:, :topk].astype(np.int32))
+
+
+def zipf_topk_gates(seed: int, source: int, tokens: int, num_experts: int = 64, topk: int = 2,
+                    exponent: float = 1.1) -> np.ndarray:
+    """Gate weights of the routing `zipf_top2_routing` draws, float32
+    [tokens][topk]: the chosen experts' keys (ln p_e + G, the same draws)
+    taken as router logits and normalised by a softmax over the top-k."""
+    logp = -exponent * np.log(np.arange(1, num_experts + 1, dtype=np.float64))
+    u = uniform(stream_key(seed, 5, source), 0, tokens * num_experts).reshape(tokens, num_experts)
+    keys = logp[None, :] - np.log(-np.log(u))
+    order = np.argsort(-keys, axis=1, kind="stable")[:, :topk]
+    top = np.take_along_axis(keys, order, axis=1)
+    e = np.exp(top - top.max(axis=1, keepdims=True))
+    return np.ascontiguousarray((e / e.sum(axis=1, keepdims=True)).astype(np.float32))
