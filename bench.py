@@ -353,7 +353,45 @@ def side_workloads(reps, flush):
                      "fused_pct_of_bf16_peak": 100 * flops / (t["median_us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
                      "fused_over_dispatch_plus_gemm": t["median_us"] / (disp["median_us"] + g["median_us"]),
                      "fused_over_gemm_only": t["median_us"] / g["median_us"]}
-    del recv_x, y
+    # MoE combine at the same rank: reverse puts of y to the 7 peers, then the
+    # gate-weighted sum of this rank's tokens (peers' returned rows pre-resident).
+    log("[bench] side a2a combine")
+    gates, ret_in = synth.combine_inputs(cfg)
+    d_gates = dev(gates)
+    d_ret_in = [None if q == cfg.rank else dev(ret_in[q]) for q in range(R)]
+    del ret_in
+    ret_out = [None if q == cfg.rank else torch.zeros(cap, cfg.n, dtype=torch.float32, device="cuda")
+               for q in range(R)]
+    out = torch.zeros(cfg.tokens, cfg.n, dtype=torch.float32, device="cuda")
+    cfb = ovl.a2a_combine_flags_bytes(desc)
+    c_out_flags = torch.zeros(cfb, dtype=torch.uint8, device="cuda")
+    c_in_flags = torch.zeros(cfb, dtype=torch.uint8, device="cuda")
+    c_in_flags.view(torch.int64).fill_(1 << 40)
+    c_ws = torch.zeros(ovl.a2a_combine_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    ovl.ovl_flags_reset(c_out_flags, cfb, c_ws, c_ws.numel())
+    cep = [0]
+
+    def comb(mode=0):
+        cep[0] += 1
+        ovl.a2a_combine_run(desc, y, recv_count, ret_out, d_ret_in, d_topk[cfg.rank], d_gates, out, c_out_flags,
+                            c_in_flags, c_ws, cep[0], mode=mode)
+
+    comb()
+    t = timed_reps(comb, reps, flush)
+    put = timed_reps(lambda: comb(ovl.MODE_COPY_ONLY), reps, flush)
+    sm = timed_reps(lambda: comb(ovl.MODE_GEMM_ONLY), reps, flush)
+    ovl.ovl_check(c_ws)
+    rc = recv_count.cpu().numpy()
+    rows_back = int(sum(rc[s].sum() for s in range(R) if s != cfg.rank))
+    put_bytes = 2 * rows_back * cfg.n * 4
+    sum_bytes = cfg.tokens * (cfg.topk + 1) * cfg.n * 4
+    res["a2a_combine_r8_t4096_n1408"] = {
+        "fused_us": t, "reverse_put_only_us": put, "sum_only_us": sm, "rows_sent_back": rows_back,
+        "bytes": put_bytes + sum_bytes,
+        "GBps": (put_bytes + sum_bytes) / (t["median_us"] * 1e-6) / 1e9,
+        "pct_of_hbm_peak": 100 * (put_bytes + sum_bytes) / (t["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+        "fused_over_put_plus_sum": t["median_us"] / (put["median_us"] + sm["median_us"])}
+    del recv_x, y, ret_out, d_ret_in, out
 
     # Plain copy, for the HBM reference point.
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")

@@ -121,9 +121,17 @@ __global__ __launch_bounds__(kThreads) void a2a_layout_kernel(A2aArgs a) {
   block_excl_scan(lt, &base_total, smem);
   int pos = base_total + block_excl_scan(eq, &cnt_total, smem);
   if (eq) {
+    // Loads in batches again: the stores below may alias them, so a plain
+    // loop would wait out one load per entry.
     int32_t* dst = a.recv_src + (int64_t)s * a.cap;
-    for (int64_t i = i0; i < i1; ++i)
-      if (idx[i] - e_lo == e) dst[pos++] = (int32_t)(i / a.topk_n);
+    for (int64_t i = i0; i < i1; i += B) {
+      int32_t v[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) v[q] = i + q < i1 ? idx[i + q] : -1;
+#pragma unroll
+      for (int q = 0; q < B; ++q)
+        if (v[q] - e_lo == e) dst[pos++] = (int32_t)((i + q) / a.topk_n);
+    }
   }
   if (threadIdx.x == 0) {
     a.recv_count[s * a.experts + e] = cnt_total;

@@ -1,0 +1,385 @@
+// MoE combine: the reverse all-to-all of this rank's expert outputs, then
+// the gate-weighted sum back in token order (the Aboleth README's compiled
+// MoE dispatch *and combine*; the reverse all-to-all for expert-parallel MoE
+// of the Triton distributed tutorials).  The same per-slice signal
+// discipline as the dispatch, in reverse:
+//  1. Layout, one workgroup per (rank q, local expert e) over this rank's
+//     own routing: the row of every (token, choice) in q's slice of this
+//     rank's tokens (ordered by (local expert, token), as q's dispatch
+//     placed them).  It also zeroes this run's slice counters.
+//  2. Fused, two workgroups per compute unit.  First the reverse puts, one
+//     peer slice at a time (positions rank+1, rank+2, ...): y[s] (s != rank,
+//     the rows this rank computed for source s, already in slice order) is
+//     copied into ret_out[s], every workgroup taking a grid-strided share;
+//     the last workgroup to finish slice s sets out_flags[s] (put + signal).
+//     Then this rank's tokens, one per wave: once the flags of the peers'
+//     returned rows are set, out[t] = sum over choices k (ascending) of
+//     gates[t][k] * Y(t, k), Y from y[rank] for local experts or from the
+//     returning peer's ret_in rows.
+#include <algorithm>
+
+#include "device.h"
+#include "host.h"
+
+namespace ovl {
+
+namespace {
+
+constexpr int kCbMaxRanks = 16;
+constexpr int kCbBlocksPerCu = 2;
+
+struct CombineArgs {
+  float* ret_out[kCbMaxRanks];
+  const float* ret_in[kCbMaxRanks];
+  const float* y;
+  const int32_t* recv_count;
+  const int32_t* topk;
+  const float* gates;
+  float* out;
+  int64_t* out_flags;
+  const int64_t* in_flags;
+  int32_t* pos;       // [tokens][topk] row of each choice in its owner's slice (workspace)
+  int64_t* counters;  // [R] workgroups done with each slice's put (workspace)
+  ErrRec* err;
+  int64_t tokens, n, cap;
+  int64_t flag_stride;  // int64 slots
+  int64_t epoch;
+  uint64_t spin_limit;
+  int32_t ranks, rank, topk_n, experts;
+  int32_t do_put, do_sum, wait_in;
+};
+
+__device__ inline int wave_incl_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+__device__ inline int block_excl_scan(int v, int* total, int* smem) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) smem[wave] = incl;
+  __syncthreads();
+  int before = 0, sum = 0;
+  for (int i = 0; i < kThreads / 64; ++i) {
+    const int wsum = smem[i];
+    if (i < wave) before += wsum;
+    sum += wsum;
+  }
+  __syncthreads();
+  *total = sum;
+  return before + incl - v;
+}
+
+// Workgroup (q, e): the choices of this rank's tokens that pick global
+// expert q*E + e take rows base + 0, 1, ... of q's slice, base = the count
+// of choices picking q's experts below e; order (token, choice).
+__global__ __launch_bounds__(kThreads) void combine_layout_kernel(CombineArgs a) {
+  __shared__ int smem[8];
+  const int q = blockIdx.x / a.experts, e = blockIdx.x % a.experts;
+  const int e_lo = q * a.experts;
+  const int64_t T = a.tokens;
+  const int64_t per = (T + kThreads - 1) / kThreads;
+  const int64_t i0 = min(T, per * threadIdx.x) * a.topk_n, i1 = min(T, per * (threadIdx.x + 1)) * a.topk_n;
+  constexpr int B = 32;
+  int lt = 0, eq = 0;
+  for (int64_t i = i0; i < i1; i += B) {
+    int32_t v[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) v[j] = i + j < i1 ? a.topk[i + j] : -1;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int ex = v[j] - e_lo;
+      lt += (ex >= 0) & (ex < e);
+      eq += ex == e;
+    }
+  }
+  int base_total, cnt_total;
+  block_excl_scan(lt, &base_total, smem);
+  int p = base_total + block_excl_scan(eq, &cnt_total, smem);
+  if (eq)
+    for (int64_t i = i0; i < i1; i += B) {  // loads batched again: the stores may alias them
+      int32_t v[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j) v[j] = i + j < i1 ? a.topk[i + j] : -1;
+#pragma unroll
+      for (int j = 0; j < B; ++j)
+        if (v[j] - e_lo == e) a.pos[i + j] = p++;
+    }
+  if (blockIdx.x == 0 && threadIdx.x < a.ranks) a.counters[threadIdx.x] = 0;
+}
+
+// Rows this rank sends back to each peer slice (rebuilt by every workgroup).
+struct CbGeom {
+  int32_t rows[kCbMaxRanks];
+};
+
+__device__ inline int cb_slice_at(const CombineArgs& a, int pos) { return (a.rank + 1 + pos) % a.ranks; }
+
+__device__ void cb_geometry(const CombineArgs& a, CbGeom* g) {
+  if (threadIdx.x < kCbMaxRanks) {
+    const int s = threadIdx.x;
+    int r = 0;
+    if (s < a.ranks && s != a.rank && a.tokens > 0)
+      for (int e = 0; e < a.experts; ++e) r += a.recv_count[s * a.experts + e];
+    g->rows[s] = (int)min((int64_t)r, a.cap);  // a slice holds at most cap rows
+  }
+  __syncthreads();
+}
+
+// Reverse put of slice s: its rows of y[s] are contiguous, as are their
+// places in ret_out[s].  Every workgroup copies a grid-strided share of the
+// slice's 8-byte words, eight in flight per lane, with agent-scope stores,
+// and then arrives; the last of them to arrive sets out_flags[s].
+__device__ void cb_put_slice(const CombineArgs& a, int s, int64_t rows) {
+  const int64_t words = rows * a.n / 2;
+  const uint64_t* src = reinterpret_cast<const uint64_t*>(a.y + (int64_t)s * a.cap * a.n);
+  uint64_t* dst = reinterpret_cast<uint64_t*>(a.ret_out[s]);
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  constexpr int U = 8;
+  for (; i + (U - 1) * stride < words; i += U * stride) {
+    uint64_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) st8_agent(dst + i + u * stride, v[u]);
+  }
+  for (; i < words; i += stride) st8_agent(dst + i, __builtin_nontemporal_load(src + i));
+  const int64_t old = wg_arrive_agent(a.counters + s);
+  if (threadIdx.x == 0 && old + 1 == (int64_t)gridDim.x) {
+    wave_acquire();
+    __hip_atomic_store(a.out_flags + (int64_t)s * a.flag_stride, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();  // separates this thread-0 branch from the next slice's
+}
+
+// Tokens t0 + j * stride (j < J), by one wave.  The lanes first load every
+// (token, choice)'s expert id, row and gate at once (lane j * KMAX + k), the
+// wave reads them back as scalars; then a lane sums 16-byte vectors lane,
+// lane + 64, ... of each output row, V at a time, all J tokens' and all
+// choices' loads issued before the first add.  KMAX bounds topk; J * KMAX * V
+// = 16 keeps the loads in flight at 64 registers.
+template <int KMAX, int J>
+__device__ void cb_sum_tokens(const CombineArgs& a, int64_t t0, int64_t stride) {
+  constexpr int V = 16 / (KMAX * J);
+  static_assert(V >= 1 && J * KMAX <= 64, "loads in flight per lane");
+  const int lane = lane_id();
+  const int64_t vpr = a.n / 4;
+  // Metadata, one (token, choice) per lane.
+  int32_t my_e = -1;
+  int32_t my_p = 0;
+  float my_g = 0.f;
+  {
+    const int j = lane / KMAX, k = lane % KMAX;
+    const int64_t t = t0 + j * stride;
+    if (j < J && k < a.topk_n && t < a.tokens) {
+      my_e = a.topk[t * a.topk_n + k];
+      my_p = a.pos[t * a.topk_n + k];
+      my_g = a.gates[t * a.topk_n + k];
+    }
+  }
+  const f32x4* rowp[J][KMAX];
+  float gk[J][KMAX];
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const int src = j * KMAX + k;
+      const int32_t e = __builtin_amdgcn_readlane(my_e, src);
+      const int64_t p = __builtin_amdgcn_readlane(my_p, src);
+      gk[j][k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_g), src));
+      rowp[j][k] = nullptr;
+      if (e < 0 || e >= a.ranks * a.experts) continue;  // not an expert (or no token): contributes nothing
+      const int q = e / a.experts;
+      rowp[j][k] = reinterpret_cast<const f32x4*>(q == a.rank ? a.y + ((int64_t)a.rank * a.cap + p) * a.n
+                                                               : a.ret_in[q] + p * a.n);
+    }
+  for (int64_t v0 = lane; v0 < vpr; v0 += 64 * V) {
+    f32x4 x[J][KMAX][V];
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k)
+#pragma unroll
+        for (int u = 0; u < V; ++u)
+          if (rowp[j][k] && v0 + 64 * u < vpr) x[j][k][u] = __builtin_nontemporal_load(rowp[j][k] + v0 + 64 * u);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int64_t t = t0 + j * stride;
+      if (t >= a.tokens) continue;
+      f32x4* o = reinterpret_cast<f32x4*>(a.out + t * a.n);
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        if (v0 + 64 * u >= vpr) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+          if (rowp[j][k]) acc += gk[j][k] * x[j][k][u];
+        o[v0 + 64 * u] = acc;
+      }
+    }
+  }
+}
+
+// The peers' returned rows: every in flag, lanes in parallel; wave 0 of
+// each workgroup polls, the workgroup continues after its acquire.
+__device__ void cb_wait_in(const CombineArgs& a) {
+  if (threadIdx.x < 64) {
+    for (uint64_t polls = 0;; ++polls) {
+      bool missing = false;
+      for (int q = lane_id(); q < a.ranks; q += 64)
+        if (q != a.rank)
+          missing |= __hip_atomic_load(a.in_flags + (int64_t)q * a.flag_stride, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT) < a.epoch;
+      if (!__ballot(missing)) break;
+      if (polls >= a.spin_limit) {
+        for (int q = 0; q < a.ranks; ++q)
+          if (q != a.rank && !wave_poll(a.in_flags + (int64_t)q * a.flag_stride, a.epoch, 0, a.err, kSiteCbIn, q))
+            break;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    wave_acquire();
+  }
+  __syncthreads();
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
+  __shared__ CbGeom g;
+  cb_geometry(a, &g);
+  if (a.do_put) {
+    // Peers this rank sends nothing back to are complete at once.
+    if (blockIdx.x == 0 && threadIdx.x < a.ranks && threadIdx.x != a.rank && g.rows[threadIdx.x] == 0)
+      __hip_atomic_store(a.out_flags + (int64_t)threadIdx.x * a.flag_stride, a.epoch, __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    // Slices in position order rank+1, rank+2, ...: each is complete (and
+    // signalled) before the next begins, so peers can start on it early.
+    for (int pos = 0; pos + 1 < a.ranks; ++pos) {
+      const int s = cb_slice_at(a, pos);
+      const int rows = uniform(g.rows[s]);
+      if (rows) cb_put_slice(a, s, rows);
+    }
+  }
+  if (!a.do_sum) return;
+  if (a.wait_in) cb_wait_in(a);
+  // J tokens per wave at a time, waves grid-strided over the tokens.
+  constexpr int J = KMAX <= 2 ? 2 : 1;
+  const int64_t waves = (int64_t)gridDim.x * (kThreads / 64);
+  for (int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); t < a.tokens; t += waves * J)
+    cb_sum_tokens<KMAX, J>(a, t, waves);
+}
+
+}  // namespace
+
+}  // namespace ovl
+
+using namespace ovl;
+
+extern "C" size_t a2a_combine_flags_bytes(const a2a_desc* d) {
+  if (!d || d->ranks < 1 || d->flag_stride < 8) return 0;
+  return (size_t)d->ranks * (size_t)d->flag_stride;
+}
+
+// Error record, then the R slice counters (256 bytes in all), then the
+// choice rows int32 [tokens][topk].
+extern "C" size_t a2a_combine_workspace_bytes(const a2a_desc* d) {
+  if (!d || d->ranks < 1 || d->tokens < 0 || d->topk < 1) return 0;
+  return 256 + aligned_up(4 * (size_t)d->tokens * (size_t)d->topk, 256);
+}
+
+extern "C" ovl_status a2a_combine_run(const a2a_desc* d, const float* y, const int32_t* recv_count,
+                                      float* const* ret_out, const float* const* ret_in,
+                                      const int32_t* topk_idx, const float* gates, float* out,
+                                      int64_t* out_flags, const int64_t* in_flags, void* workspace,
+                                      int64_t epoch, const ovl_opts* opts, hipStream_t stream) {
+  if (!d || !workspace) return OVL_EINVAL;
+  if (d->ranks < 1 || d->rank < 0 || d->rank >= d->ranks) return OVL_EINVAL;
+  if (d->ranks > kCbMaxRanks || d->experts_per_rank > 64) return OVL_EUNSUPPORTED;
+  if (d->experts_per_rank < 1 || d->topk < 1 || d->topk > 8 || d->tokens < 0 ||
+      d->num_experts != d->ranks * d->experts_per_rank)
+    return OVL_ESHAPE;
+  if (d->n < 8 || d->n % 8 || d->flag_stride < 8 || d->flag_stride % 8) return OVL_EALIGN;
+  const int64_t cap = d->tokens * std::min<int64_t>(d->topk, d->experts_per_rank);
+  if (d->tokens > (1 << 20) || d->n > (1 << 20) || (int64_t)d->ranks * cap * d->n * 4 > (1ll << 30))
+    return OVL_EUNSUPPORTED;
+  const uint32_t mode = opts ? opts->mode : OVL_MODE_FUSED;
+  if (mode != OVL_MODE_FUSED && mode != OVL_MODE_COPY_ONLY && mode != OVL_MODE_GEMM_ONLY) return OVL_EINVAL;
+  const bool put = mode != OVL_MODE_GEMM_ONLY, sum = mode != OVL_MODE_COPY_ONLY;
+  const bool empty = d->tokens == 0;
+  const bool peers = d->ranks > 1;
+  if (!recv_count) return OVL_EINVAL;
+  if (put && peers && !out_flags) return OVL_EINVAL;
+  if (sum && mode == OVL_MODE_FUSED && peers && !in_flags) return OVL_EINVAL;
+  if (!empty) {
+    if (!y) return OVL_EINVAL;
+    if (sum && (!topk_idx || !gates || !out)) return OVL_EINVAL;
+    if (!aligned16(y) || (sum && !aligned16(out)) || (sum && (reinterpret_cast<uintptr_t>(topk_idx) & 3u)) ||
+        (sum && (reinterpret_cast<uintptr_t>(gates) & 3u)))
+      return OVL_EALIGN;
+    for (int q = 0; q < d->ranks; ++q) {
+      if (q == d->rank) continue;
+      if ((put && (!ret_out || !ret_out[q])) || (sum && (!ret_in || !ret_in[q]))) return OVL_EINVAL;
+      if ((put && !aligned16(ret_out[q])) || (sum && !aligned16(ret_in[q]))) return OVL_EALIGN;
+    }
+  }
+  if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(recv_count) & 3u) ||
+      (out_flags && (reinterpret_cast<uintptr_t>(out_flags) & 7u)) ||
+      (in_flags && (reinterpret_cast<uintptr_t>(in_flags) & 7u)))
+    return OVL_EALIGN;
+  DeviceInfo di;
+  ovl_status st = current_device_info(&di);
+  if (st) return st;
+
+  CombineArgs a = {};
+  for (int q = 0; q < d->ranks; ++q) {
+    if (q == d->rank || empty) continue;
+    if (put) a.ret_out[q] = ret_out[q];
+    if (sum) a.ret_in[q] = ret_in[q];
+  }
+  a.y = y;
+  a.recv_count = recv_count;
+  a.topk = topk_idx;
+  a.gates = gates;
+  a.out = out;
+  a.out_flags = out_flags;
+  a.in_flags = in_flags;
+  a.err = static_cast<ErrRec*>(workspace);
+  a.counters = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(workspace) + OVL_ERROR_RECORD_BYTES);
+  a.pos = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + 256);
+  a.tokens = d->tokens;
+  a.n = d->n;
+  a.cap = cap;
+  a.flag_stride = d->flag_stride / 8;
+  a.epoch = epoch;
+  a.spin_limit = spin_limit_of(opts);
+  a.ranks = d->ranks;
+  a.rank = d->rank;
+  a.topk_n = d->topk;
+  a.experts = d->experts_per_rank;
+  a.do_put = put && peers;  // with no tokens no slice has rows, and every out flag is set at once
+  a.do_sum = sum && !empty;
+  a.wait_in = mode == OVL_MODE_FUSED && peers;
+
+  if (put && peers) {
+    st = epoch_accept(out_flags, epoch);
+    if (st) return st;
+  }
+  hipLaunchKernelGGL(combine_layout_kernel, dim3(d->ranks * d->experts_per_rank), dim3(kThreads), 0, stream, a);
+  OVL_HIP_TRY(hipGetLastError());
+  // Two workgroups per compute unit (the put's grid stride and the final
+  // arrival count both use this number).
+  const int blocks = kCbBlocksPerCu * di.cus;
+  if (d->topk <= 2)
+    hipLaunchKernelGGL(combine_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<8>, dim3(blocks), dim3(kThreads), 0, stream, a);
+  OVL_HIP_TRY(hipGetLastError());
+  return OVL_OK;
+}

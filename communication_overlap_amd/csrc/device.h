@@ -27,7 +27,8 @@ struct ErrRec {
 static_assert(sizeof(ErrRec) == 64, "error record size");
 
 enum : int32_t {
-  kSiteAgUnit = 1, kSiteAgBarrier = 2, kSiteRsIn = 3, kSiteA2aSlice = 4, kSiteRsOwn = 5, kSiteAgSplit = 6
+  kSiteAgUnit = 1, kSiteAgBarrier = 2, kSiteRsIn = 3, kSiteA2aSlice = 4, kSiteRsOwn = 5, kSiteAgSplit = 6,
+  kSiteCbIn = 7
 };
 
 __device__ inline void report_error(ErrRec* e, int32_t code, int32_t site, int64_t index,
@@ -124,5 +125,28 @@ __device__ inline u32x4 ld16_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 __device__ inline void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Stores for data that workgroups on other dies read after a flag.  An
+// agent-scope store (a relaxed atomic store at agent scope: the sc1 bit) is
+// complete at the device's point of coherence once it drains, so a workgroup
+// that wrote a unit only with these publishes it with a drain and a barrier
+// (wg_arrive_agent) and skips the agent-scope release fence, whose L2
+// writeback of the die was measured at about 0.5 us, serialised per die.
+// Lanes take consecutive 8-byte words, so one store covers 512 contiguous
+// bytes per wave.
+__device__ inline void st8_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// wg_arrive for a unit written only with st8_agent: every wave drains its
+// stores, the barrier orders them before thread 0's add, and no L2
+// writeback is needed.  Returns the value before the add (thread 0 only).
+__device__ inline int64_t wg_arrive_agent(int64_t* counter) {
+  wave_drain();
+  __syncthreads();
+  int64_t old = 0;
+  if (threadIdx.x == 0) old = __hip_atomic_fetch_add(counter, (int64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return old;
+}
 
 }  // namespace ovl

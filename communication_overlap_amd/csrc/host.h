@@ -16,6 +16,7 @@ namespace ovl {
 constexpr uint64_t kDefaultSpinLimit = 1ull << 22;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t aligned_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

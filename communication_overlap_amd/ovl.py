@@ -36,6 +36,7 @@ EXPORTS = (
     "ag_gemm_workspace_bytes", "ag_gemm_splits", "ag_gemm_run",
     "gemm_rs_flags_bytes", "gemm_rs_workspace_bytes", "gemm_rs_run",
     "a2a_flags_bytes", "a2a_workspace_bytes", "a2a_dispatch_grouped_gemm_run",
+    "a2a_combine_flags_bytes", "a2a_combine_workspace_bytes", "a2a_combine_run",
     "ovl_flags_reset", "ovl_check", "ovl_strerror", "ovl_copy",
 )
 
@@ -109,6 +110,14 @@ def lib() -> ctypes.CDLL:
                                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                                 c_int64, POINTER(Opts), c_void_p]
     L.a2a_dispatch_grouped_gemm_run.restype = st
+    L.a2a_combine_flags_bytes.argtypes = [POINTER(A2aDesc)]
+    L.a2a_combine_flags_bytes.restype = c_size_t
+    L.a2a_combine_workspace_bytes.argtypes = [POINTER(A2aDesc)]
+    L.a2a_combine_workspace_bytes.restype = c_size_t
+    L.a2a_combine_run.argtypes = [POINTER(A2aDesc), c_void_p, c_void_p, POINTER(c_void_p), POINTER(c_void_p),
+                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
+                                  POINTER(Opts), c_void_p]
+    L.a2a_combine_run.restype = st
     L.ovl_flags_reset.argtypes = [c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]
     L.ovl_flags_reset.restype = st
     L.ovl_check.argtypes = [c_void_p, POINTER(c_int64), c_void_p]
@@ -255,6 +264,24 @@ def a2a_dispatch_grouped_gemm_run(desc: A2aDesc, x, topk_idx, w, recv_x, recv_sr
                                              _ptr(recv_x), _ptr(recv_src), _ptr(recv_count), _ptr(y), _ptr(flags),
                                              _ptr(workspace), epoch, byref(o), _stream(stream))
     return _check(st, "a2a_dispatch_grouped_gemm_run", raise_on_error)
+
+
+def a2a_combine_flags_bytes(desc: A2aDesc) -> int:
+    return lib().a2a_combine_flags_bytes(byref(desc))
+
+
+def a2a_combine_workspace_bytes(desc: A2aDesc) -> int:
+    return lib().a2a_combine_workspace_bytes(byref(desc))
+
+
+def a2a_combine_run(desc: A2aDesc, y, recv_count, ret_out, ret_in, topk_idx, gates, out, out_flags, in_flags,
+                    workspace, epoch: int, mode: int = MODE_FUSED, spin_limit: int = 0, stream=None,
+                    raise_on_error: bool = True) -> int:
+    o = _opts(mode, 0, spin_limit)
+    st = lib().a2a_combine_run(byref(desc), _ptr(y), _ptr(recv_count), _ptr_array(ret_out), _ptr_array(ret_in),
+                               _ptr(topk_idx), _ptr(gates), _ptr(out), _ptr(out_flags), _ptr(in_flags),
+                               _ptr(workspace), epoch, byref(o), _stream(stream))
+    return _check(st, "a2a_combine_run", raise_on_error)
 
 
 # ------------------------------------------------------------------ flags, errors, copy

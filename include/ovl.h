@@ -289,6 +289,48 @@ ovl_status a2a_dispatch_grouped_gemm_run(const a2a_desc* desc, const void* const
                                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * MoE combine: the reverse all-to-all of the expert outputs, then the
+ * gate-weighted sum back in token order (the Aboleth README's compiled MoE
+ * dispatch *and combine*; the reverse all-to-all for expert-parallel MoE in
+ * the Triton distributed tutorial list).  Same slice signal discipline as
+ * the dispatch, in reverse.  The pages give no formula; the reading:
+ *
+ *  - reverse put: this rank computed y[s][0:count_s] for source s (the rows
+ *    of a2a_dispatch_grouped_gemm_run, slice order); for every peer s it
+ *    copies them to ret_out[s] (row j to row j) and sets out_flags[s] to the
+ *    epoch once all are there (a peer it sends nothing to is flagged at once);
+ *  - sum: for this rank's own tokens (routing topk_idx [tokens][topk],
+ *    gates [tokens][topk] fp32), every peer q returns, in ret_in[q], the rows
+ *    its experts computed for them, in q's slice order for this rank (local
+ *    expert, then token), valid once in_flags[q] >= epoch.  Then
+ *      out[t] = sum over choices k, ascending, of gates[t][k] * Y(t, k)
+ *    in fp32, Y(t, k) being the row of (t, k) in y[rank] when its expert is
+ *    local, else in ret_in[owner]; choices with ids outside
+ *    [0, num_experts) contribute nothing.
+ *
+ * desc: as for the dispatch (tokens = this rank's tokens = the per-source
+ * token count, so cap = tokens * min(topk, experts_per_rank) rows per
+ * slice; hidden is not used).
+ * ---------------------------------------------------------------------- */
+size_t a2a_combine_flags_bytes(const a2a_desc* desc);      /* ranks * flag_stride (each of out/in) */
+size_t a2a_combine_workspace_bytes(const a2a_desc* desc);  /* 256 + choice rows */
+
+/* y:          fp32 [R][cap][n]; recv_count: int32 [R][experts_per_rank] (both as the
+ *             dispatch left them).
+ * ret_out:    HOST array[R] of fp32 [cap][n] device buffers (entry rank ignored).
+ * ret_in:     HOST array[R] of fp32 [cap][n] device buffers (entry rank ignored).
+ * topk_idx:   int32 [tokens][topk]; gates: fp32 [tokens][topk]; out: fp32 [tokens][n].
+ * out_flags:  written (slot s), in_flags: read (slot q); a2a_combine_flags_bytes each.
+ * Modes: FUSED; COPY_ONLY (reverse put and its flags only); GEMM_ONLY (the sum
+ * only, without waiting on in_flags: ret_in must be there).  With tokens = 0
+ * the row buffers may be NULL and the out flags are still set. */
+ovl_status a2a_combine_run(const a2a_desc* desc, const float* y, const int32_t* recv_count,
+                           float* const* ret_out, const float* const* ret_in,
+                           const int32_t* topk_idx, const float* gates, float* out,
+                           int64_t* out_flags, const int64_t* in_flags, void* workspace,
+                           int64_t epoch, const ovl_opts* opts, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Flags, errors, measurement.
  * ---------------------------------------------------------------------- */
 
@@ -304,7 +346,7 @@ ovl_status ovl_flags_reset(int64_t* flags, size_t flag_bytes, void* workspace, s
  * detail (HOST, may be NULL) receives {site, flag index, observed value,
  * awaited value}; sites: 1 AG-GEMM unit flag, 2 AG-GEMM barrier mode,
  * 3 GEMM-RS in flag, 4 dispatch slice flag, 5 GEMM-RS own-tile flag,
- * 6 AG-GEMM split-K range counter (index = tile). */
+ * 6 AG-GEMM split-K range counter (index = tile), 7 combine in flag (index = peer). */
 ovl_status ovl_check(const void* workspace, int64_t* detail, hipStream_t stream);
 
 const char* ovl_strerror(ovl_status status);
