@@ -14,7 +14,8 @@ expert, then token).  The combine
      computed for them (ret_in[q], in q's slice order for this rank), and
      writes out[t] = sum over choices k (ascending) of gates[t][k] * Y(t, k),
      Y(t, k) being the expert output of token t under its k-th expert: the
-     row of (t, k) in the slice of the rank that owns that expert.
+     row of (t, k) in the slice of the rank that owns that expert; a choice
+     whose id is not an expert contributes nothing (the dispatch skips it).
 """
 
 from __future__ import annotations
@@ -56,8 +57,11 @@ def combine(y, recv_count, ret_in, topk_idx, gates, rank: int, experts_per_rank:
     T, K = np.asarray(topk_idx).shape
     out = np.zeros((T, y.shape[2]), dtype=np.float64)
     g = np.asarray(gates, dtype=np.float64)
+    idx = np.asarray(topk_idx)
     for t in range(T):
         for k in range(K):
+            if not 0 <= idx[t, k] < R * experts_per_rank:
+                continue  # not an expert: contributes nothing
             q = int(owner[t, k])
             row = y[rank, pos[t, k]] if q == rank else np.asarray(ret_in[q][pos[t, k]], dtype=np.float64)
             out[t] += g[t, k] * row

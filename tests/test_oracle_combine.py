@@ -88,3 +88,17 @@ def test_planted_mistakes_fail_the_dense_pin():
     wrong[0], wrong[2] = wrong[2], wrong[0]
     _, out = oracle.combine(c["y"], c["rc"], wrong, c["topk"], c["gates"], 1, 2)
     assert not np.allclose(out, c["dense"])
+
+
+def test_choices_that_are_not_experts_contribute_nothing():
+    c = _chain(3, 20, 16, 8, 2, 2, 1, 3)
+    topk = c["topk"].copy()
+    topk[5, 1] = -1
+    topk[9, 0] = 6  # past the 6 experts
+    # the layout of the remaining choices is what the dispatch gives them
+    _, out = oracle.combine(c["y"], c["rc"], c["ret_in"], topk, c["gates"], 1, 2)
+    pos, owner = oracle.combine_positions(topk, 3, 2)
+    for t, keep in ((5, 0), (9, 1)):
+        q = owner[t, keep]
+        row = c["y"][1, pos[t, keep]] if q == 1 else c["ret_in"][q][pos[t, keep]]
+        np.testing.assert_allclose(out[t], float(c["gates"][t, keep]) * row, rtol=1e-15)
