@@ -103,16 +103,15 @@ __device__ inline void wg_publish(int64_t* flag, int64_t epoch) {
 }
 
 // Workgroup-level arrival on a counter, with the same release as
-// wg_publish; thread 0 adds 1 and returns the value it observed before the
-// add, having acquired the earlier arrivals (only thread 0's value is
-// meaningful).
-__device__ inline int64_t wg_arrive(int64_t* counter) {
+// wg_publish; thread 0 adds n and returns the value it observed before the
+// add (only thread 0's value is meaningful).
+__device__ inline int64_t wg_arrive(int64_t* counter, int64_t n = 1) {
   wave_drain();
   __syncthreads();
   int64_t old = 0;
   if (threadIdx.x == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    old = __hip_atomic_fetch_add(counter, (int64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __hip_atomic_fetch_add(counter, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   return old;
 }
