@@ -34,8 +34,8 @@ METRIC = "fused AG-GEMM TFLOP/s (% bf16 MFMA peak) + overlap eff. vs copy+GEMM s
 # --pmc passes (FETCH_SIZE x 2.00 + WRITE_SIZE x 1.00, the factors a plain
 # 256 MiB copy reads on the same counters), and the hash of the kernel
 # sources they were taken on; reported only while the sources are unchanged.
-TRAFFIC_BYTES = (304871 * 2.0 + 180240 * 1.0) * 1024
-TRAFFIC_SOURCES_SHA = "a11acc67dd9abbc3"
+TRAFFIC_BYTES = (325373 * 2.0 + 180230 * 1.0) * 1024
+TRAFFIC_SOURCES_SHA = "e8d4cd72b0bb9d24"
 KERNEL_SOURCES = ("communication_overlap_amd/csrc/ag_gemm.hip", "communication_overlap_amd/csrc/gemm_core.h",
                   "communication_overlap_amd/csrc/device.h")
 
@@ -72,10 +72,15 @@ class Flusher:
         self.buf.zero_()
 
 
-def timed_reps(fn, reps, flush=None):
+def timed_reps(fn, reps, flush=None, warm=5):
     """Median / p10 / p90 of fn's device time in microseconds (HIP events on
-    the current stream around fn only)."""
+    the current stream around fn only), after `warm` untimed calls."""
     import torch
+    for _ in range(warm):
+        if flush:
+            flush()
+        fn()
+    torch.cuda.synchronize()
     times = []
     for _ in range(reps):
         if flush:
