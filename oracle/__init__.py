@@ -19,3 +19,4 @@ from .ag_gemm import all_gather, ag_gemm, gemm, gemm_entries, ag_flag_units, exp
 from .gemm_rs import gemm_rs, rs_expected_flags  # noqa: F401
 from .dispatch import dispatch_layout, dispatch, grouped_gemm, grouped_gemm_rows  # noqa: F401
 from .combine import combine, combine_positions  # noqa: F401
+from .ring import ring_allreduce, allreduce_sum, ring_chunk_bounds  # noqa: F401
