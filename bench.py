@@ -398,6 +398,38 @@ def side_workloads(reps, flush):
         "fused_over_put_plus_sum": t["median_us"] / (put["median_us"] + sm["median_us"])}
     del recv_x, y, ret_out, d_ret_in, out
 
+    # Ring all-reduce: 8 emulated ranks x 8M fp32 (32 MiB each), 16K-element
+    # tiles, every rank's steps in one launch (FUSED) or one launch per ring
+    # step (BARRIER: no tile-level overlap between steps).
+    cfg = synth.CONFIGS["ring_r8_n8m"]
+    log(f"[bench] side {cfg.name}")
+    R = cfg.ranks
+    r_in = [dev(v) for v in synth.ring_inputs(cfg)]
+    r_out = [torch.zeros(cfg.n, dtype=torch.float32, device="cuda") for _ in range(R)]
+    rdesc = ovl.ring_desc(R, cfg.n, cfg.tile)
+    rfb = ovl.ring_allreduce_flags_bytes(rdesc)
+    r_flags = torch.zeros(rfb, dtype=torch.uint8, device="cuda")
+    r_ws = torch.zeros(ovl.ring_allreduce_workspace_bytes(rdesc), dtype=torch.uint8, device="cuda")
+    ovl.ovl_flags_reset(r_flags, rfb, r_ws, r_ws.numel())
+    rep_ = [0]
+
+    def ring(mode=0):
+        rep_[0] += 1
+        ovl.ring_allreduce_run(rdesc, r_in, r_out, r_flags, r_ws, rep_[0], mode=mode)
+
+    ring()
+    t = timed_reps(ring, reps, flush)
+    b = timed_reps(lambda: ring(ovl.MODE_BARRIER), reps, flush)
+    ovl.ovl_check(r_ws)
+    # per rank and tile position: send (2 tile-bytes), R-2 add-and-send (3),
+    # complete-and-send (4), R-2 forwards (2): (5R - 4) x n x 4 bytes in all
+    r_bytes = (5 * R - 4) * cfg.n * 4
+    res[cfg.name] = {"fused_us": t, "barrier_us": b, "bytes": r_bytes,
+                     "GBps": r_bytes / (t["median_us"] * 1e-6) / 1e9,
+                     "pct_of_hbm_peak": 100 * r_bytes / (t["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                     "fused_over_barrier": t["median_us"] / b["median_us"]}
+    del r_in, r_out
+
     # Plain copy, for the HBM reference point.
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)

@@ -28,7 +28,7 @@ static_assert(sizeof(ErrRec) == 64, "error record size");
 
 enum : int32_t {
   kSiteAgUnit = 1, kSiteAgBarrier = 2, kSiteRsIn = 3, kSiteA2aSlice = 4, kSiteRsOwn = 5, kSiteAgSplit = 6,
-  kSiteCbIn = 7
+  kSiteCbIn = 7, kSiteRing = 8
 };
 
 __device__ inline void report_error(ErrRec* e, int32_t code, int32_t site, int64_t index,

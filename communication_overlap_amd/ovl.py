@@ -38,6 +38,7 @@ EXPORTS = (
     "a2a_flags_bytes", "a2a_workspace_bytes", "a2a_dispatch_grouped_gemm_run",
     "a2a_combine_flags_bytes", "a2a_combine_workspace_bytes", "a2a_combine_run",
     "ovl_flags_reset", "ovl_check", "ovl_strerror", "ovl_copy",
+    "ring_allreduce_flags_bytes", "ring_allreduce_workspace_bytes", "ring_allreduce_run",
 )
 
 
@@ -65,6 +66,10 @@ class A2aDesc(Structure):
     _fields_ = [("ranks", c_int32), ("rank", c_int32), ("tokens", c_int64), ("hidden", c_int64), ("n", c_int64),
                 ("topk", c_int32), ("num_experts", c_int32), ("experts_per_rank", c_int32),
                 ("flag_stride", c_int32)]
+
+
+class RingDesc(Structure):
+    _fields_ = [("ranks", c_int32), ("n", c_int64), ("tile", c_int64), ("flag_stride", c_int32)]
 
 
 _lib = None
@@ -126,6 +131,13 @@ def lib() -> ctypes.CDLL:
     L.ovl_strerror.restype = c_char_p
     L.ovl_copy.argtypes = [c_void_p, c_void_p, c_size_t, c_int32, c_void_p]
     L.ovl_copy.restype = st
+    L.ring_allreduce_flags_bytes.argtypes = [POINTER(RingDesc)]
+    L.ring_allreduce_flags_bytes.restype = c_size_t
+    L.ring_allreduce_workspace_bytes.argtypes = [POINTER(RingDesc)]
+    L.ring_allreduce_workspace_bytes.restype = c_size_t
+    L.ring_allreduce_run.argtypes = [POINTER(RingDesc), POINTER(c_void_p), POINTER(c_void_p), c_void_p, c_void_p,
+                                     c_int64, POINTER(Opts), c_void_p]
+    L.ring_allreduce_run.restype = st
     _lib = L
     return L
 
@@ -282,6 +294,28 @@ def a2a_combine_run(desc: A2aDesc, y, recv_count, ret_out, ret_in, topk_idx, gat
                                _ptr(topk_idx), _ptr(gates), _ptr(out), _ptr(out_flags), _ptr(in_flags),
                                _ptr(workspace), epoch, byref(o), _stream(stream))
     return _check(st, "a2a_combine_run", raise_on_error)
+
+
+# ------------------------------------------------------------------ ring all-reduce
+
+def ring_desc(ranks, n, tile, flag_stride=8) -> RingDesc:
+    return RingDesc(ranks, n, tile, flag_stride)
+
+
+def ring_allreduce_flags_bytes(desc: RingDesc) -> int:
+    return lib().ring_allreduce_flags_bytes(byref(desc))
+
+
+def ring_allreduce_workspace_bytes(desc: RingDesc) -> int:
+    return lib().ring_allreduce_workspace_bytes(byref(desc))
+
+
+def ring_allreduce_run(desc: RingDesc, inputs, outputs, flags, workspace, epoch: int, mode: int = MODE_FUSED,
+                       spin_limit: int = 0, stream=None, raise_on_error: bool = True) -> int:
+    o = _opts(mode, 0, spin_limit)
+    st = lib().ring_allreduce_run(byref(desc), _ptr_array(inputs), _ptr_array(outputs), _ptr(flags),
+                                  _ptr(workspace), epoch, byref(o), _stream(stream))
+    return _check(st, "ring_allreduce_run", raise_on_error)
 
 
 # ------------------------------------------------------------------ flags, errors, copy

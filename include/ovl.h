@@ -2,7 +2,7 @@
  * ovl.h: tile-centric overlap of communication with computation on one
  * MI355X (gfx950).
  *
- * Three operations, each one persistent HIP launch in which producer
+ * Five operations, each one persistent HIP launch in which producer
  * workgroups move tiles and publish one int64 flag per tile batch, and
  * consumer workgroups wait on each flag and compute on that tile at once
  * ("Triton-distributed Semantics": Producer-Consumer Model, Signal-Based
@@ -31,10 +31,12 @@
  *    Epochs used on one flag buffer must increase from call to call; zero
  *    the buffer with ovl_flags_reset() before its first use, after which
  *    epochs start again at 1.
- *  - Ordering: a producer's data stores are released at agent scope before
- *    its flag store; a consumer acquires at agent scope after its flag load
- *    and issues its tile loads only afterwards (the role consume_token plays
- *    in "Triton-distributed Semantics", Token-Based Data Dependency).  No
+ *  - Ordering: a producer's data stores are complete at agent scope before
+ *    its flag store (released by an agent-scope fence, or written as
+ *    agent-scope stores and drained); a consumer acquires at agent scope
+ *    after its flag load, or reads the data with agent-scope loads, and
+ *    issues its tile loads only afterwards (the role consume_token plays in
+ *    "Triton-distributed Semantics", Token-Based Data Dependency).  No
  *    system-scope ordering is used: every peer lives in the same HBM.
  *  - Two calls must not run concurrently on the same flags or workspace.
  *  - Results do not depend on the producer order, the mode or the number of
@@ -331,6 +333,49 @@ ovl_status a2a_combine_run(const a2a_desc* desc, const float* y, const int32_t* 
                            int64_t epoch, const ovl_opts* opts, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Ring all-reduce with per-tile signals ("Triton-distributed Semantics",
+ * Example: Ring AllReduce with Overlap).  Every one of the R ranks of the
+ * ring is emulated in the one launch: in[r] and out[r] are rank r's vectors
+ * (fp32, n elements each) and out[r] ends as the element-wise sum of all
+ * in[q], with the same bits on every rank.
+ *
+ * The vector is cut into R chunks of cs = ceil(n / R) elements, rounded up to
+ * an even count (the last ones may be short or empty), and each chunk into
+ * tiles of `tile` elements.  Reduce-scatter step s (0 <= s < R - 1): rank r
+ * sends chunk (r - s) mod R to rank r + 1 (the example's send schedule),
+ * which adds its own copy of that chunk; after R - 1 steps rank r holds the
+ * complete chunk (r + 1) mod R, and R - 1 all-gather steps pass the complete
+ * chunks on around the ring.  (The printed example reduces into the tile it
+ * has just sent and its phases disagree by one chunk; this is the reading
+ * its send schedule supports.)  So chunk c is summed in float32 as
+ * ((x_c + x_{c+1}) + x_{c+2}) + ... + x_{c-1}, ranks mod R.  Each tile of
+ * each step is signalled on its own: flag slot ((r * (2R - 2)) + s - 1) *
+ * tiles_per_chunk + j holds the epoch once tile j of rank r's step-s input
+ * (s >= 1) is in out[r]; every slot is set by the end of a run.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t ranks;        /* R, 1 .. 16 */
+  int64_t n;            /* fp32 elements per rank, 0 .. 2^31 */
+  int64_t tile;         /* elements per signalled tile: even, >= 2 */
+  int32_t flag_stride;  /* bytes between flag slots: a multiple of 8 */
+} ring_desc;
+
+size_t ring_allreduce_flags_bytes(const ring_desc* desc);      /* R * (2R - 2) * tiles_per_chunk * flag_stride */
+size_t ring_allreduce_workspace_bytes(const ring_desc* desc);  /* 256 (0 if desc is invalid) */
+
+/* in, out: HOST arrays[R] of device fp32 [n] buffers.  Partial sums travel
+ * through the outputs while the inputs are read, so no output may overlap
+ * an input or another output (OVL_EINVAL).  Modes: FUSED (one launch, tiles
+ * pipelined through their flags); BARRIER (one launch per ring step, so every
+ * tile of a step is in place before any tile of the next moves: the same
+ * steps without tile-level overlap).  Both give the same bits and flags.
+ * Device errors (site 8, index = flag slot) come only from a wait that
+ * exceeded opts->spin_limit. */
+ovl_status ring_allreduce_run(const ring_desc* desc, const float* const* in, float* const* out,
+                              int64_t* flags, void* workspace, int64_t epoch, const ovl_opts* opts,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Flags, errors, measurement.
  * ---------------------------------------------------------------------- */
 
@@ -346,7 +391,8 @@ ovl_status ovl_flags_reset(int64_t* flags, size_t flag_bytes, void* workspace, s
  * detail (HOST, may be NULL) receives {site, flag index, observed value,
  * awaited value}; sites: 1 AG-GEMM unit flag, 2 AG-GEMM barrier mode,
  * 3 GEMM-RS in flag, 4 dispatch slice flag, 5 GEMM-RS own-tile flag,
- * 6 AG-GEMM split-K range counter (index = tile), 7 combine in flag (index = peer). */
+ * 6 AG-GEMM split-K range counter (index = tile), 7 combine in flag (index = peer),
+ * 8 ring all-reduce tile flag. */
 ovl_status ovl_check(const void* workspace, int64_t* detail, hipStream_t stream);
 
 const char* ovl_strerror(ovl_status status);

@@ -20,6 +20,6 @@ from .gen import (  # noqa: F401
     zipf_topk_gates,
 )
 from .configs import (  # noqa: F401
-    CONFIGS, AgGemmCfg, GemmRsCfg, DispatchCfg,
-    ag_inputs, rs_inputs, dispatch_inputs, combine_inputs, producer_order,
+    CONFIGS, AgGemmCfg, GemmRsCfg, DispatchCfg, RingCfg,
+    ag_inputs, rs_inputs, dispatch_inputs, combine_inputs, ring_inputs, producer_order,
 )

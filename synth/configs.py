@@ -2,8 +2,9 @@
 
 Stream ids: A shard s -> (1, s); B -> (2, 0); peer partial p -> (3, p);
 tokens of source s -> (4, s); routing draws of source s -> (5, s); expert
-weight e -> (6, e); producer order of epoch e -> (7, e).  Seeds are 1000 + i
-for the i-th workload below.
+weight e -> (6, e); producer order of epoch e -> (7, e); rows a peer returns
+to the combine -> (8, q); ring all-reduce vector of rank r -> (10, r).  Seeds
+are 1000 + i for the i-th workload below.
 """
 
 from __future__ import annotations
@@ -85,6 +86,16 @@ class DispatchCfg:
         return self.tokens * min(self.topk, self.experts_per_rank)
 
 
+@dataclass(frozen=True)
+class RingCfg:
+    name: str
+    ranks: int
+    n: int        # fp32 elements per rank
+    tile: int     # elements per signalled tile
+    sigma: float
+    seed: int
+
+
 CONFIGS = {
     # R=2 ranks of 64x256 bf16 N(0,1) shards; B 256x256 N(0,1)/16; tile 32x32.
     "ag_r2_128x256x256": AgGemmCfg("ag_r2_128x256x256", 2, 64, 256, 256, 32, 32,
@@ -102,6 +113,9 @@ CONFIGS = {
     # 8 local experts with W 4096x1408.
     "a2a_r8_t4096_h4096_e64": DispatchCfg("a2a_r8_t4096_h4096_e64", 8, 4096, 4096, 1408, 2, 64, 8,
                                           1.1, 1.0, 0.02, 1004),
+    # Ring all-reduce: 8 ranks x 32 MiB fp32 (8M elements, a gradient bucket),
+    # N(0,1); chunks of 1M elements in 64 tiles of 16K (64 KiB).
+    "ring_r8_n8m": RingCfg("ring_r8_n8m", 8, 8 << 20, 16 << 10, 1.0, 1005),
 }
 
 
@@ -201,3 +215,12 @@ def combine_inputs(cfg: DispatchCfg, kind: str = "normal"):
         ret = [None if q == cfg.rank else normal_f32(stream_key(cfg.seed, 8, q), cap * N, 1.0).reshape(cap, N)
                for q in range(R)]
     return gates, ret
+
+
+# ---------------------------------------------------------------- ring all-reduce inputs
+
+def ring_inputs(cfg: RingCfg, kind: str = "normal"):
+    """R float32 [n] vectors, one per rank."""
+    if kind == "smallint":
+        return [small_int_f32(cfg.seed, 10, r, (cfg.n,), -1000, 1000) for r in range(cfg.ranks)]
+    return [normal_f32(stream_key(cfg.seed, 10, r), cfg.n, cfg.sigma) for r in range(cfg.ranks)]
