@@ -20,3 +20,4 @@ from .gemm_rs import gemm_rs, rs_expected_flags  # noqa: F401
 from .dispatch import dispatch_layout, dispatch, grouped_gemm, grouped_gemm_rows  # noqa: F401
 from .combine import combine, combine_positions  # noqa: F401
 from .ring import ring_allreduce, allreduce_sum, ring_chunk_bounds  # noqa: F401
+from .fp8 import e4m3_decode, e4m3_encode, quantize_rows, dispatch_fp8, grouped_gemm_fp8  # noqa: F401
