@@ -28,6 +28,7 @@
 
 #include "device.h"
 #include "gemm_core.h"
+#include "gemm_fp8.h"
 #include "host.h"
 
 namespace ovl {
@@ -38,14 +39,25 @@ constexpr int kA2aMaxRanks = 16;
 constexpr int kA2aMaxExperts = 64;
 constexpr int kChunkRows = 32;
 constexpr int kGbm = 256, kGbn = 256;  // grouped GEMM tile
+// The FP8 tile is half as wide: its epilogue scales every accumulator, and
+// with 256 columns the compiler moves them all out of the accumulation
+// registers at once and spills.
+constexpr int kGbn8 = 128;
 constexpr int kA2aMaxMTiles = 1024;    // m-tiles whose consumer order is sorted in LDS
 constexpr int kA2aXcds = 8;
+// LDS of a grouped-GEMM tile, bf16 or FP8 (the geometry follows it).
+constexpr int kA2aGemmLds = TileCfg<kGbm, kGbn>::LDS_BYTES > F8Cfg<kGbm, kGbn8>::LDS_BYTES
+                                ? TileCfg<kGbm, kGbn>::LDS_BYTES
+                                : F8Cfg<kGbm, kGbn8>::LDS_BYTES;
 
 struct A2aArgs {
-  const uint16_t* x[kA2aMaxRanks];
+  const uint8_t* x[kA2aMaxRanks];        // token rows of row_bytes (bf16 or FP8 codes)
+  const float* x_scale[kA2aMaxRanks];    // FP8: per-token scales (else null)
   const int32_t* topk[kA2aMaxRanks];
-  const uint16_t* w;
-  uint16_t* recv_x;
+  const uint8_t* w;        // bf16 [E][hidden][n], or FP8 codes [E][n][hidden]
+  const float* w_scale;    // FP8: [E][n]
+  uint8_t* recv_x;
+  float* recv_scale;       // FP8: [R][cap]
   int32_t* recv_src;
   int32_t* recv_count;
   float* y;
@@ -54,6 +66,7 @@ struct A2aArgs {
   int64_t* ticket;    // next chunk to copy in the fused launch (workspace)
   ErrRec* err;
   int64_t tokens, hidden, n, cap;
+  int64_t row_bytes;    // bytes of one token row: hidden * 2 (bf16) or hidden (FP8)
   int64_t flag_stride;  // int64 slots
   int64_t epoch;
   uint64_t spin_limit;
@@ -256,11 +269,12 @@ __device__ inline void mtile_at(const A2aArgs& a, const Geometry* g, int q, int*
 // flight (vector memory counters complete in order: waiting for the loads
 // then does not wait for the stores issued after them).
 __device__ inline void copy_rows(const A2aArgs& a, int s, int r0, int r1) {
-  constexpr int V = 8;  // vectors per lane per row and pass (a 4096-wide row in one pass)
+  constexpr int V = 8;  // vectors per lane per row and pass (an 8 KiB row in one pass)
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int vpr = (int)(a.hidden / 8);
-  const uint16_t* src = a.x[s];
-  uint16_t* dst = a.recv_x + (int64_t)s * a.cap * a.hidden;
+  const int vpr = (int)(a.row_bytes / 16);
+  const uint8_t* src = a.x[s];
+  uint8_t* dst = a.recv_x + (int64_t)s * a.cap * a.row_bytes;
+  const float* xs = a.x_scale[s];
   const int32_t* srow = a.recv_src + (int64_t)s * a.cap;
   // Steps: (row pair, column pass); a pair is rows r, r + 4 of this wave.
   const int passes = (vpr + 64 * V - 1) / (64 * V);
@@ -273,11 +287,11 @@ __device__ inline void copy_rows(const A2aArgs& a, int s, int r0, int r1) {
     for (int h = 0; h < 2; ++h) {
       const int rr = r + 4 * h;
       if (rr >= r1) continue;
-      const uint16_t* sp = src + (int64_t)__builtin_amdgcn_readfirstlane(srow[rr]) * a.hidden;
+      const uint8_t* sp = src + (int64_t)__builtin_amdgcn_readfirstlane(srow[rr]) * a.row_bytes;
 #pragma unroll
       for (int q = 0; q < V; ++q) {
         const int c = c0 + q * 64 + lane;
-        if (c < vpr) v[h][q] = ld16_nt(sp + c * 8);
+        if (c < vpr) v[h][q] = ld16_nt(sp + c * 16);
       }
     }
   };
@@ -287,12 +301,14 @@ __device__ inline void copy_rows(const A2aArgs& a, int s, int r0, int r1) {
     for (int h = 0; h < 2; ++h) {
       const int rr = r + 4 * h;
       if (rr >= r1) continue;
-      uint16_t* dp = dst + (int64_t)rr * a.hidden;
+      uint8_t* dp = dst + (int64_t)rr * a.row_bytes;
 #pragma unroll
       for (int q = 0; q < V; ++q) {
         const int c = c0 + q * 64 + lane;
-        if (c < vpr) st16(dp + c * 8, v[h][q]);
+        if (c < vpr) st16(dp + c * 16, v[h][q]);
       }
+      // FP8: the row's scale travels with it (once per row, in its first pass)
+      if (xs && c0 == 0 && lane == 0) a.recv_scale[(int64_t)s * a.cap + rr] = xs[srow[rr]];
     }
   };
   if (steps > 0) load(0, cur);
@@ -436,11 +452,13 @@ __device__ bool wait_slice_helping(const A2aArgs& a, const Geometry* g, int s, i
   return ok;
 }
 
-template <bool WAIT>
+template <bool WAIT, bool F8>
 __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint16_t* lds) {
   __shared__ int sh[2];
   __shared__ int32_t rowtab[2][kGbm];  // A / y row of each tile row (s * cap + slice row), or -1
-  const int ntn = (int)((a.n + kGbn - 1) / kGbn);
+  __shared__ float scaletab[F8 ? 2 : 1][F8 ? kGbm : 1];  // FP8: the scale of each tile row
+  constexpr int TBN = F8 ? kGbn8 : kGbn;
+  const int ntn = (int)((a.n + TBN - 1) / TBN);
   const int total = uniform(g->n_mt) * ntn;
   const int Cn = a.consumers;
   const int groups = (Cn % kA2aXcds == 0) ? kA2aXcds : 1;
@@ -477,21 +495,38 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
         v = s * (int32_t)a.cap + g->seg_start[pos * a.experts + e] + (r - pre[pos]);
       }
       tab[i] = v;
+      if constexpr (F8) scaletab[wv & 1][i] = v >= 0 ? a.recv_scale[v] : 0.f;
     }
     __syncthreads();
-    Operands op;
-    op.a = a.recv_x;
-    op.lda = a.hidden;
-    op.m_valid = (int64_t)a.ranks * a.cap;
-    op.rows = tab;
-    op.b = a.w + (int64_t)e * a.hidden * a.n;
-    op.ldb = a.n;
-    op.n0 = (int64_t)nt * kGbn;
-    op.n_valid = a.n;
-    op.k = a.hidden;
-    Acc<kGbm, kGbn> acc;
-    gemm_tile<kGbm, kGbn, 64, 0, true>(acc, op, 0, lds, [](int64_t, int64_t) {});
-    acc_store_rows<kGbm, kGbn>(acc, a.y, a.n, (int64_t)a.ranks * a.cap, tab, op.n0, a.n);
+    Acc<kGbm, TBN> acc;
+    if constexpr (F8) {
+      Operands8 op;
+      op.a = a.recv_x;
+      op.lda = a.hidden;
+      op.m_valid = (int64_t)a.ranks * a.cap;
+      op.rows = tab;
+      op.bt = a.w + (int64_t)e * a.n * a.hidden;
+      op.ldb = a.hidden;
+      op.n0 = (int64_t)nt * TBN;
+      op.n_valid = a.n;
+      op.k = a.hidden;
+      gemm_tile_fp8<kGbm, TBN, true>(acc, op, reinterpret_cast<uint8_t*>(lds));
+      acc_store_rows_scaled<kGbm, TBN>(acc, a.y, a.n, (int64_t)a.ranks * a.cap, tab, scaletab[wv & 1],
+                                        a.w_scale + (int64_t)e * a.n, op.n0, a.n);
+    } else {
+      Operands op;
+      op.a = reinterpret_cast<const uint16_t*>(a.recv_x);
+      op.lda = a.hidden;
+      op.m_valid = (int64_t)a.ranks * a.cap;
+      op.rows = tab;
+      op.b = reinterpret_cast<const uint16_t*>(a.w) + (int64_t)e * a.hidden * a.n;
+      op.ldb = a.n;
+      op.n0 = (int64_t)nt * TBN;
+      op.n_valid = a.n;
+      op.k = a.hidden;
+      gemm_tile<kGbm, TBN, 64, 0, true>(acc, op, 0, lds, [](int64_t, int64_t) {});
+      acc_store_rows<kGbm, TBN>(acc, a.y, a.n, (int64_t)a.ranks * a.cap, tab, op.n0, a.n);
+    }
   }
 }
 
@@ -499,11 +534,11 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
 // left; consumers take tickets too whenever the slice of their next tile is
 // not complete yet, so the first consumers copy the first slices together
 // and the copy keeps ahead of the GEMM.
-template <int MODE>  // 0 fused, 2 GEMM only
+template <int MODE, bool F8>  // MODE 0 fused, 2 GEMM only; F8: FP8 rows and grouped GEMM
 __global__ __launch_bounds__(kThreads, 1) void a2a_fused_kernel(A2aArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int sh;
-  Geometry* g = reinterpret_cast<Geometry*>(reinterpret_cast<uint8_t*>(lds) + TileCfg<kGbm, kGbn>::LDS_BYTES);
+  Geometry* g = reinterpret_cast<Geometry*>(reinterpret_cast<uint8_t*>(lds) + kA2aGemmLds);
   build_geometry(a, g);
   if (MODE == 0) {
     // Slices that receive nothing are complete at once.
@@ -518,10 +553,10 @@ __global__ __launch_bounds__(kThreads, 1) void a2a_fused_kernel(A2aArgs a) {
       return;
     }
   }
-  a2a_consume<MODE == 0>(a, g, (int)blockIdx.x - a.producers, lds);
+  a2a_consume<MODE == 0, F8>(a, g, (int)blockIdx.x - a.producers, lds);
 }
 
-constexpr int a2a_lds_bytes() { return TileCfg<kGbm, kGbn>::LDS_BYTES + (int)sizeof(Geometry); }
+constexpr int a2a_lds_bytes() { return kA2aGemmLds + (int)sizeof(Geometry); }
 
 }  // namespace
 
@@ -540,39 +575,50 @@ extern "C" size_t a2a_workspace_bytes(const a2a_desc* d) {
   return OVL_ERROR_RECORD_BYTES + 8 * (size_t)kA2aMaxRanks + 8;
 }
 
-extern "C" ovl_status a2a_dispatch_grouped_gemm_run(const a2a_desc* d, const void* const* x,
-                                                    const int32_t* const* topk_idx, const void* w, void* recv_x,
-                                                    int32_t* recv_src, int32_t* recv_count, float* y,
-                                                    int64_t* flags, void* workspace, int64_t epoch,
-                                                    const ovl_opts* opts, hipStream_t stream) {
+namespace ovl {
+namespace {
+
+// Both dispatch entry points: f8 selects FP8 rows (hidden bytes, a scale
+// each) and the FP8 grouped GEMM (weights [E][n][hidden] codes, a scale per
+// output column).
+ovl_status a2a_run(const a2a_desc* d, bool f8, const void* const* x, const float* const* x_scale,
+                   const int32_t* const* topk_idx, const void* w, const float* w_scale, void* recv_x,
+                   float* recv_scale, int32_t* recv_src, int32_t* recv_count, float* y, int64_t* flags,
+                   void* workspace, int64_t epoch, const ovl_opts* opts, hipStream_t stream) {
   if (!d || !recv_count || !flags || !workspace) return OVL_EINVAL;
   const bool empty = d->tokens == 0;  // nothing to read or write but counts and flags
-  if (!empty && (!x || !topk_idx || !recv_x || !recv_src)) return OVL_EINVAL;
+  if (!empty && (!x || !topk_idx || !recv_x || !recv_src || (f8 && (!x_scale || !recv_scale)))) return OVL_EINVAL;
   if (d->ranks < 1 || d->rank < 0 || d->rank >= d->ranks) return OVL_EINVAL;
   if (d->ranks > kA2aMaxRanks || d->experts_per_rank > kA2aMaxExperts) return OVL_EUNSUPPORTED;
   if (d->experts_per_rank < 1 || d->topk < 1 || d->topk > 8 || d->tokens < 0 ||
       d->num_experts != d->ranks * d->experts_per_rank)
     return OVL_ESHAPE;
-  if (d->hidden < 8 || d->n < 8 || d->hidden % 8 || d->n % 8 || d->flag_stride < 8 || d->flag_stride % 8)
+  const int64_t hid_mult = f8 ? 16 : 8;  // a row moves in 16-byte vectors
+  if (d->hidden < hid_mult || d->n < 8 || d->hidden % hid_mult || d->n % 8 || d->flag_stride < 8 ||
+      d->flag_stride % 8)
     return OVL_EALIGN;
   const int64_t cap = d->tokens * std::min<int64_t>(d->topk, d->experts_per_rank);
+  const int64_t esz = f8 ? 1 : 2;
   // Every operand below 1 GiB and rows below 2^20 elements: buffer offsets stay in 32 bits.
   if (d->tokens > (1 << 20) || d->hidden > (1 << 20) || d->n > (1 << 20) ||
-      (int64_t)d->ranks * cap * d->hidden * 2 > (1ll << 30) || (int64_t)d->ranks * cap * d->n * 4 > (1ll << 30) ||
-      (int64_t)d->experts_per_rank * d->hidden * d->n * 2 > (1ll << 30))
+      (int64_t)d->ranks * cap * d->hidden * esz > (1ll << 30) || (int64_t)d->ranks * cap * d->n * 4 > (1ll << 30) ||
+      (int64_t)d->experts_per_rank * d->hidden * d->n * esz > (1ll << 30))
     return OVL_EUNSUPPORTED;
   const uint32_t mode = opts ? opts->mode : OVL_MODE_FUSED;
   if (mode != OVL_MODE_FUSED && mode != OVL_MODE_GEMM_ONLY && mode != OVL_MODE_COPY_ONLY) return OVL_EINVAL;
   const bool gemm = mode != OVL_MODE_COPY_ONLY;
-  if (gemm && !empty && (!w || !y)) return OVL_EINVAL;
+  if (gemm && !empty && (!w || !y || (f8 && !w_scale))) return OVL_EINVAL;
   if (!aligned16(recv_x) || !aligned16(workspace) || (gemm && (!aligned16(w) || !aligned16(y))) ||
       (reinterpret_cast<uintptr_t>(flags) & 7u) || (reinterpret_cast<uintptr_t>(recv_src) & 3u) ||
-      (reinterpret_cast<uintptr_t>(recv_count) & 3u))
+      (reinterpret_cast<uintptr_t>(recv_count) & 3u) || (reinterpret_cast<uintptr_t>(recv_scale) & 3u) ||
+      (reinterpret_cast<uintptr_t>(w_scale) & 3u))
     return OVL_EALIGN;
   for (int s = 0; s < d->ranks; ++s) {
     if (mode == OVL_MODE_GEMM_ONLY || empty) break;
-    if (!x[s] || !topk_idx[s]) return OVL_EINVAL;
-    if (!aligned16(x[s]) || (reinterpret_cast<uintptr_t>(topk_idx[s]) & 3u)) return OVL_EALIGN;
+    if (!x[s] || !topk_idx[s] || (f8 && !x_scale[s])) return OVL_EINVAL;
+    if (!aligned16(x[s]) || (reinterpret_cast<uintptr_t>(topk_idx[s]) & 3u) ||
+        (f8 && (reinterpret_cast<uintptr_t>(x_scale[s]) & 3u)))
+      return OVL_EALIGN;
   }
   DeviceInfo di;
   ovl_status st = current_device_info(&di);
@@ -581,11 +627,14 @@ extern "C" ovl_status a2a_dispatch_grouped_gemm_run(const a2a_desc* d, const voi
   A2aArgs a = {};
   for (int s = 0; s < d->ranks; ++s) {
     if (mode == OVL_MODE_GEMM_ONLY || empty) break;
-    a.x[s] = static_cast<const uint16_t*>(x[s]);
+    a.x[s] = static_cast<const uint8_t*>(x[s]);
+    a.x_scale[s] = f8 ? x_scale[s] : nullptr;
     a.topk[s] = topk_idx[s];
   }
-  a.w = static_cast<const uint16_t*>(w);
-  a.recv_x = static_cast<uint16_t*>(recv_x);
+  a.w = static_cast<const uint8_t*>(w);
+  a.w_scale = f8 ? w_scale : nullptr;
+  a.recv_x = static_cast<uint8_t*>(recv_x);
+  a.recv_scale = f8 ? recv_scale : nullptr;
   a.recv_src = recv_src;
   a.recv_count = recv_count;
   a.y = y;
@@ -597,6 +646,7 @@ extern "C" ovl_status a2a_dispatch_grouped_gemm_run(const a2a_desc* d, const voi
   a.hidden = d->hidden;
   a.n = d->n;
   a.cap = cap;
+  a.row_bytes = d->hidden * esz;
   a.flag_stride = d->flag_stride / 8;
   a.epoch = epoch;
   a.spin_limit = spin_limit_of(opts);
@@ -606,13 +656,12 @@ extern "C" ovl_status a2a_dispatch_grouped_gemm_run(const a2a_desc* d, const voi
   a.experts = d->experts_per_rank;
 
   const int lds = a2a_lds_bytes();
-  const void* fk = (mode == OVL_MODE_GEMM_ONLY) ? reinterpret_cast<const void*>(&a2a_fused_kernel<2>)
-                                                : reinterpret_cast<const void*>(&a2a_fused_kernel<0>);
-  st = allow_lds(fk, lds);
+  auto fk = f8 ? (mode == OVL_MODE_GEMM_ONLY ? a2a_fused_kernel<2, true> : a2a_fused_kernel<0, true>)
+               : (mode == OVL_MODE_GEMM_ONLY ? a2a_fused_kernel<2, false> : a2a_fused_kernel<0, false>);
+  st = allow_lds(reinterpret_cast<const void*>(fk), lds);
   if (st) return st;
   int occ = 0;
-  OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &occ, (mode == OVL_MODE_GEMM_ONLY) ? a2a_fused_kernel<2> : a2a_fused_kernel<0>, kThreads, lds));
+  OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fk, kThreads, lds));
   const int64_t resident = (int64_t)std::max(occ, 1) * di.cus;
   const uint32_t req = opts ? opts->producers : 0;
 
@@ -644,10 +693,29 @@ extern "C" ovl_status a2a_dispatch_grouped_gemm_run(const a2a_desc* d, const voi
   if (Cn > kA2aXcds) Cn -= Cn % kA2aXcds;
   a.producers = P;
   a.consumers = (int32_t)Cn;
-  if (mode == OVL_MODE_FUSED)
-    hipLaunchKernelGGL(a2a_fused_kernel<0>, dim3(P + Cn), dim3(kThreads), lds, stream, a);
-  else
-    hipLaunchKernelGGL(a2a_fused_kernel<2>, dim3(Cn), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL(fk, dim3(P + Cn), dim3(kThreads), lds, stream, a);
   OVL_HIP_TRY(hipGetLastError());
   return OVL_OK;
+}
+
+}  // namespace
+}  // namespace ovl
+
+extern "C" ovl_status a2a_dispatch_grouped_gemm_run(const a2a_desc* d, const void* const* x,
+                                                    const int32_t* const* topk_idx, const void* w, void* recv_x,
+                                                    int32_t* recv_src, int32_t* recv_count, float* y,
+                                                    int64_t* flags, void* workspace, int64_t epoch,
+                                                    const ovl_opts* opts, hipStream_t stream) {
+  return a2a_run(d, false, x, nullptr, topk_idx, w, nullptr, recv_x, nullptr, recv_src, recv_count, y, flags,
+                 workspace, epoch, opts, stream);
+}
+
+extern "C" ovl_status a2a_dispatch_grouped_gemm_fp8_run(const a2a_desc* d, const void* const* x8,
+                                                        const float* const* x_scale, const int32_t* const* topk_idx,
+                                                        const void* w8, const float* w_scale, void* recv_x8,
+                                                        float* recv_scale, int32_t* recv_src, int32_t* recv_count,
+                                                        float* y, int64_t* flags, void* workspace, int64_t epoch,
+                                                        const ovl_opts* opts, hipStream_t stream) {
+  return a2a_run(d, true, x8, x_scale, topk_idx, w8, w_scale, recv_x8, recv_scale, recv_src, recv_count, y, flags,
+                 workspace, epoch, opts, stream);
 }

@@ -39,6 +39,7 @@ EXPORTS = (
     "a2a_combine_flags_bytes", "a2a_combine_workspace_bytes", "a2a_combine_run",
     "ovl_flags_reset", "ovl_check", "ovl_strerror", "ovl_copy",
     "ring_allreduce_flags_bytes", "ring_allreduce_workspace_bytes", "ring_allreduce_run",
+    "fp8_quantize_rows", "a2a_dispatch_grouped_gemm_fp8_run",
 )
 
 
@@ -138,6 +139,13 @@ def lib() -> ctypes.CDLL:
     L.ring_allreduce_run.argtypes = [POINTER(RingDesc), POINTER(c_void_p), POINTER(c_void_p), c_void_p, c_void_p,
                                      c_int64, POINTER(Opts), c_void_p]
     L.ring_allreduce_run.restype = st
+    L.fp8_quantize_rows.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p]
+    L.fp8_quantize_rows.restype = st
+    L.a2a_dispatch_grouped_gemm_fp8_run.argtypes = [POINTER(A2aDesc), POINTER(c_void_p), POINTER(c_void_p),
+                                                    POINTER(c_void_p), c_void_p, c_void_p, c_void_p, c_void_p,
+                                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
+                                                    POINTER(Opts), c_void_p]
+    L.a2a_dispatch_grouped_gemm_fp8_run.restype = st
     _lib = L
     return L
 
@@ -276,6 +284,23 @@ def a2a_dispatch_grouped_gemm_run(desc: A2aDesc, x, topk_idx, w, recv_x, recv_sr
                                              _ptr(recv_x), _ptr(recv_src), _ptr(recv_count), _ptr(y), _ptr(flags),
                                              _ptr(workspace), epoch, byref(o), _stream(stream))
     return _check(st, "a2a_dispatch_grouped_gemm_run", raise_on_error)
+
+
+def fp8_quantize_rows(in_bf16, codes, scale, rows: int, cols: int, stream=None, raise_on_error: bool = True) -> int:
+    st = lib().fp8_quantize_rows(_ptr(in_bf16), _ptr(codes), _ptr(scale), rows, cols, _stream(stream))
+    return _check(st, "fp8_quantize_rows", raise_on_error)
+
+
+def a2a_dispatch_grouped_gemm_fp8_run(desc: A2aDesc, x8, x_scale, topk_idx, w8, w_scale, recv_x8, recv_scale,
+                                      recv_src, recv_count, y, flags, workspace, epoch: int, mode: int = MODE_FUSED,
+                                      producers: int = 0, spin_limit: int = 0, stream=None,
+                                      raise_on_error: bool = True) -> int:
+    o = _opts(mode, producers, spin_limit)
+    st = lib().a2a_dispatch_grouped_gemm_fp8_run(byref(desc), _ptr_array(x8), _ptr_array(x_scale),
+                                                 _ptr_array(topk_idx), _ptr(w8), _ptr(w_scale), _ptr(recv_x8),
+                                                 _ptr(recv_scale), _ptr(recv_src), _ptr(recv_count), _ptr(y),
+                                                 _ptr(flags), _ptr(workspace), epoch, byref(o), _stream(stream))
+    return _check(st, "a2a_dispatch_grouped_gemm_fp8_run", raise_on_error)
 
 
 def a2a_combine_flags_bytes(desc: A2aDesc) -> int:

@@ -291,6 +291,41 @@ ovl_status a2a_dispatch_grouped_gemm_run(const a2a_desc* desc, const void* const
                                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * FP8 dispatch -> FP8 grouped expert GEMM.  The Aboleth README measures its
+ * compiled MoE dispatch and combine on "one FP8 layer" and fixes no format;
+ * the reading: OCP FP8 E4M3 codes (bias 7, subnormals, no infinities,
+ * largest finite 448) with one float32 scale per row.
+ *
+ * fp8_quantize_rows: bf16 [rows][cols] (uint16 bits) -> codes uint8
+ * [rows][cols] and scales float32 [rows]: for a row with amax = max |x|,
+ * scale = amax / 448 and code = E4M3(clamp(x * (448 / amax), +-448)), nearest
+ * with ties to even, both quotients in float32; a row of zeros gets scale 1
+ * and zero codes.  Used for the tokens (each source, before its dispatch)
+ * and for the expert weights, quantized as rows of W_e transposed ([n][hidden]:
+ * one scale per output column).  cols must be a multiple of 16.
+ * ---------------------------------------------------------------------- */
+ovl_status fp8_quantize_rows(const void* in_bf16, void* codes, float* scale, int64_t rows, int64_t cols,
+                             hipStream_t stream);
+
+/* As a2a_dispatch_grouped_gemm_run, with FP8 rows: x8 (HOST array[R] of
+ * uint8 [tokens][hidden] codes) and x_scale (HOST array[R] of float32
+ * [tokens]) per source; w8 uint8 [experts_per_rank][n][hidden] (W_e
+ * transposed, K contiguous) with w_scale float32 [experts_per_rank][n].
+ * The dispatch moves each row's codes to recv_x8 uint8 [R][cap][hidden] and
+ * its scale to recv_scale float32 [R][cap] (same layout, recv_src and
+ * recv_count as the bf16 call); then
+ *   y[s][j][c] = (sum_k recv_x8[s][j][k] * w8[e][c][k]) * recv_scale[s][j] * w_scale[e][c]
+ * in fp32 (MFMA sums of exact code products, K ascending in steps of 64).
+ * hidden must be a multiple of 16.  Same modes, flags, workspace
+ * (a2a_workspace_bytes) and errors as the bf16 call. */
+ovl_status a2a_dispatch_grouped_gemm_fp8_run(const a2a_desc* desc, const void* const* x8,
+                                             const float* const* x_scale, const int32_t* const* topk_idx,
+                                             const void* w8, const float* w_scale, void* recv_x8,
+                                             float* recv_scale, int32_t* recv_src, int32_t* recv_count,
+                                             float* y, int64_t* flags, void* workspace, int64_t epoch,
+                                             const ovl_opts* opts, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * MoE combine: the reverse all-to-all of the expert outputs, then the
  * gate-weighted sum back in token order (the Aboleth README's compiled MoE
  * dispatch *and combine*; the reverse all-to-all for expert-parallel MoE in
