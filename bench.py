@@ -26,6 +26,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+PEAK_FP8_TFLOPS = 5000.0  # dense MFMA fp8, published
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, published
 METRIC = "fused AG-GEMM TFLOP/s (% bf16 MFMA peak) + overlap eff. vs copy+GEMM serial"
@@ -358,6 +359,47 @@ def side_workloads(reps, flush):
                      "fused_pct_of_bf16_peak": 100 * flops / (t["median_us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
                      "fused_over_dispatch_plus_gemm": t["median_us"] / (disp["median_us"] + g["median_us"]),
                      "fused_over_gemm_only": t["median_us"] / g["median_us"]}
+    # The same dispatch in FP8: tokens quantized per row at each source (E4M3
+    # codes + a float32 scale), weights as transposed E4M3 rows with a scale
+    # per output column; the quantization is done once, outside the timing.
+    log("[bench] side a2a fp8")
+    x8, xs8 = [], []
+    for s in range(R):
+        q8 = torch.empty(cfg.tokens, cfg.hidden, dtype=torch.uint8, device="cuda")
+        sc8 = torch.empty(cfg.tokens, dtype=torch.float32, device="cuda")
+        ovl.fp8_quantize_rows(d_x[s], q8, sc8, cfg.tokens, cfg.hidden)
+        x8.append(q8)
+        xs8.append(sc8)
+    wt = d_w.view(E, cfg.hidden, cfg.n).transpose(1, 2).contiguous().view(E * cfg.n, cfg.hidden)
+    w8 = torch.empty(E * cfg.n, cfg.hidden, dtype=torch.uint8, device="cuda")
+    ws8 = torch.empty(E * cfg.n, dtype=torch.float32, device="cuda")
+    ovl.fp8_quantize_rows(wt, w8, ws8, E * cfg.n, cfg.hidden)
+    del wt
+    recv_x8 = torch.zeros(R, cap, cfg.hidden, dtype=torch.uint8, device="cuda")
+    recv_s8 = torch.zeros(R, cap, dtype=torch.float32, device="cuda")
+    y8 = torch.zeros(R, cap, cfg.n, dtype=torch.float32, device="cuda")
+
+    def a2a8(mode=0):
+        ep[0] += 1
+        ovl.a2a_dispatch_grouped_gemm_fp8_run(desc, x8, xs8, d_topk, w8, ws8, recv_x8, recv_s8, recv_src,
+                                              recv_count, y8, flags, ws, ep[0], mode=mode)
+
+    a2a8()
+    t8 = timed_reps(a2a8, reps, flush)
+    disp8 = timed_reps(lambda: a2a8(ovl.MODE_COPY_ONLY), reps, flush)
+    g8 = timed_reps(lambda: a2a8(ovl.MODE_GEMM_ONLY), reps, flush)
+    ovl.ovl_check(ws)
+    d8_bytes = uniq * (cfg.hidden + 4) + rows * (cfg.hidden + 4 + 4)  # codes + scale read; row, scale, source written
+    res["a2a_fp8_r8_t4096_h4096_e64"] = {
+        "fused_us": t8, "dispatch_only_us": disp8, "gemm_only_us": g8, "dispatch_bytes": d8_bytes,
+        "dispatch_GBps": d8_bytes / (disp8["median_us"] * 1e-6) / 1e9,
+        "gemm_only_TFLOPs": flops / (g8["median_us"] * 1e-6) / 1e12,
+        "gemm_only_pct_of_fp8_peak": 100 * flops / (g8["median_us"] * 1e-6) / 1e12 / PEAK_FP8_TFLOPS,
+        "fused_TFLOPs": flops / (t8["median_us"] * 1e-6) / 1e12,
+        "fused_over_dispatch_plus_gemm": t8["median_us"] / (disp8["median_us"] + g8["median_us"]),
+        "fused_over_gemm_only": t8["median_us"] / g8["median_us"]}
+    del x8, recv_x8, y8, w8
+
     # MoE combine at the same rank: reverse puts of y to the 7 peers, then the
     # gate-weighted sum of this rank's tokens (peers' returned rows pre-resident).
     log("[bench] side a2a combine")
