@@ -262,53 +262,68 @@ __device__ inline void mtile_at(const A2aArgs& a, const Geometry* g, int q, int*
 // ---------------------------------------------------------------- producer
 
 // Copies rows [r0, r1) of slice s: row r of the slice is token recv_src[r]
-// of source s.  Each wave takes whole rows (its first row r0 + wave, then
-// every fourth), two rows per step, each lane moving the row's 16-byte
-// vectors lane, lane + 64, ...  The loads of the next step are issued before
-// the stores of the current one, so that a wave always has a row pair in
-// flight (vector memory counters complete in order: waiting for the loads
-// then does not wait for the stores issued after them).
+// of source s.  A wave moves 8 KiB slots, two per step, each lane 16-byte
+// vectors lane, lane + 64, ... of a slot: a slot is one row (in passes, for
+// rows longer than 8 KiB), or several whole rows when rows are shorter (a
+// power-of-two count of at least 1 KiB: FP8 tokens), so that every lane
+// always has work.  The wave takes slots w, w + 4 (a pair), then w + 8, ....
+// The loads of the next step are issued before the stores of the current
+// one, so that a wave always has a slot pair in flight (vector memory
+// counters complete in order: waiting for the loads then does not wait for
+// the stores issued after them).
 __device__ inline void copy_rows(const A2aArgs& a, int s, int r0, int r1) {
-  constexpr int V = 8;  // vectors per lane per row and pass (an 8 KiB row in one pass)
+  constexpr int V = 8;  // vectors per lane per slot: 8 KiB
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int vpr = (int)(a.row_bytes / 16);
   const uint8_t* src = a.x[s];
   uint8_t* dst = a.recv_x + (int64_t)s * a.cap * a.row_bytes;
   const float* xs = a.x_scale[s];
   const int32_t* srow = a.recv_src + (int64_t)s * a.cap;
-  // Steps: (row pair, column pass); a pair is rows r, r + 4 of this wave.
-  const int passes = (vpr + 64 * V - 1) / (64 * V);
-  const int pairs = (r1 - r0 - wave + 7) / 8 > 0 ? (r1 - r0 - wave + 7) / 8 : 0;
+  // rows per slot: 64 * V / vpr for rows of 1 KiB .. 4 KiB (a power of two)
+  const bool multi = vpr >= 64 && vpr < 64 * V && (vpr & (vpr - 1)) == 0;
+  const int lg_qpr = multi ? __builtin_ctz(vpr / 64) : 0;  // log2(vectors per lane per row)
+  const int rps = multi ? (64 * V) / vpr : 1;
+  const int units = (r1 - r0 + rps - 1) / rps;
+  // Steps: (slot pair, column pass); a pair is slots u, u + 4 of this wave.
+  const int passes = multi ? 1 : (vpr + 64 * V - 1) / (64 * V);
+  const int pairs = (units - wave + 7) / 8 > 0 ? (units - wave + 7) / 8 : 0;
   const int steps = pairs * passes;
   u32x4 cur[2][V], nxt[2][V];
   auto load = [&](int st, u32x4 (&v)[2][V]) {
-    const int r = r0 + wave + (st / passes) * 8, c0 = (st % passes) * 64 * V;
+    const int u = wave + (st / passes) * 8, c0 = (st % passes) * 64 * V;
+    // every vector's source token first (all lanes read the same entries),
+    // then the data loads: one wait for the table, not one per row
+    int32_t tok[2][V];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int rr = r + 4 * h;
-      if (rr >= r1) continue;
-      const uint8_t* sp = src + (int64_t)__builtin_amdgcn_readfirstlane(srow[rr]) * a.row_bytes;
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int q = 0; q < V; ++q) {
-        const int c = c0 + q * 64 + lane;
-        if (c < vpr) v[h][q] = ld16_nt(sp + c * 16);
+        const int rr = r0 + (u + 4 * h) * rps + (multi ? q >> lg_qpr : 0);
+        tok[h][q] = rr < r1 ? srow[rr] : -1;
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int q = 0; q < V; ++q) {
+        const int c = multi ? ((q & ((1 << lg_qpr) - 1)) << 6) + lane : c0 + q * 64 + lane;
+        if (tok[h][q] < 0 || c >= vpr) continue;
+        v[h][q] = ld16_nt(src + (int64_t)tok[h][q] * a.row_bytes + c * 16);
       }
     }
   };
   auto store = [&](int st, const u32x4 (&v)[2][V]) {
-    const int r = r0 + wave + (st / passes) * 8, c0 = (st % passes) * 64 * V;
+    const int u = wave + (st / passes) * 8, c0 = (st % passes) * 64 * V;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int rr = r + 4 * h;
-      if (rr >= r1) continue;
-      uint8_t* dp = dst + (int64_t)rr * a.row_bytes;
 #pragma unroll
       for (int q = 0; q < V; ++q) {
-        const int c = c0 + q * 64 + lane;
-        if (c < vpr) st16(dp + c * 16, v[h][q]);
+        const int rr = r0 + (u + 4 * h) * rps + (multi ? q >> lg_qpr : 0);
+        const int c = multi ? ((q & ((1 << lg_qpr) - 1)) << 6) + lane : c0 + q * 64 + lane;
+        if (rr >= r1 || c >= vpr) continue;
+        st16(dst + (int64_t)rr * a.row_bytes + c * 16, v[h][q]);
+        // FP8: the row's scale travels with it (from the lane holding its first vector)
+        if (xs && c == 0) a.recv_scale[(int64_t)s * a.cap + rr] = xs[srow[rr]];
       }
-      // FP8: the row's scale travels with it (once per row, in its first pass)
-      if (xs && c0 == 0 && lane == 0) a.recv_scale[(int64_t)s * a.cap + rr] = xs[srow[rr]];
     }
   };
   if (steps > 0) load(0, cur);

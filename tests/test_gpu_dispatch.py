@@ -69,6 +69,7 @@ def _cfg(name, R=2, T=64, H=64, N=128, topk=2, E=4, rank=0, seed=3):
     _cfg("a2a_small"),
     _cfg("a2a_ragged", R=3, T=100, H=200, N=136, E=3, rank=1, seed=5),
     _cfg("a2a_skewed", R=4, T=300, H=72, N=256, E=2, rank=3, seed=8),
+    _cfg("a2a_rows_2k", R=3, T=90, H=1024, N=136, E=3, rank=1, seed=6),  # 4 rows per copy slot
 ])
 def test_small_matches_oracle(cfg):
     case = A2aCase(cfg)

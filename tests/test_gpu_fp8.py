@@ -129,6 +129,8 @@ def _cfg(name, R=2, T=64, H=64, N=128, topk=2, E=4, rank=0, seed=3):
     _cfg("f8_small"),
     _cfg("f8_ragged", R=3, T=100, H=208, N=136, E=3, rank=1, seed=5),
     _cfg("f8_skewed", R=4, T=300, H=80, N=264, E=2, rank=3, seed=8),
+    _cfg("f8_rows_1k", R=3, T=90, H=1024, N=136, E=3, rank=1, seed=6),  # 8 rows per copy slot
+    _cfg("f8_rows_2k", R=2, T=77, H=2048, N=128, E=4, rank=0, seed=7),  # 4 rows per copy slot
 ])
 def test_fp8_dispatch_and_gemm_match_oracle(cfg):
     case = Fp8Case(cfg)
