@@ -134,6 +134,37 @@ class AgBench:
             raise RuntimeError(f"device error {st} {det}")
 
 
+def trace_summary(ag, flush):
+    """One traced fused launch (cache flushed): when the copy finished, how
+    long consumers waited for flags, from the device's 100 MHz clock."""
+    import torch
+    trace = torch.zeros(ag.plan.trace_bytes // 8, dtype=torch.int64, device="cuda")
+    flush()
+    ag.epoch += 1
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    ag.ovl.ag_gemm_run(ag.plan, ag.d_shards, ag.d_b, ag.g, ag.c, ag.flags, ag.ws, ag.epoch,
+                       ag.orders[(ag.epoch - 1) % 5], trace=trace)
+    e1.record()
+    e1.synchronize()
+    ag.check()
+    tr = trace.cpu().numpy()
+    units = ag.plan.num_units
+    pub, items = tr[:units], tr[units:].reshape(-1, 4)
+    t0 = int(items[:, 0].min())
+    us = lambda ticks: float(ticks) / 100.0  # noqa: E731  (100 MHz)
+    busy = items[:, 1] - items[:, 0]
+    return {"event_us": e0.elapsed_time(e1) * 1e3,
+            "span_us": us(items[:, 1].max() - t0),
+            "last_publish_us": us(pub.max() - t0),
+            "items": int(len(items)),
+            "consumer_wait_frac": float(items[:, 2].sum() / busy.sum()),
+            "mean_wait_per_item_us": us(items[:, 2].mean()),
+            "items_that_waited": int((items[:, 2] > 0).sum()),
+            "note": "times from the first item's start; waits = wave-0 flag polling inside the tiles"}
+
+
 def cpu_baseline(cfg):
     """The oracle (gather + float64 GEMM) on the full workload, on host cores."""
     import oracle
@@ -211,6 +242,7 @@ def main():
         "copy_only_GBps": copy_bytes / (copy_only["median_us"] * 1e-6) / 1e9,
         "gemm_only_TFLOPs": cfg.flops() / (gemm_only["median_us"] * 1e-6) / 1e12,
         "fused_flushed_TFLOPs": cfg.flops() / (fused["median_us"] * 1e-6) / 1e12,
+        "trace": trace_summary(ag, flush),
     }
 
     extra = {}

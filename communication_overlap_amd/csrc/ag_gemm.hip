@@ -52,7 +52,11 @@ struct AgArgs {
   int32_t splits, split_cols, split_sync;
   float* partial;     // [splits][m][n]
   int64_t* counters;  // [tiles][2], zero between launches
+  int64_t* trace;     // optional timestamps: [num_units] publishes, then [items][4]
 };
+
+// The constant-rate (100 MHz) real-time counter, common to all compute units.
+__device__ inline int64_t now_ticks() { return (int64_t)__builtin_amdgcn_s_memrealtime(); }
 
 constexpr int kMaxSplits = 8;
 // Split-K plans run the 128x128 tile with this many LDS stages, and only
@@ -142,6 +146,7 @@ __device__ inline void move_unit(const AgArgs& a, int u) {
   const int64_t cols = min((int64_t)a.batch_cols, a.k - c0);
   copy_block(a.shards[s] + r0 * a.k + c0, a.g + ((int64_t)s * a.shard_m + r0) * a.k + c0, rows, cols, a.k);
   wg_publish(a.flags + (int64_t)u * a.flag_stride, a.epoch);
+  if (a.trace && threadIdx.x == 0) a.trace[u] = now_ticks();
 }
 
 // Moves the units at producer-order positions w, w + P, ..., skipping the
@@ -413,11 +418,14 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
           f(((int64_t)s * a.panels + p) * a.batches + bt);
       }
     };
+    const int64_t t_item = a.trace ? now_ticks() : 0;
+    int64_t waited = 0;  // ticks wave 0 spent polling for this item (traced runs)
     auto before_step = [&](int64_t, int64_t k1) {
       if (MODE != kModeFused || own || timed_out) return;
       if (threadIdx.x >= 64) return;  // wave 0 waits for the workgroup (see gemm_tile)
       const int need = (int)((k_lo + k1 - 1) / a.batch_cols);
       if (need <= ready) return;
+      const int64_t t_wait = a.trace ? now_ticks() : 0;
       const int lane = lane_id();
       for (uint64_t polls = 0;; ++polls) {
         int bad = last + 1;  // first batch with a unit not there yet (this lane's share)
@@ -459,12 +467,23 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
         __builtin_amdgcn_s_sleep(2);
       }
       wave_acquire();  // one acquire for all the units seen
+      if (a.trace) waited += now_ticks() - t_wait;
+    };
+    // Thread 0 (in wave 0, which holds `waited`) records the item.
+    auto trace_item = [&]() {
+      if (!a.trace || threadIdx.x != 0) return;
+      int64_t* rec = a.trace + a.num_units + 4 * j;
+      rec[0] = t_item;
+      rec[1] = now_ticks();
+      rec[2] = waited;
+      rec[3] = cidx;
     };
 
     Acc<BM, BN> acc;
     gemm_tile<BM, BN, 64, NS>(acc, op, m0_op, lds, before_step);
     if (NS != kSplitStages || a.splits == 1) {
       acc_store<BM, BN>(acc, a.c, a.n, m0, n0, a.m, a.n);
+      trace_item();
       continue;
     }
     acc_store<BM, BN>(acc, a.partial + (int64_t)sp * a.m * a.n, a.n, m0, n0, a.m, a.n);
@@ -486,6 +505,7 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
         __hip_atomic_store(cnt + 1, (int64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();
+      trace_item();
       continue;
     }
     if (threadIdx.x == 0) {
@@ -498,6 +518,7 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
     }
     __syncthreads();
     if (uniform(s_last)) reduce_splits<BM, BN>(a, m0, n0, 0, BM);
+    trace_item();
   }
 }
 
@@ -710,6 +731,12 @@ extern "C" size_t ag_gemm_workspace_bytes(ag_gemm_plan_t p) {
 
 extern "C" int32_t ag_gemm_splits(ag_gemm_plan_t p) { return p ? p->splits : 0; }
 
+// Publish times of the units, then four records per work item.
+extern "C" size_t ag_gemm_trace_bytes(ag_gemm_plan_t p) {
+  if (!p) return 0;
+  return 8 * ((size_t)p->num_units + 4 * (size_t)p->tiles_m * (size_t)p->tiles_n * (size_t)p->splits);
+}
+
 extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, const void* b, void* gathered,
                                   float* c, int64_t* flags, void* workspace, int64_t epoch,
                                   const int32_t* producer_order, const ovl_opts* opts, hipStream_t stream) {
@@ -735,6 +762,7 @@ extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, c
     if (reinterpret_cast<uintptr_t>(flags) & 7u) return OVL_EALIGN;
   }
   if (producer_order && (reinterpret_cast<uintptr_t>(producer_order) & 3u)) return OVL_EALIGN;
+  if (opts && opts->trace && (reinterpret_cast<uintptr_t>(opts->trace) & 7u)) return OVL_EALIGN;
 
   DeviceInfo di;
   ovl_status st = current_device_info(&di);
@@ -748,6 +776,7 @@ extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, c
   a.flags = flags;
   a.err = static_cast<ErrRec*>(workspace);
   a.order = producer_order;
+  a.trace = opts ? opts->trace : nullptr;
   a.shard_m = d.shard_m;
   a.m = p->m;
   a.k = d.k;

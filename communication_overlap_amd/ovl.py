@@ -39,7 +39,7 @@ EXPORTS = (
     "a2a_combine_flags_bytes", "a2a_combine_workspace_bytes", "a2a_combine_run",
     "ovl_flags_reset", "ovl_check", "ovl_strerror", "ovl_copy",
     "ring_allreduce_flags_bytes", "ring_allreduce_workspace_bytes", "ring_allreduce_run",
-    "fp8_quantize_rows", "a2a_dispatch_grouped_gemm_fp8_run",
+    "fp8_quantize_rows", "a2a_dispatch_grouped_gemm_fp8_run", "ag_gemm_trace_bytes",
 )
 
 
@@ -50,7 +50,7 @@ class OvlError(RuntimeError):
 
 
 class Opts(Structure):
-    _fields_ = [("mode", c_uint32), ("producers", c_uint32), ("spin_limit", c_uint64)]
+    _fields_ = [("mode", c_uint32), ("producers", c_uint32), ("spin_limit", c_uint64), ("trace", c_void_p)]
 
 
 class AgGemmDesc(Structure):
@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.ag_gemm_workspace_bytes.restype = c_size_t
     L.ag_gemm_splits.argtypes = [c_void_p]
     L.ag_gemm_splits.restype = c_int32
+    L.ag_gemm_trace_bytes.argtypes = [c_void_p]
+    L.ag_gemm_trace_bytes.restype = c_size_t
     L.ag_gemm_run.argtypes = [c_void_p, POINTER(c_void_p), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                               c_int64, c_void_p, POINTER(Opts), c_void_p]
     L.ag_gemm_run.restype = st
@@ -174,8 +176,8 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
-def _opts(mode: int, producers: int, spin_limit: int) -> Opts:
-    return Opts(mode, producers, spin_limit)
+def _opts(mode: int, producers: int, spin_limit: int, trace=None) -> Opts:
+    return Opts(mode, producers, spin_limit, _ptr(trace))
 
 
 def _check(status: int, where: str, raise_on_error: bool) -> int:
@@ -224,6 +226,10 @@ class AgGemmPlan:
     def splits(self) -> int:
         return lib().ag_gemm_splits(self.handle)
 
+    @property
+    def trace_bytes(self) -> int:
+        return lib().ag_gemm_trace_bytes(self.handle)
+
 
 def ag_gemm_plan(*args, **kw) -> AgGemmPlan:
     return AgGemmPlan(*args, **kw)
@@ -231,9 +237,9 @@ def ag_gemm_plan(*args, **kw) -> AgGemmPlan:
 
 def ag_gemm_run(plan: AgGemmPlan, shards, b, gathered, c, flags, workspace, epoch: int, producer_order=None,
                 mode: int = MODE_FUSED, producers: int = 0, spin_limit: int = 0, stream=None,
-                raise_on_error: bool = True) -> int:
+                raise_on_error: bool = True, trace=None) -> int:
     arr = _ptr_array(shards)
-    o = _opts(mode, producers, spin_limit)
+    o = _opts(mode, producers, spin_limit, trace)
     st = lib().ag_gemm_run(plan.handle, arr, _ptr(b), _ptr(gathered), _ptr(c), _ptr(flags), _ptr(workspace),
                            epoch, _ptr(producer_order), byref(o), _stream(stream))
     return _check(st, "ag_gemm_run", raise_on_error)

@@ -85,6 +85,8 @@ typedef struct ovl_opts {
   uint32_t mode;        /* OVL_MODE_* */
   uint32_t producers;   /* producer workgroups; 0 = library default */
   uint64_t spin_limit;  /* polls before a wait gives up (OVL_ETIMEOUT); 0 = default (~2^22) */
+  int64_t* trace;       /* AG-GEMM only: device buffer of ag_gemm_trace_bytes() bytes that the
+                           run fills with timestamps (see there), or NULL for none */
 } ovl_opts;
 
 /* Size in bytes of the device-side error record at the start of every
@@ -170,6 +172,18 @@ int32_t ag_gemm_splits(ag_gemm_plan_t plan);
  * unit index out of range. */
 ovl_status ag_gemm_consumer_order(ag_gemm_plan_t plan, const int32_t* producer_order, int32_t* out);
 
+/* Device trace of a run (the pages ask to profile overlap efficiency and
+ * synchronisation bottlenecks: "Triton-distributed Semantics", Best
+ * Practices).  int64 records, times from the constant 100 MHz real-time
+ * counter (s_memrealtime, 10 ns ticks), common to all compute units:
+ *   [u], u < num_units:    the time unit u's flag was published (0: not moved);
+ *   [num_units + 4 j + 0]: work item j's start (j = tile * splits + range, in
+ *                          the launch's item order), [+1] its end (after its
+ *                          stores), [+2] ticks its workgroup spent waiting for
+ *                          flags, [+3] the consumer index that ran it.
+ * Items of BARRIER and GEMM_ONLY runs record no waits. */
+size_t ag_gemm_trace_bytes(ag_gemm_plan_t plan);
+
 /* shards:   HOST array of R device pointers, bf16 [shard_m][k] each (read only).
  * b:        bf16 [k][n] (read only).
  * gathered: bf16 [R*shard_m][k], written by the producer (bit-exact copy).
@@ -181,7 +195,8 @@ ovl_status ag_gemm_consumer_order(ag_gemm_plan_t plan, const int32_t* producer_o
  *           ascending.  Entries outside [0, num_units) are skipped; a unit
  *           that never appears is never moved, and waits on it end in
  *           OVL_ETIMEOUT.
- * opts:     NULL = FUSED with defaults.
+ * opts:     NULL = FUSED with defaults; opts->trace: see ag_gemm_trace_bytes
+ *           (8-byte aligned).
  * In GEMM_ONLY mode `gathered` must already hold the gathered operand and
  * neither flags nor shards other than the own one are read. */
 ovl_status ag_gemm_run(ag_gemm_plan_t plan, const void* const* shards, const void* b,

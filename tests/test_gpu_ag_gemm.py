@@ -257,3 +257,57 @@ def test_full_size_small_integers_exact():
     st, det = case.run(1, case.order(1))
     assert st == 0, det
     _sampled_check(case, count=3000, exact=True)
+
+
+# ------------------------------------------------------------------ device trace
+
+def test_trace_records_publishes_and_waits_in_causal_order():
+    """A traced run gives the same bits as an untraced one, and its records
+    hold together: every unit is published, every item ends after it starts
+    and after the publish of every unit its rows and K range need, and its
+    waits fit inside it."""
+    import ctypes
+    import torch
+    o = ovl()
+    cfg = _small("ag_trace", 4, 256, 512, 2048, 256, 256, seed=9)
+    case = AgCase(cfg, tiles_per_flag=1)
+    plan = case.plan
+    assert plan.splits == 1  # enough tiles for the consumers: one item per tile
+    order = case.order(1, "units")
+    assert case.run(1, order)[0] == 0
+    c_plain = host(case.c).copy()
+    trace = torch.zeros(plan.trace_bytes // 8, dtype=torch.int64, device="cuda")
+    case.c.zero_()
+    case.g.zero_()
+    say("  traced run")
+    o.ag_gemm_run(plan, case.d_shards, case.d_b, case.g, case.c, case.flags, case.ws, 2, dev(order), trace=trace)
+    st, det = o.ovl_check(case.ws, raise_on_error=False)
+    assert st == 0, det
+    assert np.array_equal(host(case.c).view(np.uint32), c_plain.view(np.uint32))
+    tr = host(trace)
+    units = plan.num_units
+    pub = tr[:units]
+    items = tr[units:].reshape(-1, 4)
+    assert np.all(pub > 0), "a unit without a publish time"
+    assert np.all(items[:, 0] > 0) and np.all(items[:, 1] >= items[:, 0])
+    assert np.all((items[:, 2] >= 0) & (items[:, 2] <= items[:, 1] - items[:, 0]))
+    # consumer order (host copy of the device rule) -> each item's row tile
+    lib = o.lib()
+    lib.ag_gemm_row_tiles.argtypes = [ctypes.c_void_p]
+    lib.ag_gemm_row_tiles.restype = ctypes.c_int32
+    lib.ag_gemm_consumer_order.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ag_gemm_consumer_order.restype = ctypes.c_int32
+    row_tiles = lib.ag_gemm_row_tiles(plan.handle.value)
+    bm = cfg.m // row_tiles
+    tiles_n = len(items) // row_tiles
+    o32 = np.ascontiguousarray(order.astype(np.int32))
+    sorted_rt = np.zeros(row_tiles, dtype=np.int32)
+    assert lib.ag_gemm_consumer_order(plan.handle.value, o32.ctypes.data, sorted_rt.ctypes.data) == 0
+    for j, rec in enumerate(items):
+        rt = int(sorted_rt[j // tiles_n])
+        s = rt * bm // cfg.shard_m  # the shard holding the tile's rows (one panel per shard here)
+        if s == 0:  # the own shard: nothing to wait for
+            assert rec[2] == 0
+            continue
+        need = [s * case.batches + bt for bt in range(case.batches)]
+        assert pub[need].max() <= rec[1], f"item {j} ended before its units were published"
