@@ -52,11 +52,14 @@ struct AgArgs {
   int32_t splits, split_cols, split_sync;
   float* partial;     // [splits][m][n]
   int64_t* counters;  // [tiles][2], zero between launches
-  int64_t* trace;     // optional timestamps: [num_units] publishes, then [items][4]
+  int64_t* trace;     // optional timestamps: [num_units] publishes, then [items][kTraceItem]
 };
 
 // The constant-rate (100 MHz) real-time counter, common to all compute units.
 __device__ inline int64_t now_ticks() { return (int64_t)__builtin_amdgcn_s_memrealtime(); }
+// The shader-clock cycle counter (its rate is the actual clock).
+__device__ inline int64_t now_cycles() { return (int64_t)__builtin_amdgcn_s_memtime(); }
+constexpr int kTraceItem = 6;  // int64 per traced work item
 
 constexpr int kMaxSplits = 8;
 // Split-K plans run the 128x128 tile with this many LDS stages, and only
@@ -419,6 +422,7 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
       }
     };
     const int64_t t_item = a.trace ? now_ticks() : 0;
+    const int64_t c_item = a.trace ? now_cycles() : 0;
     int64_t waited = 0;  // ticks wave 0 spent polling for this item (traced runs)
     auto before_step = [&](int64_t, int64_t k1) {
       if (MODE != kModeFused || own || timed_out) return;
@@ -472,11 +476,13 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
     // Thread 0 (in wave 0, which holds `waited`) records the item.
     auto trace_item = [&]() {
       if (!a.trace || threadIdx.x != 0) return;
-      int64_t* rec = a.trace + a.num_units + 4 * j;
+      int64_t* rec = a.trace + a.num_units + kTraceItem * j;
       rec[0] = t_item;
       rec[1] = now_ticks();
       rec[2] = waited;
       rec[3] = cidx;
+      rec[4] = c_item;
+      rec[5] = now_cycles();
     };
 
     Acc<BM, BN> acc;
@@ -734,7 +740,7 @@ extern "C" int32_t ag_gemm_splits(ag_gemm_plan_t p) { return p ? p->splits : 0; 
 // Publish times of the units, then four records per work item.
 extern "C" size_t ag_gemm_trace_bytes(ag_gemm_plan_t p) {
   if (!p) return 0;
-  return 8 * ((size_t)p->num_units + 4 * (size_t)p->tiles_m * (size_t)p->tiles_n * (size_t)p->splits);
+  return 8 * ((size_t)p->num_units + kTraceItem * (size_t)p->tiles_m * (size_t)p->tiles_n * (size_t)p->splits);
 }
 
 extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, const void* b, void* gathered,

@@ -177,10 +177,13 @@ ovl_status ag_gemm_consumer_order(ag_gemm_plan_t plan, const int32_t* producer_o
  * Practices).  int64 records, times from the constant 100 MHz real-time
  * counter (s_memrealtime, 10 ns ticks), common to all compute units:
  *   [u], u < num_units:    the time unit u's flag was published (0: not moved);
- *   [num_units + 4 j + 0]: work item j's start (j = tile * splits + range, in
+ *   [num_units + 6 j + 0]: work item j's start (j = tile * splits + range, in
  *                          the launch's item order), [+1] its end (after its
  *                          stores), [+2] ticks its workgroup spent waiting for
- *                          flags, [+3] the consumer index that ran it.
+ *                          flags, [+3] the consumer index that ran it, [+4] and
+ *                          [+5] the shader-clock cycle counter (s_memtime) at
+ *                          its start and end (their rate over the ticks is the
+ *                          clock the item ran at).
  * Items of BARRIER and GEMM_ONLY runs record no waits. */
 size_t ag_gemm_trace_bytes(ag_gemm_plan_t plan);
 

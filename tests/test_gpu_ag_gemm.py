@@ -287,10 +287,13 @@ def test_trace_records_publishes_and_waits_in_causal_order():
     tr = host(trace)
     units = plan.num_units
     pub = tr[:units]
-    items = tr[units:].reshape(-1, 4)
+    items = tr[units:].reshape(-1, 6)
     assert np.all(pub > 0), "a unit without a publish time"
     assert np.all(items[:, 0] > 0) and np.all(items[:, 1] >= items[:, 0])
     assert np.all((items[:, 2] >= 0) & (items[:, 2] <= items[:, 1] - items[:, 0]))
+    # the shader clock over the 100 MHz ticks: a plausible clock (0.5 to 3 GHz)
+    ghz = (items[:, 5] - items[:, 4]).sum() / ((items[:, 1] - items[:, 0]).sum() * 10.0)
+    assert 0.5 < ghz < 3.0, ghz
     # consumer order (host copy of the device rule) -> each item's row tile
     lib = o.lib()
     lib.ag_gemm_row_tiles.argtypes = [ctypes.c_void_p]
