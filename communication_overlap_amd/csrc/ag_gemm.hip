@@ -69,6 +69,12 @@ constexpr int kSplitStages = 4;
 
 enum { kModeFused = 0, kModeBarrier = 1, kModeGemmOnly = 2 };
 
+// Wavefronts per workgroup of the fused kernel: 256 x 256 tiles run 8 (a
+// 2 x 4 grid, two waves per SIMD: one's MFMAs cover the other's LDS reads;
+// measured faster than 4), 128 x 128 tiles 4.
+constexpr int ag_waves(int bm) { return bm == 256 ? 8 : 4; }
+constexpr int kMaxWaves = 8;
+
 // ---------------------------------------------------------------- producer
 
 // Copies rows x cols bf16 (cols a multiple of 8) between two row-major
@@ -78,14 +84,15 @@ enum { kModeFused = 0, kModeBarrier = 1, kModeGemmOnly = 2 };
 // of block i, so that a lane always has a block in flight (vector memory
 // counters complete in order: waiting for the loads does not wait for the
 // stores issued after them).
+template <int NT>
 __device__ inline void copy_block(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int64_t rows,
                                   int64_t cols, int64_t ld) {
   constexpr int U = 8;
   const uint32_t vpr = (uint32_t)(cols / 8);
   const uint32_t total = (uint32_t)(rows * vpr);
-  const uint32_t step_r = kThreads / vpr, step_c = kThreads % vpr;
+  const uint32_t step_r = NT / vpr, step_c = NT % vpr;
   uint32_t r = threadIdx.x / vpr, c = threadIdx.x % vpr;  // next vector to load
-  const uint32_t blocks = (total + kThreads * U - 1) / (kThreads * U);
+  const uint32_t blocks = (total + NT * U - 1) / (NT * U);
   struct Blk {
     u32x4 v[U];
     uint32_t off[U];  // element offset, or ~0u past the end
@@ -93,7 +100,7 @@ __device__ inline void copy_block(const uint16_t* __restrict__ src, uint16_t* __
   auto load = [&](uint32_t bi, Blk& b) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const bool in = bi * kThreads * U + j * kThreads + threadIdx.x < total;
+      const bool in = bi * NT * U + j * NT + threadIdx.x < total;
       b.off[j] = in ? r * (uint32_t)ld + c * 8 : ~0u;
       if (in) b.v[j] = ld16_nt(src + b.off[j]);
       c += step_c;
@@ -137,7 +144,9 @@ struct Sched {
 
 constexpr int kBootBits = 2048 * 32;  // presence bitmap: n_boot * batches <= this
 
-// Copies one flag unit into the gathered buffer and publishes its flag.
+// Copies one flag unit into the gathered buffer and publishes its flag (NT
+// threads per workgroup).
+template <int NT>
 __device__ inline void move_unit(const AgArgs& a, int u) {
   const int bt = u % a.batches;
   const int sp = u / a.batches;
@@ -147,34 +156,36 @@ __device__ inline void move_unit(const AgArgs& a, int u) {
   const int64_t rows = min((int64_t)a.unit_rows, a.shard_m - r0);
   const int64_t c0 = (int64_t)bt * a.batch_cols;
   const int64_t cols = min((int64_t)a.batch_cols, a.k - c0);
-  copy_block(a.shards[s] + r0 * a.k + c0, a.g + ((int64_t)s * a.shard_m + r0) * a.k + c0, rows, cols, a.k);
+  copy_block<NT>(a.shards[s] + r0 * a.k + c0, a.g + ((int64_t)s * a.shard_m + r0) * a.k + c0, rows, cols, a.k);
   wg_publish(a.flags + (int64_t)u * a.flag_stride, a.epoch);
   if (a.trace && threadIdx.x == 0) a.trace[u] = now_ticks();
 }
 
 // Moves the units at producer-order positions w, w + P, ..., skipping the
 // bootstrap panels' units when sc is given (those were moved already).
+template <int NT>
 __device__ inline void produce(const AgArgs& a, int w, int P, const Sched* sc) {
   for (int i = w; i < a.num_units; i += P) {
     const int u = uniform(a.order ? a.order[i] : i);
     if (u < 0 || u >= a.num_units) continue;  // not a unit index: nothing to move
     if (sc && uniform(sc->bidx[u / a.batches]) >= 0) continue;
-    move_unit(a, u);
+    move_unit<NT>(a, u);
   }
 }
 
 // Bootstrap: workgroup w of G moves the bootstrap units number w, w + G, ...
 // (every K-batch of every bootstrap panel, panel-major) that occur in the
 // producer order; a unit the order omits stays unmoved.
+template <int NT>
 __device__ inline void produce_boot(const AgArgs& a, int w, int G, const Sched& sc) {
   const int items = sc.n_boot * a.batches;
   for (int i = w; i < items; i += G)
     if (uniform((sc.present[i >> 5] >> (i & 31)) & 1u))
-      move_unit(a, uniform(sc.boot[i / a.batches]) * a.batches + i % a.batches);
+      move_unit<NT>(a, uniform(sc.boot[i / a.batches]) * a.batches + i % a.batches);
 }
 
 __global__ __launch_bounds__(kThreads) void ag_produce_kernel(AgArgs a) {
-  produce(a, blockIdx.x, gridDim.x, nullptr);
+  produce<kThreads>(a, blockIdx.x, gridDim.x, nullptr);
 }
 
 // ---------------------------------------------------------------- consumer order
@@ -213,7 +224,7 @@ constexpr int kBootTabBytes = (3 * kMaxRowTiles + kBootBits / 32) * (int)sizeof(
 // table, and keeps only as many panels as the presence bitmap holds.
 __device__ Sched build_schedule(const AgArgs& a, int BM, int* sorted, int* tab, bool with_boot) {
   __shared__ int s_nboot;
-  __shared__ int s_wave[kThreads / 64];
+  __shared__ int s_wave[kMaxWaves];
   int* key = tab;  // reused as bidx once the order is known
   int* pos = tab + kMaxRowTiles;
   int* boot = pos + kMaxRowTiles;
@@ -269,7 +280,7 @@ __device__ Sched build_schedule(const AgArgs& a, int BM, int* sorted, int* tab, 
       __syncthreads();
       if (threadIdx.x == 0) {
         int t = 0;
-        for (int q = 0; q < kThreads / 64; ++q) t += s_wave[q];
+        for (int q = 0; q < (int)(blockDim.x / 64); ++q) t += s_wave[q];
         s_nboot = min(s_nboot + t, cap);
       }
       __syncthreads();
@@ -305,10 +316,10 @@ __device__ Sched build_schedule(const AgArgs& a, int BM, int* sorted, int* tab, 
 // Tile rows [lo, hi) of a split tile: C = ((P_0 + P_1) + ...) over the
 // partial products in range order, 16 bytes per lane, two row groups of
 // every partial loaded before the first add.
-template <int BM, int BN>
+template <int BM, int BN, int NT>
 __device__ void reduce_splits(const AgArgs& a, int64_t m0, int64_t n0, int64_t lo, int64_t hi) {
   constexpr int VPR = BN / 4;           // 16-byte vectors per tile row
-  constexpr int RPP = kThreads / VPR;   // rows per pass
+  constexpr int RPP = NT / VPR;         // rows per pass
   constexpr int U = 2;
   const int64_t rows = min(hi, a.m - m0);
   const int64_t cols = min((int64_t)BN, a.n - n0);
@@ -339,7 +350,7 @@ __device__ void reduce_splits(const AgArgs& a, int64_t m0, int64_t n0, int64_t l
   }
 }
 
-template <int BM, int BN, int NS, int MODE>
+template <int BM, int BN, int NS, int NW, int MODE>
 __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* lds) {
 
   bool timed_out = false;
@@ -485,14 +496,14 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
       rec[5] = now_cycles();
     };
 
-    Acc<BM, BN> acc;
-    gemm_tile<BM, BN, 64, NS>(acc, op, m0_op, lds, before_step);
+    Acc<BM, BN, NW> acc;
+    gemm_tile<BM, BN, 64, NS, false, NW>(acc, op, m0_op, lds, before_step);
     if (NS != kSplitStages || a.splits == 1) {
-      acc_store<BM, BN>(acc, a.c, a.n, m0, n0, a.m, a.n);
+      acc_store<BM, BN, 0, NW>(acc, a.c, a.n, m0, n0, a.m, a.n);
       trace_item();
       continue;
     }
-    acc_store<BM, BN>(acc, a.partial + (int64_t)sp * a.m * a.n, a.n, m0, n0, a.m, a.n);
+    acc_store<BM, BN, 0, NW>(acc, a.partial + (int64_t)sp * a.m * a.n, a.n, m0, n0, a.m, a.n);
     int64_t* cnt = a.counters + 2 * tl;
     const int64_t before = wg_arrive(cnt);  // releases this range's partial
     if (a.split_sync) {
@@ -503,7 +514,7 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
       }
       __syncthreads();
       const int64_t rs = (BM + a.splits - 1) / a.splits;
-      reduce_splits<BM, BN>(a, m0, n0, sp * rs, min((int64_t)BM, (sp + 1) * rs));
+      reduce_splits<BM, BN, 64 * NW>(a, m0, n0, sp * rs, min((int64_t)BM, (sp + 1) * rs));
       // The last range out returns both counters to zero for the next launch.
       const int64_t out = wg_arrive(cnt + 1);
       if (threadIdx.x == 0 && out == a.splits - 1) {
@@ -523,7 +534,7 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
       s_last = last;
     }
     __syncthreads();
-    if (uniform(s_last)) reduce_splits<BM, BN>(a, m0, n0, 0, BM);
+    if (uniform(s_last)) reduce_splits<BM, BN, 64 * NW>(a, m0, n0, 0, BM);
     trace_item();
   }
 }
@@ -534,19 +545,20 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
 // chip copies what is needed first); then producers move the remaining units
 // in the caller's order while consumers compute.
 template <int BM, int BN, int NS, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void ag_gemm_kernel(AgArgs a) {
+__global__ __launch_bounds__(64 * ag_waves(BM), 1) void ag_gemm_kernel(AgArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
-  using C = TileCfg<BM, BN, 64, NS>;
+  constexpr int NW = ag_waves(BM);
+  using C = TileCfg<BM, BN, 64, NS, NW>;
   static_assert(kBootTabBytes <= C::LDS_BYTES, "bootstrap tables alias the stage area");
   int* sorted = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(lds) + C::LDS_BYTES);
   const Sched sc = build_schedule(a, BM, sorted, reinterpret_cast<int*>(lds), MODE != kModeGemmOnly);
-  if (MODE != kModeGemmOnly) produce_boot(a, blockIdx.x, gridDim.x, sc);
+  if (MODE != kModeGemmOnly) produce_boot<64 * NW>(a, blockIdx.x, gridDim.x, sc);
   if ((int)blockIdx.x < a.producers) {
-    produce(a, blockIdx.x, a.producers, &sc);
+    produce<64 * NW>(a, blockIdx.x, a.producers, &sc);
     return;
   }
   __syncthreads();  // every read of the bootstrap tables is done: the stages may be written
-  consume<BM, BN, NS, MODE>(a, (int)blockIdx.x - a.producers, sc.sorted, lds);
+  consume<BM, BN, NS, NW, MODE>(a, (int)blockIdx.x - a.producers, sc.sorted, lds);
 }
 
 template <int BM, int BN, int NS>
@@ -576,8 +588,8 @@ ovl_status launch_fused(const AgArgs& a, hipStream_t stream) {
   const int lds = ag_lds_bytes<BM, BN, NS>();
   ovl_status st = allow_lds(fn, lds);
   if (st) return st;
-  hipLaunchKernelGGL((ag_gemm_kernel<BM, BN, NS, MODE>), dim3(a.producers + a.consumers), dim3(kThreads), lds,
-                     stream, a);
+  hipLaunchKernelGGL((ag_gemm_kernel<BM, BN, NS, MODE>), dim3(a.producers + a.consumers), dim3(64 * ag_waves(BM)),
+                     lds, stream, a);
   OVL_HIP_TRY(hipGetLastError());
   return OVL_OK;
 }
@@ -588,7 +600,7 @@ ovl_status occupancy(int* out) {
   ovl_status st = allow_lds(reinterpret_cast<const void*>(&ag_gemm_kernel<BM, BN, NS, kModeFused>), lds);
   if (st) return st;
   OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(out, ag_gemm_kernel<BM, BN, NS, kModeFused>,
-                                                           kThreads, lds));
+                                                           64 * ag_waves(BM), lds));
   return OVL_OK;
 }
 

@@ -1,8 +1,9 @@
 // bf16 x bf16 -> fp32 tile GEMM on gfx950 matrix cores.
 //
-// One workgroup of 4 wavefronts computes a BM x BN output tile; the waves
-// form a 2 x 2 grid, each owning a (BM/2) x (BN/2) sub-tile made of 32 x 32
-// blocks computed with v_mfma_f32_32x32x16_bf16.  K advances in steps of BK
+// One workgroup of NW = 4 or 8 wavefronts computes a BM x BN output tile; the
+// waves form a 2 x (NW/2) grid, each owning a (BM/2) x (2*BN/NW) sub-tile made
+// of 32 x 32 blocks computed with v_mfma_f32_32x32x16_bf16 (8 waves: half the
+// accumulators per wave, two waves per SIMD to hide each other's LDS reads).  K advances in steps of BK
 // through a ring of NS LDS stages (BK = 32: 4 stages, the loads of a step
 // issued three steps ahead; BK = 64: 2 stages, one step ahead).
 //
@@ -99,29 +100,31 @@ __device__ inline uint32_t swz_b(uint32_t k) { return (0xCA60u >> ((k & 3) * 4))
 
 // NSTAGES: LDS ring depth (0: 4 for BK 32, 2 for BK 64).  Deeper rings keep
 // more loads in flight for bandwidth-bound (skinny) tiles.
-template <int BM, int BN, int BK = 64, int NSTAGES = 0>
+template <int BM, int BN, int BK = 64, int NSTAGES = 0, int NW = 4>
 struct TileCfg {
   static_assert(BM % 64 == 0 && BN % 128 == 0 && BN <= 256 && BM <= 256, "tile shape");
   static_assert(BK == 32 || BK == 64, "K step");
   static constexpr int NS = NSTAGES ? NSTAGES : (BK == 32 ? 4 : 2);  // LDS stages
+  static_assert(NW == 4 || NW == 8, "waves per workgroup: a 2 x 2 or 2 x 4 grid");
+  static constexpr int WN = NW / 2;              // waves along N
   static constexpr int FM = BM / 64;             // 32-row blocks per wave
-  static constexpr int FN = BN / 64;             // 32-col blocks per wave
+  static constexpr int FN = BN / (32 * WN);      // 32-col blocks per wave
   static constexpr int KK = BK / 16;             // MFMA sub-steps per stage
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int B_BYTES = BN * BK * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = NS * STAGE_BYTES;
   static constexpr int A_RPI = 1024 / (BK * 2);  // A rows per load instruction
-  static constexpr int QA = BM / A_RPI / 4;      // A load instructions per wave per stage
+  static constexpr int QA = BM / A_RPI / NW;     // A load instructions per wave per stage
   static constexpr int B_LPR = BN / 8;           // lanes per B row in one instruction
   static constexpr int B_RPI = 64 / B_LPR;       // B rows per instruction
-  static constexpr int QB = BK / B_RPI / 4;      // B load instructions per wave per stage
+  static constexpr int QB = BK / B_RPI / NW;     // B load instructions per wave per stage
   static constexpr int LPS = QA + QB;            // load instructions per wave per stage
 };
 
-template <int BM, int BN>
+template <int BM, int BN, int NW = 4>
 struct Acc {
-  f32x16 v[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN];
+  f32x16 v[TileCfg<BM, BN, 64, 0, NW>::FM][TileCfg<BM, BN, 64, 0, NW>::FN];
 };
 
 // Operand view for one tile: A rows [0, m_valid) at a (row pitch lda),
@@ -142,12 +145,12 @@ struct Operands {
 
 // Per-tile, per-lane addressing of the global -> LDS loads.  IND: A rows
 // come from a row table, so every A instruction keeps its own offset.
-template <int BM, int BN, int BK, bool IND = false>
+template <int BM, int BN, int BK, bool IND = false, int NW = 4>
 struct TileAddr {
   u32x4 ra, rb;
   // Direct: lane offset of A instructions with index parity 0 / 1 at k0 = 0
   // (bytes).  IND: lane offset of each A instruction, or kOOB for no row.
-  uint32_t a_off[IND ? TileCfg<BM, BN, BK>::QA : 2];
+  uint32_t a_off[IND ? TileCfg<BM, BN, BK, 0, NW>::QA : 2];
   uint32_t a_kc[2];    // lane's K column (elements) for A instructions of index parity 0 / 1
   uint32_t a_qstep;    // direct: bytes between consecutive A instructions
   uint32_t b_off[2];   // lane offset of B instructions with index parity 0 / 1 at k0 = 0, or kOOB past N
@@ -156,10 +159,10 @@ struct TileAddr {
   int32_t k;
 };
 
-template <int BM, int BN, int BK, bool IND = false>
-__device__ inline TileAddr<BM, BN, BK, IND> tile_addr(const Operands& op, int64_t m0) {
-  using C = TileCfg<BM, BN, BK>;
-  TileAddr<BM, BN, BK, IND> t;
+template <int BM, int BN, int BK, bool IND = false, int NW = 4>
+__device__ inline TileAddr<BM, BN, BK, IND, NW> tile_addr(const Operands& op, int64_t m0) {
+  using C = TileCfg<BM, BN, BK, 0, NW>;
+  TileAddr<BM, BN, BK, IND, NW> t;
   const uint32_t l = lane_id();
   const uint32_t w = threadIdx.x >> 6;
   t.ra = make_srd(op.a + m0 * op.lda, (op.m_valid - m0) * op.lda * 2);
@@ -199,8 +202,8 @@ __device__ inline TileAddr<BM, BN, BK, IND> tile_addr(const Operands& op, int64_
 
 // Buffer offset of A instruction q of the K-step at k0 (kOOB past K, or for
 // a row the table leaves out: kOOB + 2 * k0 is still past every buffer).
-template <int BM, int BN, int BK, bool IND>
-__device__ inline uint32_t a_offset(const TileAddr<BM, BN, BK, IND>& t, int q, int32_t k0) {
+template <int BM, int BN, int BK, bool IND, int NW>
+__device__ inline uint32_t a_offset(const TileAddr<BM, BN, BK, IND, NW>& t, int q, int32_t k0) {
   const int par = q & 1;
   if (k0 + (int32_t)t.a_kc[par] >= t.k) return kOOB;
   if constexpr (IND)
@@ -213,17 +216,17 @@ __device__ inline uint32_t a_offset(const TileAddr<BM, BN, BK, IND>& t, int q, i
 // the A part and the B part separately, so that each can sit under MFMAs.
 // The swizzle of an instruction's rows depends on the instruction index only
 // through its parity (even QA / QB and row counts), hence the two variants.
-template <int BM, int BN, int BK, bool IND>
-__device__ inline void stage_issue_a(const TileAddr<BM, BN, BK, IND>& t, uint32_t stage, int32_t k0) {
-  using C = TileCfg<BM, BN, BK>;
+template <int BM, int BN, int BK, bool IND, int NW>
+__device__ inline void stage_issue_a(const TileAddr<BM, BN, BK, IND, NW>& t, uint32_t stage, int32_t k0) {
+  using C = TileCfg<BM, BN, BK, 0, NW>;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int q = 0; q < C::QA; ++q) load_to_lds(t.ra, stage + (w * C::QA + q) * 1024, a_offset(t, q, k0));
 }
 
-template <int BM, int BN, int BK, bool IND>
-__device__ inline void stage_issue_b(const TileAddr<BM, BN, BK, IND>& t, uint32_t stage, int32_t k0) {
-  using C = TileCfg<BM, BN, BK>;
+template <int BM, int BN, int BK, bool IND, int NW>
+__device__ inline void stage_issue_b(const TileAddr<BM, BN, BK, IND, NW>& t, uint32_t stage, int32_t k0) {
+  using C = TileCfg<BM, BN, BK, 0, NW>;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t sb = stage + C::A_BYTES;
   const uint32_t kb = (uint32_t)k0 * t.ldb_b;
@@ -236,9 +239,9 @@ __device__ inline void stage_issue_b(const TileAddr<BM, BN, BK, IND>& t, uint32_
 
 // One load instruction of a stage: q < QA is A instruction q, otherwise B
 // instruction q - QA.
-template <int BM, int BN, int BK, bool IND, int Q>
-__device__ inline void stage_issue_one(const TileAddr<BM, BN, BK, IND>& t, uint32_t stage, int32_t k0) {
-  using C = TileCfg<BM, BN, BK>;
+template <int BM, int BN, int BK, bool IND, int NW, int Q>
+__device__ inline void stage_issue_one(const TileAddr<BM, BN, BK, IND, NW>& t, uint32_t stage, int32_t k0) {
+  using C = TileCfg<BM, BN, BK, 0, NW>;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if constexpr (Q < C::QA) {
     load_to_lds(t.ra, stage + (w * C::QA + Q) * 1024, a_offset(t, Q, k0));
@@ -251,33 +254,33 @@ __device__ inline void stage_issue_one(const TileAddr<BM, BN, BK, IND>& t, uint3
 
 // The loads of one stage, to be spread over the MFMA groups of the step
 // before (on == false: nothing to load).
-template <int BM, int BN, int BK, bool IND>
+template <int BM, int BN, int BK, bool IND, int NW>
 struct Prefetch {
-  const TileAddr<BM, BN, BK, IND>* t;
+  const TileAddr<BM, BN, BK, IND, NW>* t;
   uint32_t slot;
   int32_t k0;
   bool on;
   template <int Q>
   __device__ inline void issue() const {
-    if (on) stage_issue_one<BM, BN, BK, IND, Q>(*t, slot, k0);
+    if (on) stage_issue_one<BM, BN, BK, IND, NW, Q>(*t, slot, k0);
   }
 };
 
 // Per-lane LDS read offsets (bytes, within a stage) of the MFMA fragments.
-template <int BM, int BN, int BK>
+template <int BM, int BN, int BK, int NW>
 struct FragAddr {
   uint32_t a[BK / 16];               // A fragment of sub-step kk (add fm * 32 rows)
-  uint32_t b[TileCfg<BM, BN, BK>::FN];  // B: row (h*8 + s/4), chunk for block fn (add kk*16 rows)
+  uint32_t b[TileCfg<BM, BN, BK, 0, NW>::FN];  // B: row (h*8 + s/4), chunk for block fn (add kk*16 rows)
 };
 
-template <int BM, int BN, int BK>
-__device__ inline FragAddr<BM, BN, BK> frag_addr() {
-  using C = TileCfg<BM, BN, BK>;
-  FragAddr<BM, BN, BK> f;
+template <int BM, int BN, int BK, int NW>
+__device__ inline FragAddr<BM, BN, BK, NW> frag_addr() {
+  using C = TileCfg<BM, BN, BK, 0, NW>;
+  FragAddr<BM, BN, BK, NW> f;
   const uint32_t l = lane_id();
   const uint32_t wave = threadIdx.x >> 6;
-  const uint32_t wm = (wave >> 1) * (BM / 2);
-  const uint32_t wn = (wave & 1) * (BN / 2);
+  const uint32_t wm = (wave / C::WN) * (BM / 2);
+  const uint32_t wn = (wave % C::WN) * (BN / C::WN);
   // A: row wm + fm*32 + l%32, logical chunk 2*kk + l/32 (the swizzle of a
   // row depends on it modulo 16 only, so fm*32 does not change it).
   const uint32_t row = wm + (l & 31);
@@ -297,24 +300,25 @@ __device__ inline FragAddr<BM, BN, BK> frag_addr() {
 
 // MFMA operands of one sub-step: A fragments, and B fragments as the two
 // 4-element halves that two transposing LDS reads produce.
-template <int BM, int BN>
+template <int BM, int BN, int NW>
 struct Frags {
-  bf16x8 a[TileCfg<BM, BN>::FM];
-  s16x4 blo[TileCfg<BM, BN>::FN];
-  s16x4 bhi[TileCfg<BM, BN>::FN];
+  bf16x8 a[TileCfg<BM, BN, 64, 0, NW>::FM];
+  s16x4 blo[TileCfg<BM, BN, 64, 0, NW>::FN];
+  s16x4 bhi[TileCfg<BM, BN, 64, 0, NW>::FN];
 };
 
-template <int BM, int BN>
-__device__ inline bf16x8 bfrag(const Frags<BM, BN>& f, int fn) {
+template <int BM, int BN, int NW>
+__device__ inline bf16x8 bfrag(const Frags<BM, BN, NW>& f, int fn) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(f.blo[fn], f.bhi[fn], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Read R of the fragments of sub-step kk, in the order the next sub-step
 // needs them: the low and high halves of each B fragment first (the first
 // MFMA group uses them all), then A fragment R - 2*FN.
-template <int BM, int BN, int BK, int R>
-__device__ inline void load_piece(Frags<BM, BN>& f, const uint8_t* stage, const FragAddr<BM, BN, BK>& fa, int kk) {
-  using C = TileCfg<BM, BN, BK>;
+template <int BM, int BN, int BK, int NW, int R>
+__device__ inline void load_piece(Frags<BM, BN, NW>& f, const uint8_t* stage, const FragAddr<BM, BN, BK, NW>& fa,
+                                  int kk) {
+  using C = TileCfg<BM, BN, BK, 0, NW>;
   if constexpr (R >= 2 * C::FN) {
     constexpr int fm = R - 2 * C::FN;
     f.a[fm] = *OVL_LDS(const bf16x8, stage + fa.a[kk] + fm * 32 * (BK * 2));
@@ -330,23 +334,25 @@ __device__ inline void load_piece(Frags<BM, BN>& f, const uint8_t* stage, const 
   }
 }
 
-template <int BM, int BN, int BK, int R0, int R1>
-__device__ inline void load_pieces(Frags<BM, BN>& f, const uint8_t* stage, const FragAddr<BM, BN, BK>& fa, int kk) {
+template <int BM, int BN, int BK, int NW, int R0, int R1>
+__device__ inline void load_pieces(Frags<BM, BN, NW>& f, const uint8_t* stage, const FragAddr<BM, BN, BK, NW>& fa,
+                                   int kk) {
   if constexpr (R0 < R1) {
-    load_piece<BM, BN, BK, R0>(f, stage, fa, kk);
-    load_pieces<BM, BN, BK, R0 + 1, R1>(f, stage, fa, kk);
+    load_piece<BM, BN, BK, NW, R0>(f, stage, fa, kk);
+    load_pieces<BM, BN, BK, NW, R0 + 1, R1>(f, stage, fa, kk);
   }
 }
 
-template <int BM, int BN, int BK>
-__device__ inline void load_frags(Frags<BM, BN>& f, const uint8_t* stage, const FragAddr<BM, BN, BK>& fa, int kk) {
-  using C = TileCfg<BM, BN, BK>;
-  load_pieces<BM, BN, BK, 0, C::FM + 2 * C::FN>(f, stage, fa, kk);
+template <int BM, int BN, int BK, int NW>
+__device__ inline void load_frags(Frags<BM, BN, NW>& f, const uint8_t* stage, const FragAddr<BM, BN, BK, NW>& fa,
+                                  int kk) {
+  using C = TileCfg<BM, BN, BK, 0, NW>;
+  load_pieces<BM, BN, BK, NW, 0, C::FM + 2 * C::FN>(f, stage, fa, kk);
 }
 
-template <int BM, int BN>
-__device__ inline void mfma_frags(Acc<BM, BN>& acc, const Frags<BM, BN>& f) {
-  using C = TileCfg<BM, BN>;
+template <int BM, int BN, int NW>
+__device__ inline void mfma_frags(Acc<BM, BN, NW>& acc, const Frags<BM, BN, NW>& f) {
+  using C = TileCfg<BM, BN, 64, 0, NW>;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
@@ -388,10 +394,10 @@ __device__ inline void issue_range(const P& p) {
 // KKI, on fragments `cur`, with this group's share of the next sub-step's
 // fragment reads into `nxt` interleaved (one read after each MFMA), followed
 // by a burst of a later stage's global loads where it is due.
-template <int BM, int BN, int BK, int KKI, int G, class P>
-__device__ inline void mfma_group(Acc<BM, BN>& acc, const Frags<BM, BN>& cur, Frags<BM, BN>& nxt,
-                                  const uint8_t* stage, const FragAddr<BM, BN, BK>& fa, const P& pf) {
-  using C = TileCfg<BM, BN, BK>;
+template <int BM, int BN, int BK, int NW, int KKI, int G, class P>
+__device__ inline void mfma_group(Acc<BM, BN, NW>& acc, const Frags<BM, BN, NW>& cur, Frags<BM, BN, NW>& nxt,
+                                  const uint8_t* stage, const FragAddr<BM, BN, BK, NW>& fa, const P& pf) {
+  using C = TileCfg<BM, BN, BK, 0, NW>;
   constexpr int fm = G % C::FM;
   constexpr int reads = C::FM + 2 * C::FN;  // fragment reads per sub-step
   constexpr int per = (reads + C::FM - 1) / C::FM;
@@ -401,7 +407,7 @@ __device__ inline void mfma_group(Acc<BM, BN>& acc, const Frags<BM, BN>& cur, Fr
 #pragma unroll
   for (int fn = 0; fn < C::FN; ++fn)
     acc.v[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[fm], bfrag(cur, fn), acc.v[fm][fn], 0, 0, 0);
-  if constexpr (KKI + 1 < C::KK) load_pieces<BM, BN, BK, r0, r1>(nxt, stage, fa, KKI + 1);
+  if constexpr (KKI + 1 < C::KK) load_pieces<BM, BN, BK, NW, r0, r1>(nxt, stage, fa, KKI + 1);
 #pragma unroll
   for (int i = 0; i < C::FN; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -416,12 +422,12 @@ __device__ inline void mfma_group(Acc<BM, BN>& acc, const Frags<BM, BN>& cur, Fr
   OVL_SCHED_FENCE();
 }
 
-template <int BM, int BN, int BK, int KKI, int G0, int N, class P>
-__device__ inline void mfma_groups(Acc<BM, BN>& acc, const Frags<BM, BN>& cur, Frags<BM, BN>& nxt,
-                                   const uint8_t* stage, const FragAddr<BM, BN, BK>& fa, const P& pf) {
+template <int BM, int BN, int BK, int NW, int KKI, int G0, int N, class P>
+__device__ inline void mfma_groups(Acc<BM, BN, NW>& acc, const Frags<BM, BN, NW>& cur, Frags<BM, BN, NW>& nxt,
+                                   const uint8_t* stage, const FragAddr<BM, BN, BK, NW>& fa, const P& pf) {
   if constexpr (N > 0) {
-    mfma_group<BM, BN, BK, KKI, G0>(acc, cur, nxt, stage, fa, pf);
-    mfma_groups<BM, BN, BK, KKI, G0 + 1, N - 1>(acc, cur, nxt, stage, fa, pf);
+    mfma_group<BM, BN, BK, NW, KKI, G0>(acc, cur, nxt, stage, fa, pf);
+    mfma_groups<BM, BN, BK, NW, KKI, G0 + 1, N - 1>(acc, cur, nxt, stage, fa, pf);
   }
 }
 
@@ -429,20 +435,20 @@ __device__ inline void mfma_groups(Acc<BM, BN>& acc, const Frags<BM, BN>& cur, F
 // double-buffered so that the LDS reads of sub-step kk+1 are in flight
 // during the MFMAs of kk (one read after each MFMA), with the global -> LDS
 // loads of a later stage in two bursts in mid-step.
-template <int BM, int BN, int BK, class P>
-__device__ inline void stage_compute(Acc<BM, BN>& acc, const uint8_t* stage, const FragAddr<BM, BN, BK>& fa,
+template <int BM, int BN, int BK, int NW, class P>
+__device__ inline void stage_compute(Acc<BM, BN, NW>& acc, const uint8_t* stage, const FragAddr<BM, BN, BK, NW>& fa,
                                      const P& pf) {
-  using C = TileCfg<BM, BN, BK>;
-  Frags<BM, BN> f0, f1;
+  using C = TileCfg<BM, BN, BK, 0, NW>;
+  Frags<BM, BN, NW> f0, f1;
   load_frags(f0, stage, fa, 0);
   OVL_SCHED_FENCE();
-  mfma_groups<BM, BN, BK, 0, 0, C::FM>(acc, f0, f1, stage, fa, pf);
+  mfma_groups<BM, BN, BK, NW, 0, 0, C::FM>(acc, f0, f1, stage, fa, pf);
   if constexpr (C::KK == 4) {
-    mfma_groups<BM, BN, BK, 1, C::FM, C::FM>(acc, f1, f0, stage, fa, pf);
-    mfma_groups<BM, BN, BK, 2, 2 * C::FM, C::FM>(acc, f0, f1, stage, fa, pf);
-    mfma_groups<BM, BN, BK, 3, 3 * C::FM, C::FM>(acc, f1, f0, stage, fa, pf);
+    mfma_groups<BM, BN, BK, NW, 1, C::FM, C::FM>(acc, f1, f0, stage, fa, pf);
+    mfma_groups<BM, BN, BK, NW, 2, 2 * C::FM, C::FM>(acc, f0, f1, stage, fa, pf);
+    mfma_groups<BM, BN, BK, NW, 3, 3 * C::FM, C::FM>(acc, f1, f0, stage, fa, pf);
   } else {
-    mfma_groups<BM, BN, BK, 1, C::FM, C::FM>(acc, f1, f0, stage, fa, pf);
+    mfma_groups<BM, BN, BK, NW, 1, C::FM, C::FM>(acc, f1, f0, stage, fa, pf);
   }
 }
 
@@ -459,9 +465,9 @@ __device__ inline void wait_stage_loads(int pending_stages) {
   }
 }
 
-template <int BM, int BN>
-__device__ inline void acc_zero(Acc<BM, BN>& acc) {
-  using C = TileCfg<BM, BN>;
+template <int BM, int BN, int NW>
+__device__ inline void acc_zero(Acc<BM, BN, NW>& acc) {
+  using C = TileCfg<BM, BN, 64, 0, NW>;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
@@ -475,16 +481,16 @@ __device__ inline void acc_zero(Acc<BM, BN>& acc) {
 // calls it, before a workgroup barrier that precedes the first load of that
 // step (so a wave that acquires there orders the whole workgroup's loads).
 // Ends with a workgroup barrier, so LDS may be reused at once.
-template <int BM, int BN, int BK = 64, int NSTAGES = 0, bool IND = false, class BeforeStep>
-__device__ inline void gemm_tile(Acc<BM, BN>& acc, const Operands& op, int64_t m0, uint16_t* lds,
+template <int BM, int BN, int BK = 64, int NSTAGES = 0, bool IND = false, int NW = 4, class BeforeStep>
+__device__ inline void gemm_tile(Acc<BM, BN, NW>& acc, const Operands& op, int64_t m0, uint16_t* lds,
                                  BeforeStep before_step) {
-  using C = TileCfg<BM, BN, BK, NSTAGES>;
+  using C = TileCfg<BM, BN, BK, NSTAGES, NW>;
   constexpr int NS = C::NS;
   static_assert(NS - 2 <= 2, "wait_stage_loads covers up to two pending stages");
   uint8_t* l8 = reinterpret_cast<uint8_t*>(lds);
   acc_zero(acc);
-  const TileAddr<BM, BN, BK, IND> ta = tile_addr<BM, BN, BK, IND>(op, m0);
-  const FragAddr<BM, BN, BK> fa = frag_addr<BM, BN, BK>();
+  const TileAddr<BM, BN, BK, IND, NW> ta = tile_addr<BM, BN, BK, IND, NW>(op, m0);
+  const FragAddr<BM, BN, BK, NW> fa = frag_addr<BM, BN, BK, NW>();
   const int32_t steps = (int32_t)((op.k + BK - 1) / BK);
   const uint32_t lbase = lds_addr(l8);
   // Prologue: the first NS-1 stages.
@@ -500,8 +506,8 @@ __device__ inline void gemm_tile(Acc<BM, BN>& acc, const Operands& op, int64_t m
   __syncthreads();
   for (int32_t s = 0; s < steps; ++s) {
     const int32_t nxt = s + NS - 1;  // stage issued during this step
-    const Prefetch<BM, BN, BK, IND> pf{&ta, lbase + (uint32_t)(nxt % NS) * C::STAGE_BYTES, nxt * BK, nxt < steps};
-    stage_compute<BM, BN, BK>(acc, l8 + (s % NS) * C::STAGE_BYTES, fa, pf);
+    const Prefetch<BM, BN, BK, IND, NW> pf{&ta, lbase + (uint32_t)(nxt % NS) * C::STAGE_BYTES, nxt * BK, nxt < steps};
+    stage_compute<BM, BN, BK, NW>(acc, l8 + (s % NS) * C::STAGE_BYTES, fa, pf);
     if (s + NS < steps) step_cols(s + NS);
     // Stage s+1 must have landed; the stages issued after it may stay in flight.
     wait_stage_loads<C::LPS>(max(0, min(s + NS - 1, steps - 1) - (s + 1)));
@@ -512,13 +518,13 @@ __device__ inline void gemm_tile(Acc<BM, BN>& acc, const Operands& op, int64_t m
 // Calls f(row, col, value) for every accumulator element of this lane, with
 // row/col relative to the tile origin (32x32 MFMA output layout: lane l holds
 // column l%32; register r holds row (r%4) + 8*(r/4) + 4*(l/32)).
-template <int BM, int BN, class F>
-__device__ inline void acc_foreach(const Acc<BM, BN>& acc, F f) {
-  using C = TileCfg<BM, BN>;
+template <int BM, int BN, int NW, class F>
+__device__ inline void acc_foreach(const Acc<BM, BN, NW>& acc, F f) {
+  using C = TileCfg<BM, BN, 64, 0, NW>;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  const int wm = (wave >> 1) * (BM / 2);
-  const int wn = (wave & 1) * (BN / 2);
+  const int wm = (wave / C::WN) * (BM / 2);
+  const int wn = (wave % C::WN) * (BN / C::WN);
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
@@ -561,8 +567,8 @@ __device__ inline uint32_t out_off(const OutTile& o, int row, int col) {
 // AUX is the buffer store's cache-policy operand (0: default).  Each store
 // instruction writes 128 contiguous bytes of two rows (measured faster than
 // computing the blocks transposed for 16-byte stores: 32-byte row pieces).
-template <int BM, int BN, int AUX = 0>
-__device__ inline void acc_store(const Acc<BM, BN>& acc, float* c, int64_t ldc, int64_t m0, int64_t n0,
+template <int BM, int BN, int AUX = 0, int NW = 4>
+__device__ inline void acc_store(const Acc<BM, BN, NW>& acc, float* c, int64_t ldc, int64_t m0, int64_t n0,
                                  int64_t m_valid, int64_t n_valid) {
   const OutTile o = out_tile(c, ldc, m0, n0, m_valid, n_valid);
   acc_foreach(acc, [&](int row, int col, float v) { bstoref<AUX>(o.r, out_off(o, row, col), v); });
@@ -571,17 +577,17 @@ __device__ inline void acc_store(const Acc<BM, BN>& acc, float* c, int64_t ldc, 
 // Stores the tile through a row table: tile row i goes to row rows[i] of
 // fp32 C (row pitch ldc, c_rows rows; nothing where rows[i] < 0), columns
 // n0 + col clipped to n_valid.
-template <int BM, int BN>
-__device__ inline void acc_store_rows(const Acc<BM, BN>& acc, float* c, int64_t ldc, int64_t c_rows,
+template <int BM, int BN, int NW = 4>
+__device__ inline void acc_store_rows(const Acc<BM, BN, NW>& acc, float* c, int64_t ldc, int64_t c_rows,
                                       const int32_t* rows, int64_t n0, int64_t n_valid) {
-  using C = TileCfg<BM, BN>;
+  using C = TileCfg<BM, BN, 64, 0, NW>;
   const rsrc_t r = make_rsrc(c, c_rows * ldc * 4);
   const uint32_t ldc_b = opaque((uint32_t)(ldc * 4));
   const int64_t n_left = n_valid - n0;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  const int wm = (wave >> 1) * (BM / 2);
-  const int wn = (wave & 1) * (BN / 2);
+  const int wm = (wave / C::WN) * (BM / 2);
+  const int wn = (wave % C::WN) * (BN / C::WN);
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
