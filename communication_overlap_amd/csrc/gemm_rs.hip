@@ -30,6 +30,10 @@ namespace {
 constexpr int kRsMaxRanks = 16;
 constexpr int kRsTile = 256;
 constexpr int kRsXcds = 8;
+// Wavefronts per workgroup: the 256 x 256 tile as a 2 x 4 grid of waves, two
+// per SIMD (one's MFMAs cover the other's LDS reads; measured faster than 4).
+constexpr int kRsWaves = 8;
+constexpr int kRsThreads = 64 * kRsWaves;
 
 struct RsArgs {
   float* peer_out[kRsMaxRanks];
@@ -106,18 +110,18 @@ __device__ void reduce_job(const RsArgs& a, int64_t j, int64_t J, bool& timed_ou
     wave_acquire();
   }
   __syncthreads();
-  // 64 lanes of 16 bytes cover one 256-column row; each wave takes two rows
-  // per pass and issues all of their loads (accumulator and R-1 partials)
-  // before the first add.
-  constexpr int U = 2;
+  // 64 lanes of 16 bytes cover one 256-column row; each wave takes U rows
+  // per pass (8 rows per workgroup) and issues all of their loads
+  // (accumulator and R-1 partials) before the first add.
+  constexpr int U = 8 / kRsWaves;
   const int lane = threadIdx.x & 63, rsub = threadIdx.x >> 6;
-  for (int64_t q = q0 + rsub; q < q1; q += 4 * U) {
+  for (int64_t q = q0 + rsub; q < q1; q += kRsWaves * U) {
     int64_t off[U];
     bool ok[U];
     f32x4 acc[U], v[U][kRsMaxRanks];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t qq = q + 4 * u;
+      const int64_t qq = q + kRsWaves * u;
       const int64_t t = qq / kRsTile;
       const int64_t row = (t / a.tc) * kRsTile + (qq % kRsTile);
       const int64_t col = (t % a.tc) * kRsTile + lane * 4;
@@ -154,7 +158,7 @@ __device__ void reduce_job(const RsArgs& a, int64_t j, int64_t J, bool& timed_ou
 }
 
 template <int SYNC>
-__global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs a) {
+__global__ __launch_bounds__(kRsThreads, 1) void gemm_rs_kernel(RsArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
   constexpr int BM = kRsTile, BN = kRsTile;
   const int tpb = a.tr * a.tc;
@@ -187,15 +191,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs a) {
     op.k = a.k;
     const int64_t m0 = (int64_t)trow * BM;
 
-    Acc<BM, BN> acc;
-    gemm_tile<BM, BN>(acc, op, m0, lds, [](int64_t, int64_t) {});
+    Acc<BM, BN, kRsWaves> acc;
+    gemm_tile<BM, BN, 64, 0, false, kRsWaves>(acc, op, m0, lds, [](int64_t, int64_t) {});
 
     if (blk != a.rank) {
-      acc_store<BM, BN>(acc, a.peer_out[blk], a.n, m0, op.n0, a.bm, a.n);
+      acc_store<BM, BN, 0, kRsWaves>(acc, a.peer_out[blk], a.n, m0, op.n0, a.bm, a.n);
       if (SYNC) wg_publish(a.out_flags + ((int64_t)blk * tpb + t) * a.flag_stride, a.epoch);
       reduce_job(a, pj, J, timed_out);
     } else {
-      acc_store<BM, BN>(acc, a.out, a.n, m0, op.n0, a.bm, a.n);
+      acc_store<BM, BN, 0, kRsWaves>(acc, a.out, a.n, m0, op.n0, a.bm, a.n);
       if (J > 0) wg_publish(a.own_flags + t, a.epoch);
     }
   }
@@ -289,7 +293,7 @@ extern "C" ovl_status gemm_rs_run(const gemm_rs_desc* d, const void* a, const vo
   st = allow_lds(reinterpret_cast<const void*>(&gemm_rs_kernel<1>), lds);
   if (st) return st;
   int occ = 0;
-  OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_rs_kernel<1>, kThreads, lds));
+  OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_rs_kernel<1>, kRsThreads, lds));
   const int64_t total = (int64_t)d->ranks * r.tr * r.tc;
   int64_t workers = std::min<int64_t>(total, (int64_t)std::max(occ, 1) * di.cus);
   if (workers > kRsXcds) workers -= workers % kRsXcds;
@@ -303,9 +307,9 @@ extern "C" ovl_status gemm_rs_run(const gemm_rs_desc* d, const void* a, const vo
   st = epoch_accept(workspace, epoch);
   if (st) return st;
   if (mode == OVL_MODE_FUSED)
-    hipLaunchKernelGGL(gemm_rs_kernel<1>, dim3(workers), dim3(kThreads), lds, stream, r);
+    hipLaunchKernelGGL(gemm_rs_kernel<1>, dim3(workers), dim3(kRsThreads), lds, stream, r);
   else
-    hipLaunchKernelGGL(gemm_rs_kernel<0>, dim3(workers), dim3(kThreads), lds, stream, r);
+    hipLaunchKernelGGL(gemm_rs_kernel<0>, dim3(workers), dim3(kRsThreads), lds, stream, r);
   OVL_HIP_TRY(hipGetLastError());
   return OVL_OK;
 }
