@@ -45,6 +45,10 @@ constexpr int kGbm = 256, kGbn = 256;  // grouped GEMM tile
 constexpr int kGbn8 = 128;
 constexpr int kA2aMaxMTiles = 1024;    // m-tiles whose consumer order is sorted in LDS
 constexpr int kA2aXcds = 8;
+// Wavefronts per workgroup of the fused launch: the bf16 tile runs as a
+// 2 x 4 grid of waves, two per SIMD (one's MFMAs cover the other's LDS
+// reads; measured faster than 4); the FP8 tile as a 2 x 2 grid.
+constexpr int a2a_waves(bool f8) { return f8 ? 4 : 8; }
 // LDS of a grouped-GEMM tile, bf16 or FP8 (the geometry follows it).
 constexpr int kA2aGemmLds = TileCfg<kGbm, kGbn>::LDS_BYTES > F8Cfg<kGbm, kGbn8>::LDS_BYTES
                                 ? TileCfg<kGbm, kGbn>::LDS_BYTES
@@ -186,7 +190,7 @@ __device__ inline int pos_of_row(const A2aArgs& a, const Geometry* g, int e, int
 
 __device__ void build_geometry(const A2aArgs& a, Geometry* g) {
   __shared__ int32_t s_key[kA2aMaxMTiles];
-  for (int i = threadIdx.x; i < a.ranks * a.experts; i += kThreads) g->count[i] = a.recv_count[i];
+  for (int i = threadIdx.x; i < a.ranks * a.experts; i += blockDim.x) g->count[i] = a.recv_count[i];
   __syncthreads();
   if (threadIdx.x == 0) {
     int chunks = 0;
@@ -222,7 +226,7 @@ __device__ void build_geometry(const A2aArgs& a, Geometry* g) {
   // expert, m-tile), identical in every workgroup.
   const int n_mt = uniform(g->n_mt);
   if (n_mt <= kA2aMaxMTiles) {
-    for (int q = threadIdx.x; q < n_mt; q += kThreads) {
+    for (int q = threadIdx.x; q < n_mt; q += blockDim.x) {
       int e = 0;
       while (g->mt_base[e + 1] <= q) ++e;
       const int mt = q - g->mt_base[e];
@@ -233,7 +237,7 @@ __device__ void build_geometry(const A2aArgs& a, Geometry* g) {
       s_key[q] = (pos * kA2aMaxExperts + e) * kA2aMaxMTiles + mt;  // distinct keys
     }
     __syncthreads();
-    for (int q = threadIdx.x; q < n_mt; q += kThreads) {
+    for (int q = threadIdx.x; q < n_mt; q += blockDim.x) {
       const int32_t k = s_key[q];
       int rank = 0;
       for (int o = 0; o < n_mt; ++o) rank += s_key[o] < k;
@@ -266,7 +270,7 @@ __device__ inline void mtile_at(const A2aArgs& a, const Geometry* g, int q, int*
 // vectors lane, lane + 64, ... of a slot: a slot is one row (in passes, for
 // rows longer than 8 KiB), or several whole rows when rows are shorter (a
 // power-of-two count of at least 1 KiB: FP8 tokens), so that every lane
-// always has work.  The wave takes slots w, w + 4 (a pair), then w + 8, ....
+// always has work.  Wave w of W takes slots w, w + W (a pair), then w + 2W, ....
 // The loads of the next step are issued before the stores of the current
 // one, so that a wave always has a slot pair in flight (vector memory
 // counters complete in order: waiting for the loads then does not wait for
@@ -274,6 +278,7 @@ __device__ inline void mtile_at(const A2aArgs& a, const Geometry* g, int q, int*
 __device__ inline void copy_rows(const A2aArgs& a, int s, int r0, int r1) {
   constexpr int V = 8;  // vectors per lane per slot: 8 KiB
   const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int W = (int)(blockDim.x >> 6);
   const int vpr = (int)(a.row_bytes / 16);
   const uint8_t* src = a.x[s];
   uint8_t* dst = a.recv_x + (int64_t)s * a.cap * a.row_bytes;
@@ -284,13 +289,13 @@ __device__ inline void copy_rows(const A2aArgs& a, int s, int r0, int r1) {
   const int lg_qpr = multi ? __builtin_ctz(vpr / 64) : 0;  // log2(vectors per lane per row)
   const int rps = multi ? (64 * V) / vpr : 1;
   const int units = (r1 - r0 + rps - 1) / rps;
-  // Steps: (slot pair, column pass); a pair is slots u, u + 4 of this wave.
+  // Steps: (slot pair, column pass); a pair is slots u, u + W of this wave.
   const int passes = multi ? 1 : (vpr + 64 * V - 1) / (64 * V);
-  const int pairs = (units - wave + 7) / 8 > 0 ? (units - wave + 7) / 8 : 0;
+  const int pairs = units > wave ? (units - wave + 2 * W - 1) / (2 * W) : 0;
   const int steps = pairs * passes;
   u32x4 cur[2][V], nxt[2][V];
   auto load = [&](int st, u32x4 (&v)[2][V]) {
-    const int u = wave + (st / passes) * 8, c0 = (st % passes) * 64 * V;
+    const int u = wave + (st / passes) * 2 * W, c0 = (st % passes) * 64 * V;
     // every vector's source token first (all lanes read the same entries),
     // then the data loads: one wait for the table, not one per row
     int32_t tok[2][V];
@@ -298,7 +303,7 @@ __device__ inline void copy_rows(const A2aArgs& a, int s, int r0, int r1) {
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int q = 0; q < V; ++q) {
-        const int rr = r0 + (u + 4 * h) * rps + (multi ? q >> lg_qpr : 0);
+        const int rr = r0 + (u + W * h) * rps + (multi ? q >> lg_qpr : 0);
         tok[h][q] = rr < r1 ? srow[rr] : -1;
       }
 #pragma unroll
@@ -312,12 +317,12 @@ __device__ inline void copy_rows(const A2aArgs& a, int s, int r0, int r1) {
     }
   };
   auto store = [&](int st, const u32x4 (&v)[2][V]) {
-    const int u = wave + (st / passes) * 8, c0 = (st % passes) * 64 * V;
+    const int u = wave + (st / passes) * 2 * W, c0 = (st % passes) * 64 * V;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int q = 0; q < V; ++q) {
-        const int rr = r0 + (u + 4 * h) * rps + (multi ? q >> lg_qpr : 0);
+        const int rr = r0 + (u + W * h) * rps + (multi ? q >> lg_qpr : 0);
         const int c = multi ? ((q & ((1 << lg_qpr) - 1)) << 6) + lane : c0 + q * 64 + lane;
         if (rr >= r1 || c >= vpr) continue;
         st16(dst + (int64_t)rr * a.row_bytes + c * 16, v[h][q]);
@@ -500,7 +505,7 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
     // Row table of the tile: expert row r0 + i lies in the slice at the
     // first position whose expert prefix exceeds it.
     int32_t* tab = rowtab[wv & 1];
-    for (int i = threadIdx.x; i < kGbm; i += kThreads) {
+    for (int i = threadIdx.x; i < kGbm; i += blockDim.x) {
       int32_t v = -1;
       if (i < nrows) {
         const int r = r0 + i;
@@ -513,7 +518,8 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
       if constexpr (F8) scaletab[wv & 1][i] = v >= 0 ? a.recv_scale[v] : 0.f;
     }
     __syncthreads();
-    Acc<kGbm, TBN> acc;
+    constexpr int NW = a2a_waves(F8);
+    Acc<kGbm, TBN, NW> acc;
     if constexpr (F8) {
       Operands8 op;
       op.a = a.recv_x;
@@ -539,8 +545,8 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
       op.n0 = (int64_t)nt * TBN;
       op.n_valid = a.n;
       op.k = a.hidden;
-      gemm_tile<kGbm, TBN, 64, 0, true>(acc, op, 0, lds, [](int64_t, int64_t) {});
-      acc_store_rows<kGbm, TBN>(acc, a.y, a.n, (int64_t)a.ranks * a.cap, tab, op.n0, a.n);
+      gemm_tile<kGbm, TBN, 64, 0, true, NW>(acc, op, 0, lds, [](int64_t, int64_t) {});
+      acc_store_rows<kGbm, TBN, NW>(acc, a.y, a.n, (int64_t)a.ranks * a.cap, tab, op.n0, a.n);
     }
   }
 }
@@ -550,7 +556,7 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
 // not complete yet, so the first consumers copy the first slices together
 // and the copy keeps ahead of the GEMM.
 template <int MODE, bool F8>  // MODE 0 fused, 2 GEMM only; F8: FP8 rows and grouped GEMM
-__global__ __launch_bounds__(kThreads, 1) void a2a_fused_kernel(A2aArgs a) {
+__global__ __launch_bounds__(64 * a2a_waves(F8), 1) void a2a_fused_kernel(A2aArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int sh;
   Geometry* g = reinterpret_cast<Geometry*>(reinterpret_cast<uint8_t*>(lds) + kA2aGemmLds);
@@ -676,7 +682,8 @@ ovl_status a2a_run(const a2a_desc* d, bool f8, const void* const* x, const float
   st = allow_lds(reinterpret_cast<const void*>(fk), lds);
   if (st) return st;
   int occ = 0;
-  OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fk, kThreads, lds));
+  const int threads = 64 * a2a_waves(f8);
+  OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fk, threads, lds));
   const int64_t resident = (int64_t)std::max(occ, 1) * di.cus;
   const uint32_t req = opts ? opts->producers : 0;
 
@@ -708,7 +715,7 @@ ovl_status a2a_run(const a2a_desc* d, bool f8, const void* const* x, const float
   if (Cn > kA2aXcds) Cn -= Cn % kA2aXcds;
   a.producers = P;
   a.consumers = (int32_t)Cn;
-  hipLaunchKernelGGL(fk, dim3(P + Cn), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL(fk, dim3(P + Cn), dim3(threads), lds, stream, a);
   OVL_HIP_TRY(hipGetLastError());
   return OVL_OK;
 }
