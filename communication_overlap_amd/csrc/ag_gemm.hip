@@ -374,7 +374,12 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
   // Work items (tile, K range) in consumer order are dealt out in rounds of
   // C; inside a round, consecutive items go to consumers on the same die
   // (workgroup ids are dispatched round-robin over the dies), so that items
-  // sharing A rows or B columns share an L2.
+  // sharing A rows or B columns share an L2.  When a round is whole rows of
+  // unsplit tiles, each die takes a block of it instead (gr x gc dies over
+  // the round's row tiles x column tiles, the split that needs the fewest A
+  // and B panels per die): 4 row tiles x 7 column tiles at 224 consumers
+  // and 14 column tiles, i.e. 11 operand panels per die and round where
+  // 2 whole rows of tiles need 16.
   const int Cn = a.consumers;
   const int groups = (Cn % kXcds == 0) ? kXcds : 1;
   const int per = Cn / groups;
@@ -383,8 +388,25 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
   const int own_lo = a.rank;  // shard index of the own rank
   __shared__ int s_last;
 
+  int gr = 0, gc = 0;
+  if (a.splits == 1 && groups == kXcds && Cn % a.tiles_n == 0) {
+    const int rr = Cn / a.tiles_n;
+    int best = 1 << 30;
+    for (int c = 1; c <= kXcds; c *= 2) {
+      const int r = kXcds / c;
+      if (rr % r == 0 && a.tiles_n % c == 0 && rr / r + a.tiles_n / c < best) {
+        best = rr / r + a.tiles_n / c;
+        gr = r;
+        gc = c;
+      }
+    }
+  }
   for (int64_t w = 0;; ++w) {
-    const int64_t j = w * Cn + (int64_t)x * per + q;
+    int64_t j = w * Cn + (int64_t)x * per + q;
+    if (gr && (w + 1) * Cn <= items) {
+      const int rr = Cn / a.tiles_n, rpd = rr / gr, cpd = a.tiles_n / gc;
+      j = (w * rr + (x / gc) * rpd + q / cpd) * a.tiles_n + (x % gc) * cpd + q % cpd;
+    }
     if (j >= items) break;
     const int64_t tl = j / a.splits;
     const int sp = (int)(j % a.splits);
@@ -498,7 +520,7 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
 
     Acc<BM, BN, NW> acc;
     gemm_tile<BM, BN, 64, NS, false, NW>(acc, op, m0_op, lds, before_step);
-    if (NS != kSplitStages || a.splits == 1) {
+    if (BM != 128 || NS != kSplitStages || a.splits == 1) {
       acc_store<BM, BN, 0, NW>(acc, a.c, a.n, m0, n0, a.m, a.n);
       trace_item();
       continue;
