@@ -444,16 +444,14 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
     // up to the first missing unit are there.
     int ready = (int)(k_lo / a.batch_cols) - 1;
     const int last = (int)((k_hi - 1) / a.batch_cols);
+    // The (shard, row panel) pairs that cover the tile's rows are consecutive
+    // in unit numbering (unit = (shard * panels + panel) * batches + batch):
+    // panel ids sp_lo .. sp_lo + npan - 1.  Computed once per item, so that a
+    // poll costs no 64-bit division.
     const int s_lo = (int)(m0 / a.shard_m), s_hi = (int)((m_end - 1) / a.shard_m);
-    // Calls f(u) for the units of batch bt that cover the tile's rows.
-    auto units_of = [&](int bt, auto f) {
-      for (int s = s_lo; s <= s_hi; ++s) {
-        const int64_t lo = max(m0, (int64_t)s * a.shard_m) - (int64_t)s * a.shard_m;
-        const int64_t hi = min(m_end, (int64_t)(s + 1) * a.shard_m) - (int64_t)s * a.shard_m;
-        for (int p = (int)(lo / a.unit_rows); p <= (int)((hi - 1) / a.unit_rows); ++p)
-          f(((int64_t)s * a.panels + p) * a.batches + bt);
-      }
-    };
+    const int sp_lo = s_lo * a.panels + (int)((m0 - (int64_t)s_lo * a.shard_m) / a.unit_rows);
+    const int npan =
+        s_hi * a.panels + (int)((m_end - 1 - (int64_t)s_hi * a.shard_m) / a.unit_rows) - sp_lo + 1;
     const int64_t t_item = a.trace ? now_ticks() : 0;
     const int64_t c_item = a.trace ? now_cycles() : 0;
     int64_t waited = 0;  // ticks wave 0 spent polling for this item (traced runs)
@@ -465,25 +463,16 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
       const int64_t t_wait = a.trace ? now_ticks() : 0;
       const int lane = lane_id();
       for (uint64_t polls = 0;; ++polls) {
-        int bad = last + 1;  // first batch with a unit not there yet (this lane's share)
-        // Units numbered batch-major; lane l reads units l, l + 64, ...: the
-        // numbering pass only picks this lane's unit, then one load per lane
-        // goes out for all lanes at once.
-        for (int base = 0;; base += 64) {
-          int64_t mine = -1;
-          int mine_bt = 0, i = 0;
-          for (int bt = ready + 1; bt <= last; ++bt)
-            units_of(bt, [&](int64_t u) {
-              if (i == base + lane) {
-                mine = u;
-                mine_bt = bt;
-              }
-              ++i;
-            });
-          if (mine >= 0 &&
-              __hip_atomic_load(a.flags + mine * a.flag_stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.epoch)
-            bad = min(bad, mine_bt);
-          if (base + 64 >= i) break;
+        // One round trip reads the units of every remaining batch (numbered
+        // batch-major: i -> batch ready + 1 + i / npan, panel i % npan),
+        // lanes in parallel; bad = first batch with a unit not there yet.
+        int bad = last + 1;
+        const int cnt = npan * (last - ready);
+        for (int i = lane; i < cnt; i += 64) {
+          const int bt = ready + 1 + i / npan;
+          const int64_t u = (int64_t)(sp_lo + i % npan) * a.batches + bt;
+          if (__hip_atomic_load(a.flags + u * a.flag_stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.epoch)
+            bad = min(bad, bt);
         }
         for (int d = 1; d < 64; d <<= 1) bad = min(bad, __shfl_xor(bad, d, 64));
         bad = uniform(bad);
@@ -494,10 +483,10 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
         if (polls >= a.spin_limit) {
           // Name the first missing unit in the error record.
           for (int bt = ready + 1; bt <= need && !timed_out; ++bt)
-            units_of(bt, [&](int64_t u) {
-              if (!timed_out && !wave_poll(a.flags + u * a.flag_stride, a.epoch, 0, a.err, kSiteAgUnit, u))
-                timed_out = true;
-            });
+            for (int j = 0; j < npan && !timed_out; ++j) {
+              const int64_t u = (int64_t)(sp_lo + j) * a.batches + bt;
+              if (!wave_poll(a.flags + u * a.flag_stride, a.epoch, 0, a.err, kSiteAgUnit, u)) timed_out = true;
+            }
           timed_out = true;
           break;
         }

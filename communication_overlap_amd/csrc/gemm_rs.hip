@@ -76,9 +76,12 @@ __device__ void reduce_job(const RsArgs& a, int64_t j, int64_t J, bool& timed_ou
   if (threadIdx.x < 64 && !timed_out) {
     const int64_t t0 = q0 / kRsTile, nt = (q1 - 1) / kRsTile - t0 + 1;
     const int64_t nflags = nt * (a.sync ? a.ranks : 1);
-    auto flag_at = [&](int64_t i, int64_t* idx, int32_t* site) -> const int64_t* {
+    // (32-bit index arithmetic: a job has few flags, and a poll should not
+    // pay for 64-bit divisions.)
+    auto flag_at = [&](int64_t i64, int64_t* idx, int32_t* site) -> const int64_t* {
+      const int32_t i = (int32_t)i64;
       const int64_t t = t0 + (a.sync ? i / a.ranks : i);
-      const int p = a.sync ? (int)(i % a.ranks) : a.rank;
+      const int p = a.sync ? i % a.ranks : a.rank;
       if (p == a.rank) {
         *idx = t;
         *site = kSiteRsOwn;
