@@ -57,6 +57,8 @@ constexpr int kA2aGemmLds = TileCfg<kGbm, kGbn>::LDS_BYTES > F8Cfg<kGbm, kGbn8>:
 struct A2aArgs {
   const uint8_t* x[kA2aMaxRanks];        // token rows of row_bytes (bf16 or FP8 codes)
   const float* x_scale[kA2aMaxRanks];    // FP8: per-token scales (else null)
+  const uint8_t* x_own;                  // x[rank] and x_scale[rank] (read in place by own-slice tiles)
+  const float* x_scale_own;
   const int32_t* topk[kA2aMaxRanks];
   const uint8_t* w;        // bf16 [E][hidden][n], or FP8 codes [E][n][hidden]
   const float* w_scale;    // FP8: [E][n]
@@ -475,7 +477,10 @@ __device__ bool wait_slice_helping(const A2aArgs& a, const Geometry* g, int s, i
 template <bool WAIT, bool F8>
 __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint16_t* lds) {
   __shared__ int sh[2];
-  __shared__ int32_t rowtab[2][kGbm];  // A / y row of each tile row (s * cap + slice row), or -1
+  // Per tile (double-buffered): [0] the y row of each tile row (s * cap +
+  // slice row; also the A row in recv_x), or -1; [1] for own-slice tiles,
+  // the token row of x[rank] each tile row reads.
+  __shared__ int32_t rowtab[2][2][kGbm];
   __shared__ float scaletab[F8 ? 2 : 1][F8 ? kGbm : 1];  // FP8: the scale of each tile row
   constexpr int TBN = F8 ? kGbn8 : kGbn;
   const int ntn = (int)((a.n + TBN - 1) / TBN);
@@ -496,7 +501,16 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
     const int r0 = mt * kGbm, rows_e = uniform(pre[a.ranks]);
     const int nrows = min(kGbm, rows_e - r0);
     const int pos_hi = pos_of_row(a, g, e, r0 + nrows - 1);
-    if (WAIT) {
+    // A tile whose rows all lie in the own slice reads them from the own
+    // tokens in place (recv_src, from the layout kernel, names each row's
+    // token): the same bits as the slice's copy, with nothing to wait for,
+    // so the first consumers compute while the others copy.  Its row table
+    // holds token ids (< tokens) or -1 (no row: an out-of-range offset), so
+    // the A resource keeps the ranks * cap row bound of the received rows
+    // (>= tokens) and is never read past x[rank]'s rows; a bound selected
+    // per tile made the compiler reserve scratch.
+    const bool local = WAIT && pos_hi == 0;
+    if (WAIT && !local) {
       while (waited_hi < pos_hi && !timed_out) {
         ++waited_hi;
         if (!wait_slice_helping(a, g, slice_at(a, waited_hi), sh)) timed_out = true;
@@ -504,7 +518,8 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
     }
     // Row table of the tile: expert row r0 + i lies in the slice at the
     // first position whose expert prefix exceeds it.
-    int32_t* tab = rowtab[wv & 1];
+    int32_t* tab = rowtab[wv & 1][0];
+    int32_t* tokrow = rowtab[wv & 1][1];
     for (int i = threadIdx.x; i < kGbm; i += blockDim.x) {
       int32_t v = -1;
       if (i < nrows) {
@@ -515,7 +530,10 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
         v = s * (int32_t)a.cap + g->seg_start[pos * a.experts + e] + (r - pre[pos]);
       }
       tab[i] = v;
-      if constexpr (F8) scaletab[wv & 1][i] = v >= 0 ? a.recv_scale[v] : 0.f;
+      const int32_t tk = (local && v >= 0) ? a.recv_src[v] : -1;
+      if (local) tokrow[i] = tk;
+      if constexpr (F8)
+        scaletab[wv & 1][i] = local ? (tk >= 0 ? a.x_scale_own[tk] : 0.f) : (v >= 0 ? a.recv_scale[v] : 0.f);
     }
     __syncthreads();
     constexpr int NW = a2a_waves(F8);
@@ -525,7 +543,8 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
       op.a = a.recv_x;
       op.lda = a.hidden;
       op.m_valid = (int64_t)a.ranks * a.cap;
-      op.rows = tab;
+      if (local) op.a = a.x_own;  // rows: token ids < tokens <= ranks * cap (see above)
+      op.rows = rowtab[wv & 1][local ? 1 : 0];
       op.bt = a.w + (int64_t)e * a.n * a.hidden;
       op.ldb = a.hidden;
       op.n0 = (int64_t)nt * TBN;
@@ -539,7 +558,8 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
       op.a = reinterpret_cast<const uint16_t*>(a.recv_x);
       op.lda = a.hidden;
       op.m_valid = (int64_t)a.ranks * a.cap;
-      op.rows = tab;
+      if (local) op.a = reinterpret_cast<const uint16_t*>(a.x_own);  // rows: token ids (see above)
+      op.rows = rowtab[wv & 1][local ? 1 : 0];
       op.b = reinterpret_cast<const uint16_t*>(a.w) + (int64_t)e * a.hidden * a.n;
       op.ldb = a.n;
       op.n0 = (int64_t)nt * TBN;
@@ -652,6 +672,8 @@ ovl_status a2a_run(const a2a_desc* d, bool f8, const void* const* x, const float
     a.x_scale[s] = f8 ? x_scale[s] : nullptr;
     a.topk[s] = topk_idx[s];
   }
+  a.x_own = a.x[d->rank];
+  a.x_scale_own = a.x_scale[d->rank];
   a.w = static_cast<const uint8_t*>(w);
   a.w_scale = f8 ? w_scale : nullptr;
   a.recv_x = static_cast<uint8_t*>(recv_x);
@@ -706,9 +728,12 @@ ovl_status a2a_run(const a2a_desc* d, bool f8, const void* const* x, const float
   int P = 0;
   if (mode == OVL_MODE_FUSED) {
     // Few dedicated producers: consumers take chunks themselves whenever
-    // the slice they need is behind (measured with 256x256 tiles: 16
-    // producers beat 8 and 64).
-    P = req ? (int)req : 2 * kA2aXcds;
+    // the slice they need is behind.  Measured with 256x256 tiles: 16
+    // producers beat 8 and 64 while every tile waited for a copied slice;
+    // with the own-slice tiles reading in place, 32 (fused 622-644 us)
+    // beat 16 (664-675), 24 and 48 (640-662) and 64 (689) for bf16 rows.
+    // FP8 rows (half the bytes) keep 16.
+    P = req ? (int)req : (f8 ? 2 : 4) * kA2aXcds;
     if (P >= resident) return OVL_EINVAL;
   }
   int64_t Cn = resident - P;
