@@ -84,10 +84,11 @@ constexpr int kMaxWaves = 8;
 // of block i, so that a lane always has a block in flight (vector memory
 // counters complete in order: waiting for the loads does not wait for the
 // stores issued after them).
-template <int NT>
+template <int NT, bool AGENT = false>
 __device__ inline void copy_block(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int64_t rows,
                                   int64_t cols, int64_t ld) {
   constexpr int U = 8;
+  const rsrc_t dr = make_rsrc(dst, rows * ld * 2);  // AGENT: the stores go through a buffer resource
   const uint32_t vpr = (uint32_t)(cols / 8);
   const uint32_t total = (uint32_t)(rows * vpr);
   const uint32_t step_r = NT / vpr, step_c = NT % vpr;
@@ -114,7 +115,12 @@ __device__ inline void copy_block(const uint16_t* __restrict__ src, uint16_t* __
   auto store = [&](const Blk& b) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
-      if (b.off[j] != ~0u) st16(dst + b.off[j], b.v[j]);
+      if (b.off[j] != ~0u) {
+        if constexpr (AGENT)
+          __builtin_amdgcn_raw_buffer_store_b128(b.v[j], dr, (int)(b.off[j] * 2), 0, kAuxAgent);
+        else
+          st16(dst + b.off[j], b.v[j]);
+      }
   };
   Blk x, y;
   if (blocks > 0) load(0, x);
@@ -146,8 +152,17 @@ constexpr int kBootBits = 2048 * 32;  // presence bitmap: n_boot * batches <= th
 
 // Copies one flag unit into the gathered buffer and publishes its flag (NT
 // threads per workgroup).
+// `agent`: the unit is written with agent-scope stores and published
+// without the release fence.  Used for the bootstrap units (moved by every
+// workgroup at once), small units (at most 64 KiB) and the copy-only
+// launch: there the per-die serialised L2 writebacks of the fences, not the
+// bytes, bound the copy (skinny 128x7168x8192 fused 61.0 -> 58.6 us; the
+// 8192 x 4096 copy alone 41 -> 33 us).  Large units of the fused launch's
+// producers keep plain stores and the fence: with agent-scope stores there
+// the copy ran beside the GEMM's traffic slower (last unit published at
+// 146 against 127 us) and the fused launch took 250-253 against 240-242 us.
 template <int NT>
-__device__ inline void move_unit(const AgArgs& a, int u) {
+__device__ inline void move_unit(const AgArgs& a, int u, bool agent_hint = false) {
   const int bt = u % a.batches;
   const int sp = u / a.batches;
   const int p = sp % a.panels;
@@ -156,20 +171,30 @@ __device__ inline void move_unit(const AgArgs& a, int u) {
   const int64_t rows = min((int64_t)a.unit_rows, a.shard_m - r0);
   const int64_t c0 = (int64_t)bt * a.batch_cols;
   const int64_t cols = min((int64_t)a.batch_cols, a.k - c0);
-  copy_block<NT>(a.shards[s] + r0 * a.k + c0, a.g + ((int64_t)s * a.shard_m + r0) * a.k + c0, rows, cols, a.k);
-  wg_publish(a.flags + (int64_t)u * a.flag_stride, a.epoch);
+  const bool agent = agent_hint || rows * cols * 2 <= 64 * 1024;
+  int64_t* flag = a.flags + (int64_t)u * a.flag_stride;
+  if (agent) {
+    copy_block<NT, true>(a.shards[s] + r0 * a.k + c0, a.g + ((int64_t)s * a.shard_m + r0) * a.k + c0, rows, cols,
+                         a.k);
+    wave_drain();
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(flag, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    copy_block<NT>(a.shards[s] + r0 * a.k + c0, a.g + ((int64_t)s * a.shard_m + r0) * a.k + c0, rows, cols, a.k);
+    wg_publish(flag, a.epoch);
+  }
   if (a.trace && threadIdx.x == 0) a.trace[u] = now_ticks();
 }
 
 // Moves the units at producer-order positions w, w + P, ..., skipping the
 // bootstrap panels' units when sc is given (those were moved already).
 template <int NT>
-__device__ inline void produce(const AgArgs& a, int w, int P, const Sched* sc) {
+__device__ inline void produce(const AgArgs& a, int w, int P, const Sched* sc, bool agent = false) {
   for (int i = w; i < a.num_units; i += P) {
     const int u = uniform(a.order ? a.order[i] : i);
     if (u < 0 || u >= a.num_units) continue;  // not a unit index: nothing to move
     if (sc && uniform(sc->bidx[u / a.batches]) >= 0) continue;
-    move_unit<NT>(a, u);
+    move_unit<NT>(a, u, agent);
   }
 }
 
@@ -181,11 +206,11 @@ __device__ inline void produce_boot(const AgArgs& a, int w, int G, const Sched& 
   const int items = sc.n_boot * a.batches;
   for (int i = w; i < items; i += G)
     if (uniform((sc.present[i >> 5] >> (i & 31)) & 1u))
-      move_unit<NT>(a, uniform(sc.boot[i / a.batches]) * a.batches + i % a.batches);
+      move_unit<NT>(a, uniform(sc.boot[i / a.batches]) * a.batches + i % a.batches, true);
 }
 
 __global__ __launch_bounds__(kThreads) void ag_produce_kernel(AgArgs a) {
-  produce<kThreads>(a, blockIdx.x, gridDim.x, nullptr);
+  produce<kThreads>(a, blockIdx.x, gridDim.x, nullptr, true);
 }
 
 // ---------------------------------------------------------------- consumer order

@@ -50,6 +50,12 @@ __device__ inline rsrc_t make_rsrc(const void* base, int64_t bytes) {
 __device__ inline float bloadf(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
+// Cache-policy operand of a buffer store that makes it an agent-scope store
+// (the sc1 bit on gfx950): complete at the device's point of coherence once
+// it drains, so data written only with such stores is published by a drain,
+// a barrier and a relaxed flag store, with no release fence.
+constexpr int kAuxAgent = 16;
+
 template <int AUX = 0>
 __device__ inline void bstoref(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, AUX);

@@ -34,9 +34,6 @@ constexpr int kRsXcds = 8;
 // per SIMD (one's MFMAs cover the other's LDS reads; measured faster than 4).
 constexpr int kRsWaves = 8;
 constexpr int kRsThreads = 64 * kRsWaves;
-// Cache-policy operand of a buffer store that makes it an agent-scope store
-// (the sc1 bit on gfx950).
-constexpr int kAuxAgent = 16;
 
 struct RsArgs {
   float* peer_out[kRsMaxRanks];
