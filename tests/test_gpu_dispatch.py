@@ -102,6 +102,30 @@ def test_small_integers_bit_exact_and_modes_agree():
         assert np.array_equal(host(case.y).view(np.uint32), first.view(np.uint32))
 
 
+def test_own_slice_tiles_read_in_place_match_the_copy():
+    # Every own token picks local expert 0, so that expert's first two
+    # m-tiles (256 rows each) hold own-slice rows only: the fused launch
+    # reads them from the own tokens in place, the GEMM-only launch from the
+    # copied slice.  Small integers: both must equal the oracle bit for bit.
+    o = ovl()
+    cfg = _cfg("a2a_own", R=2, T=600, H=128, N=256, topk=1, E=2, rank=0, seed=9)
+    rng = np.random.default_rng(11)
+    topk = [np.zeros((cfg.tokens, 1), dtype=np.int32),
+            rng.integers(0, 2 * cfg.experts_per_rank, (cfg.tokens, 1)).astype(np.int32)]
+    case = A2aCase(cfg, "smallint", topk=topk)
+    for epoch, producers in ((1, 0), (2, 1)):
+        case.y.zero_()
+        assert case.run(epoch, producers=producers)[0] == 0
+        rx, rs, rc = case.check_layout(epoch)
+        assert rc[0, 0] == cfg.tokens  # the own slice: all to local expert 0
+        y_ref = oracle.grouped_gemm(rx, rc, case.w)
+        assert np.array_equal(host(case.y), y_ref.astype(np.float32))
+    fused = host(case.y).view(np.uint32).copy()
+    case.y.zero_()
+    assert case.run(3, mode=o.MODE_GEMM_ONLY)[0] == 0
+    assert np.array_equal(host(case.y).view(np.uint32), fused)
+
+
 def test_slices_with_nothing_routed_complete():
     # Every token of every source picks experts of other ranks only.
     cfg = _cfg("a2a_empty", R=3, T=40, E=2, rank=1)
