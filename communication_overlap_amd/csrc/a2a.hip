@@ -731,9 +731,9 @@ ovl_status a2a_run(const a2a_desc* d, bool f8, const void* const* x, const float
     // the slice they need is behind.  Measured with 256x256 tiles: 16
     // producers beat 8 and 64 while every tile waited for a copied slice;
     // with the own-slice tiles reading in place, 32 (fused 622-644 us)
-    // beat 16 (664-675), 24 and 48 (640-662) and 64 (689) for bf16 rows.
-    // FP8 rows (half the bytes) keep 16.
-    P = req ? (int)req : (f8 ? 2 : 4) * kA2aXcds;
+    // beat 16 (664-675), 24 and 48 (640-662) and 64 (689) for bf16 rows,
+    // and for FP8 rows 32 (447-448) beat 8, 16, 24 and 48 (451-492).
+    P = req ? (int)req : 4 * kA2aXcds;
     if (P >= resident) return OVL_EINVAL;
   }
   int64_t Cn = resident - P;
