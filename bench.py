@@ -313,6 +313,19 @@ def side_workloads(reps, flush):
     from communication_overlap_amd import ovl
     res = {}
 
+    # The small R=2 AllGather -> GEMM (128x256x256, 32x32 flag tiles): a
+    # latency-bound correctness workload; its time is reported, with no target.
+    cfg = synth.CONFIGS["ag_r2_128x256x256"]
+    log(f"[bench] side {cfg.name}")
+    sm = AgBench(cfg, tiles_per_flag=1)
+    sm.run()
+    t = timed_reps(lambda: sm.run(), reps, flush)
+    gemm = timed_reps(lambda: sm.run(ovl.MODE_GEMM_ONLY), reps, flush)
+    sm.check()
+    res[cfg.name] = {"fused_us": t, "gemm_only_us": gemm, "flag_units": sm.plan.num_units,
+                     "TFLOPs": cfg.flops() / (t["median_us"] * 1e-6) / 1e12}
+    del sm
+
     # Skinny decode-like AllGather -> GEMM (HBM bound: B is 117 MB).
     cfg = synth.CONFIGS["ag_r8_skinny_128x7168x8192"]
     log(f"[bench] side {cfg.name}")
