@@ -565,8 +565,17 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
       op.n0 = (int64_t)nt * TBN;
       op.n_valid = a.n;
       op.k = a.hidden;
-      gemm_tile<kGbm, TBN, 64, 0, true, NW>(acc, op, 0, lds, [](int64_t, int64_t) {});
-      acc_store_rows<kGbm, TBN, NW>(acc, a.y, a.n, (int64_t)a.ranks * a.cap, tab, op.n0, a.n);
+      if (a.n - op.n0 <= TBN / 2) {
+        // The last column block is at most half a tile wide (1408 = 5.5 x
+        // 256): a half-width tile does half the MFMA work, with the same
+        // K order per element (so the same bits).
+        Acc<kGbm, TBN / 2, NW> acc2;
+        gemm_tile<kGbm, TBN / 2, 64, 0, true, NW>(acc2, op, 0, lds, [](int64_t, int64_t) {});
+        acc_store_rows<kGbm, TBN / 2, NW>(acc2, a.y, a.n, (int64_t)a.ranks * a.cap, tab, op.n0, a.n);
+      } else {
+        gemm_tile<kGbm, TBN, 64, 0, true, NW>(acc, op, 0, lds, [](int64_t, int64_t) {});
+        acc_store_rows<kGbm, TBN, NW>(acc, a.y, a.n, (int64_t)a.ranks * a.cap, tab, op.n0, a.n);
+      }
     }
   }
 }
