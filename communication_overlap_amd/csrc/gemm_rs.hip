@@ -60,7 +60,62 @@ struct RsArgs {
 // [j*OR/J, (j+1)*OR/J), OR = tiles_per_block * 256.
 __device__ inline int64_t job_begin(int64_t j, int64_t J, int64_t OR) { return j * OR / J; }
 
-__device__ void reduce_job(const RsArgs& a, int64_t j, int64_t J, bool& timed_out) {
+// 16 bytes per lane from global memory straight into LDS at lds_block +
+// 16 * lane (gfx950's global load to LDS; no registers hold the data).
+__device__ inline void gload16_to_lds(const void* g, uint32_t lds_block) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds_block), "v"(g) : "memory", "m0");
+}
+
+// Rows [q0, q1) of the own-row space: out = acc + ((P_a + P_b) + ...), the
+// partials in ascending peer order.  64 lanes of 16 bytes cover one
+// 256-column row.  Each wave stages the accumulator row and the R-1 partial
+// rows of `rw` rows (1 KiB each) in its own 16 KiB of the idle GEMM stage
+// area with global-to-LDS loads, all issued before the first add, then
+// sums them: twice the rows in flight that registers allowed (measured:
+// fused 169 -> 156-163 us, reduction-included GEMM-only 163-165 -> 151-152
+// us at 8192x4096x1792 over 8 ranks).  Index arithmetic is 32-bit (a block
+// has fewer than 2^31 elements).
+__device__ void reduce_rows_lds(const RsArgs& a, int64_t q0, int64_t q1, uint16_t* lds) {
+  uint8_t* l8 = reinterpret_cast<uint8_t*>(lds);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int R = a.ranks;
+  const int rw = R <= 8 ? 2 : 1;
+  const uint32_t wbase = lds_addr(l8) + (uint32_t)w * 16384u;
+  const int tc = a.tc, n = (int)a.n, bm = (int)a.bm;
+  for (int q = (int)q0 + w * rw; q < (int)q1; q += kRsWaves * rw) {
+    for (int u = 0; u < rw; ++u) {
+      const int qq = q + u;
+      const int t = qq / kRsTile;
+      const int row = (t / tc) * kRsTile + (qq % kRsTile);
+      const int col = (t % tc) * kRsTile + lane * 4;
+      if (qq >= (int)q1 || row >= bm) continue;  // wave-uniform
+      if (col >= n) continue;                    // lanes past N load nothing
+      const int off = row * n + col;
+      const uint32_t slot = wbase + (uint32_t)u * 8192u;
+      gload16_to_lds(a.out + off, slot);
+      int si = 1;
+#pragma unroll
+      for (int p = 0; p < kRsMaxRanks; ++p)
+        if (p < R && p != a.rank) gload16_to_lds(a.peer_in[p] + off, slot + 1024u * (uint32_t)si++);
+    }
+    wave_drain();
+    for (int u = 0; u < rw; ++u) {
+      const int qq = q + u;
+      const int t = qq / kRsTile;
+      const int row = (t / tc) * kRsTile + (qq % kRsTile);
+      const int col = (t % tc) * kRsTile + lane * 4;
+      if (qq >= (int)q1 || row >= bm || col >= n) continue;
+      const uint8_t* slot = l8 + (size_t)w * 16384 + (size_t)u * 8192 + (size_t)lane * 16;
+      const f32x4 acc = *OVL_LDS(const f32x4, slot);
+      f32x4 sum = *OVL_LDS(const f32x4, slot + 1024);
+      for (int si = 2; si < R; ++si) sum += *OVL_LDS(const f32x4, slot + 1024 * si);
+      *reinterpret_cast<f32x4*>(a.out + (int64_t)row * n + col) = acc + sum;
+    }
+  }
+}
+
+__device__ void reduce_job(const RsArgs& a, int64_t j, int64_t J, bool& timed_out, uint16_t* lds) {
   const int tpb = a.tr * a.tc;
   const int64_t OR = (int64_t)tpb * kRsTile;
   const int64_t q0 = job_begin(j, J, OR), q1 = job_begin(j + 1, J, OR);
@@ -113,51 +168,7 @@ __device__ void reduce_job(const RsArgs& a, int64_t j, int64_t J, bool& timed_ou
     wave_acquire();
   }
   __syncthreads();
-  // 64 lanes of 16 bytes cover one 256-column row; each wave takes U rows
-  // per pass (8 rows per workgroup) and issues all of their loads
-  // (accumulator and R-1 partials) before the first add.
-  constexpr int U = 8 / kRsWaves;
-  const int lane = threadIdx.x & 63, rsub = threadIdx.x >> 6;
-  for (int64_t q = q0 + rsub; q < q1; q += kRsWaves * U) {
-    int64_t off[U];
-    bool ok[U];
-    f32x4 acc[U], v[U][kRsMaxRanks];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t qq = q + kRsWaves * u;
-      const int64_t t = qq / kRsTile;
-      const int64_t row = (t / a.tc) * kRsTile + (qq % kRsTile);
-      const int64_t col = (t % a.tc) * kRsTile + lane * 4;
-      ok[u] = qq < q1 && row < a.bm && col < a.n;
-      off[u] = ok[u] ? row * a.n + col : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (!ok[u]) continue;
-      acc[u] = *reinterpret_cast<const f32x4*>(a.out + off[u]);
-#pragma unroll
-      for (int p = 0; p < kRsMaxRanks; ++p)
-        if (p < a.ranks && p != a.rank)
-          v[u][p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.peer_in[p] + off[u]));
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (!ok[u]) continue;
-      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-      bool first = true;
-#pragma unroll
-      for (int p = 0; p < kRsMaxRanks; ++p) {
-        if (p >= a.ranks || p == a.rank) continue;
-        if (first) {
-          sum = v[u][p];
-          first = false;
-        } else {
-          sum += v[u][p];
-        }
-      }
-      *reinterpret_cast<f32x4*>(a.out + off[u]) = acc[u] + sum;
-    }
-  }
+  reduce_rows_lds(a, q0, q1, lds);
 }
 
 template <int SYNC>
@@ -210,7 +221,7 @@ __global__ __launch_bounds__(kRsThreads, 1) void gemm_rs_kernel(RsArgs a) {
     if (blk != a.rank) {
       acc_store<BM, BN, kAuxAgent, kRsWaves>(acc, a.peer_out[blk], a.n, m0, op.n0, a.bm, a.n);
       if (SYNC) publish(a.out_flags + ((int64_t)blk * tpb + t) * a.flag_stride);
-      reduce_job(a, pj, J, timed_out);
+      reduce_job(a, pj, J, timed_out, lds);
     } else {
       acc_store<BM, BN, kAuxAgent, kRsWaves>(acc, a.out, a.n, m0, op.n0, a.bm, a.n);
       if (J > 0) publish(a.own_flags + t);
