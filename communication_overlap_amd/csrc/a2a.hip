@@ -139,6 +139,12 @@ __global__ __launch_bounds__(kThreads) void a2a_layout_kernel(A2aArgs a) {
   int base_total, cnt_total;
   block_excl_scan(lt, &base_total, smem);
   int pos = base_total + block_excl_scan(eq, &cnt_total, smem);
+  // A slice holds at most cap rows.  Only routing rows that repeat a local
+  // expert (which the call's contract excludes) can ask for more; then the
+  // rows past cap are dropped, the counts are clipped so that every later
+  // step stays inside the slice, and the run reports OVL_ESHAPE.
+  const int64_t end = min((int64_t)base_total + cnt_total, a.cap);
+  const int cnt = (int)max((int64_t)0, end - base_total);
   if (eq) {
     // Loads in batches again: the stores below may alias them, so a plain
     // loop would wait out one load per entry.
@@ -149,11 +155,15 @@ __global__ __launch_bounds__(kThreads) void a2a_layout_kernel(A2aArgs a) {
       for (int q = 0; q < B; ++q) v[q] = i + q < i1 ? idx[i + q] : -1;
 #pragma unroll
       for (int q = 0; q < B; ++q)
-        if (v[q] - e_lo == e) dst[pos++] = (int32_t)((i + q) / a.topk_n);
+        if (v[q] - e_lo == e) {
+          if (pos < end) dst[pos] = (int32_t)((i + q) / a.topk_n);
+          ++pos;
+        }
     }
   }
   if (threadIdx.x == 0) {
-    a.recv_count[s * a.experts + e] = cnt_total;
+    if (cnt < cnt_total) report_error(a.err, OVL_ESHAPE, kSiteA2aCap, s, (int64_t)base_total + cnt_total, a.cap);
+    a.recv_count[s * a.experts + e] = cnt;
     if (e == 0) a.counters[s] = 0;
     if (blockIdx.x == 0) *a.ticket = 0;
   }
@@ -445,33 +455,40 @@ __global__ __launch_bounds__(kThreads) void a2a_produce_kernel(A2aArgs a) {
 // while copying work remains: measured better than helping only with the
 // chunks up to s).  Ends with the acquire done by wave 0 and a workgroup
 // barrier.  Returns false on timeout.
+// The result is the same in every wave: wave 0's poll result goes through
+// LDS, because callers loop over this call and every barrier in it.
 __device__ bool wait_slice_helping(const A2aArgs& a, const Geometry* g, int s, int* sh) {
   const int total = uniform(g->chunk_base[a.ranks]);
   const int64_t* flag = a.flags + (int64_t)s * a.flag_stride;
-  bool ok = true;
+  int st;
   for (;;) {
     if (threadIdx.x == 0) {
-      int st = 2;  // 0 ready, 1 help, 2 wait
-      if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= a.epoch)
-        st = 0;
-      else if (__hip_atomic_load(a.ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < total)
-        st = 1;
-      sh[1] = st;
+      int v = 2;  // 0 ready, 1 help, 2 wait
+      const int64_t f = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (f >= a.epoch) {
+        v = 0;
+        check_epoch(a.err, kSiteA2aSlice, s, f, a.epoch);
+      } else if (__hip_atomic_load(a.ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < total) {
+        v = 1;
+      }
+      sh[1] = v;
     }
     __syncthreads();
-    const int st = uniform(sh[1]);
+    st = uniform(sh[1]);
     __syncthreads();
-    if (st == 1) {
-      const int ch = take_chunk(a, total, sh);
-      if (ch < total) a2a_copy_chunk(a, g, ch);
-      continue;
-    }
-    if (st == 2 && threadIdx.x < 64) ok = wave_poll(flag, a.epoch, a.spin_limit, a.err, kSiteA2aSlice, s);
-    break;
+    if (st != 1) break;
+    const int ch = take_chunk(a, total, sh);
+    if (ch < total) a2a_copy_chunk(a, g, ch);
   }
-  if (threadIdx.x < 64) wave_acquire();
+  if (threadIdx.x < 64) {
+    const bool ok = st != 2 || wave_poll(flag, a.epoch, a.spin_limit, a.err, kSiteA2aSlice, s);
+    wave_acquire();
+    if (threadIdx.x == 0) sh[1] = ok;
+  }
   __syncthreads();
-  return ok;
+  const int ok = uniform(sh[1]);
+  __syncthreads();  // sh[1] is rewritten by the next call
+  return ok != 0;
 }
 
 template <bool WAIT, bool F8>
@@ -635,7 +652,11 @@ ovl_status a2a_run(const a2a_desc* d, bool f8, const void* const* x, const float
                    const int32_t* const* topk_idx, const void* w, const float* w_scale, void* recv_x,
                    float* recv_scale, int32_t* recv_src, int32_t* recv_count, float* y, int64_t* flags,
                    void* workspace, int64_t epoch, const ovl_opts* opts, hipStream_t stream) {
-  if (!d || !recv_count || !flags || !workspace) return OVL_EINVAL;
+  if (!d) return OVL_EINVAL;
+  // The grouped-GEMM tile: the default or the one implemented for the row type.
+  const int32_t tile_n = f8 ? kGbn8 : kGbn;
+  if (!((d->tile_m == 0 && d->tile_n == 0) || (d->tile_m == kGbm && d->tile_n == tile_n))) return OVL_EUNSUPPORTED;
+  if (!recv_count || !flags || !workspace) return OVL_EINVAL;
   const bool empty = d->tokens == 0;  // nothing to read or write but counts and flags
   if (!empty && (!x || !topk_idx || !recv_x || !recv_src || (f8 && (!x_scale || !recv_scale)))) return OVL_EINVAL;
   if (d->ranks < 1 || d->rank < 0 || d->rank >= d->ranks) return OVL_EINVAL;

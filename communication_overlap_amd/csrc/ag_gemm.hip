@@ -53,6 +53,7 @@ struct AgArgs {
   float* partial;     // [splits][m][n]
   int64_t* counters;  // [tiles][2], zero between launches
   int64_t* trace;     // optional timestamps: [num_units] publishes, then [items][kTraceItem]
+  uint32_t jitter;    // producers sleep up to this many intervals before each unit (test aid)
 };
 
 // The constant-rate (100 MHz) real-time counter, common to all compute units.
@@ -186,6 +187,18 @@ __device__ inline void move_unit(const AgArgs& a, int u, bool agent_hint = false
   if (a.trace && threadIdx.x == 0) a.trace[u] = now_ticks();
 }
 
+// Test aid: a pause of h(u, epoch) mod (jitter + 1) sleeps of about 64
+// clocks before unit u is moved, h a fixed integer hash, so that units land
+// in an uneven, shuffled order.
+__device__ inline void jitter_pause(const AgArgs& a, int u) {
+  uint32_t h = (uint32_t)u * 0x9E3779B1u ^ (uint32_t)a.epoch * 0x85EBCA77u;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  const uint32_t n = uniform((int)(h % (a.jitter + 1)));
+  for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(1);
+}
+
 // Moves the units at producer-order positions w, w + P, ..., skipping the
 // bootstrap panels' units when sc is given (those were moved already).
 template <int NT>
@@ -193,7 +206,11 @@ __device__ inline void produce(const AgArgs& a, int w, int P, const Sched* sc, b
   for (int i = w; i < a.num_units; i += P) {
     const int u = uniform(a.order ? a.order[i] : i);
     if (u < 0 || u >= a.num_units) continue;  // not a unit index: nothing to move
-    if (sc && uniform(sc->bidx[u / a.batches]) >= 0) continue;
+    if (a.jitter) jitter_pause(a, u);
+    // Bootstrap units were moved already.  The bootstrap is off (n_boot = 0)
+    // when the panels outnumber the bidx table, which then holds no entry for
+    // most panels.
+    if (sc && sc->n_boot > 0 && uniform(sc->bidx[u / a.batches]) >= 0) continue;
     move_unit<NT>(a, u, agent);
   }
 }
@@ -392,6 +409,7 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
         }
         __builtin_amdgcn_s_sleep(2);
       }
+      check_epoch(a.err, kSiteAgBarrier, u, v, a.epoch);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
@@ -496,8 +514,9 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
         for (int i = lane; i < cnt; i += 64) {
           const int bt = ready + 1 + i / npan;
           const int64_t u = (int64_t)(sp_lo + i % npan) * a.batches + bt;
-          if (__hip_atomic_load(a.flags + u * a.flag_stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.epoch)
-            bad = min(bad, bt);
+          const int64_t v = __hip_atomic_load(a.flags + u * a.flag_stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (v < a.epoch) bad = min(bad, bt);
+          check_epoch(a.err, kSiteAgUnit, u, v, a.epoch);
         }
         for (int d = 1; d < 64; d <<= 1) bad = min(bad, __shfl_xor(bad, d, 64));
         bad = uniform(bad);
@@ -831,6 +850,7 @@ extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, c
   a.err = static_cast<ErrRec*>(workspace);
   a.order = producer_order;
   a.trace = opts ? opts->trace : nullptr;
+  a.jitter = opts ? opts->jitter : 0;
   a.shard_m = d.shard_m;
   a.m = p->m;
   a.k = d.k;

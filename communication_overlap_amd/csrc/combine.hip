@@ -233,9 +233,12 @@ __device__ void cb_wait_in(const CombineArgs& a) {
     for (uint64_t polls = 0;; ++polls) {
       bool missing = false;
       for (int q = lane_id(); q < a.ranks; q += 64)
-        if (q != a.rank)
-          missing |= __hip_atomic_load(a.in_flags + (int64_t)q * a.flag_stride, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT) < a.epoch;
+        if (q != a.rank) {
+          const int64_t v =
+              __hip_atomic_load(a.in_flags + (int64_t)q * a.flag_stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          missing |= v < a.epoch;
+          check_epoch(a.err, kSiteCbIn, q, v, a.epoch);
+        }
       if (!__ballot(missing)) break;
       if (polls >= a.spin_limit) {
         for (int q = 0; q < a.ranks; ++q)

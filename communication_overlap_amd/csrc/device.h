@@ -28,7 +28,7 @@ static_assert(sizeof(ErrRec) == 64, "error record size");
 
 enum : int32_t {
   kSiteAgUnit = 1, kSiteAgBarrier = 2, kSiteRsIn = 3, kSiteA2aSlice = 4, kSiteRsOwn = 5, kSiteAgSplit = 6,
-  kSiteCbIn = 7, kSiteRing = 8
+  kSiteCbIn = 7, kSiteRing = 8, kSiteA2aCap = 9
 };
 
 __device__ inline void report_error(ErrRec* e, int32_t code, int32_t site, int64_t index,
@@ -42,6 +42,17 @@ __device__ inline void report_error(ErrRec* e, int32_t code, int32_t site, int64
 }
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
+
+// A flag above the awaited epoch breaks the epoch rule (epochs increase from
+// run to run, and a producer stores exactly the run's epoch): the slot holds
+// a signal of a later run, or the caller awaits a stale epoch.  The wait
+// still counts the flag as set (the predicate is flag >= epoch, the pages'
+// ge wait), so nothing blocks, but the run reports OVL_EEPOCH with the slot
+// and the value seen: a consumer may have read data its producer had not
+// written yet.  Any lane may call this with its own value.
+__device__ inline void check_epoch(ErrRec* e, int32_t site, int64_t index, int64_t v, int64_t epoch) {
+  if (v > epoch) report_error(e, -4 /* OVL_EEPOCH */, site, index, v, epoch);
+}
 
 // A value every lane of the workgroup holds alike (read from LDS after a
 // barrier, or from a broadcast), made a scalar.  Loop bounds and branches
@@ -67,6 +78,7 @@ __device__ inline bool wave_poll(const int64_t* flag, int64_t epoch, uint64_t sp
     __builtin_amdgcn_s_sleep(2);
     v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  if (lane_id() == 0) check_epoch(err, site, index, v, epoch);
   return true;
 }
 

@@ -151,7 +151,9 @@ __device__ void reduce_job(const RsArgs& a, int64_t j, int64_t J, bool& timed_ou
       for (int64_t i = lane_id(); i < nflags; i += 64) {
         int64_t idx;
         int32_t site;
-        missing |= __hip_atomic_load(flag_at(i, &idx, &site), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.epoch;
+        const int64_t v = __hip_atomic_load(flag_at(i, &idx, &site), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        missing |= v < a.epoch;
+        check_epoch(a.err, site, idx, v, a.epoch);
       }
       if (!__ballot(missing)) break;
       if (polls >= a.spin_limit) {

@@ -142,7 +142,9 @@ __global__ __launch_bounds__(kThreads) void ring_kernel(RingArgs a) {
     if (s >= 1 && a.wait) {
       if (threadIdx.x < 64) {
         const int64_t f = ring_flag(a, r, s, j);
-        wave_poll(a.flags + f * a.flag_stride, a.epoch, a.spin_limit, a.err, kSiteRing, f);
+        // Poll, then an agent-scope acquire before the workgroup reads the
+        // predecessor's partial (the barrier below hands it to every wave).
+        wave_wait(a.flags + f * a.flag_stride, a.epoch, a.spin_limit, a.err, kSiteRing, f);
       }
       __syncthreads();
     }

@@ -40,6 +40,7 @@ EXPORTS = (
     "ovl_flags_reset", "ovl_check", "ovl_strerror", "ovl_copy",
     "ring_allreduce_flags_bytes", "ring_allreduce_workspace_bytes", "ring_allreduce_run",
     "fp8_quantize_rows", "a2a_dispatch_grouped_gemm_fp8_run", "ag_gemm_trace_bytes",
+    "ag_gemm_row_tiles", "ag_gemm_tile_rows", "ag_gemm_consumer_order",
 )
 
 
@@ -50,7 +51,8 @@ class OvlError(RuntimeError):
 
 
 class Opts(Structure):
-    _fields_ = [("mode", c_uint32), ("producers", c_uint32), ("spin_limit", c_uint64), ("trace", c_void_p)]
+    _fields_ = [("mode", c_uint32), ("producers", c_uint32), ("spin_limit", c_uint64), ("trace", c_void_p),
+                ("jitter", c_uint32), ("reserved", c_uint32)]
 
 
 class AgGemmDesc(Structure):
@@ -66,7 +68,7 @@ class GemmRsDesc(Structure):
 class A2aDesc(Structure):
     _fields_ = [("ranks", c_int32), ("rank", c_int32), ("tokens", c_int64), ("hidden", c_int64), ("n", c_int64),
                 ("topk", c_int32), ("num_experts", c_int32), ("experts_per_rank", c_int32),
-                ("flag_stride", c_int32)]
+                ("flag_stride", c_int32), ("tile_m", c_int32), ("tile_n", c_int32)]
 
 
 class RingDesc(Structure):
@@ -100,6 +102,10 @@ def lib() -> ctypes.CDLL:
     L.ag_gemm_splits.restype = c_int32
     L.ag_gemm_trace_bytes.argtypes = [c_void_p]
     L.ag_gemm_trace_bytes.restype = c_size_t
+    L.ag_gemm_row_tiles.argtypes = [c_void_p]
+    L.ag_gemm_row_tiles.restype = c_int32
+    L.ag_gemm_tile_rows.argtypes = [c_void_p]
+    L.ag_gemm_tile_rows.restype = c_int32
     L.ag_gemm_run.argtypes = [c_void_p, POINTER(c_void_p), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                               c_int64, c_void_p, POINTER(Opts), c_void_p]
     L.ag_gemm_run.restype = st
@@ -176,8 +182,8 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
-def _opts(mode: int, producers: int, spin_limit: int, trace=None) -> Opts:
-    return Opts(mode, producers, spin_limit, _ptr(trace))
+def _opts(mode: int, producers: int, spin_limit: int, trace=None, jitter: int = 0) -> Opts:
+    return Opts(mode, producers, spin_limit, _ptr(trace), jitter, 0)
 
 
 def _check(status: int, where: str, raise_on_error: bool) -> int:
@@ -230,6 +236,15 @@ class AgGemmPlan:
     def trace_bytes(self) -> int:
         return lib().ag_gemm_trace_bytes(self.handle)
 
+    @property
+    def tile_rows(self) -> int:
+        """Rows of the consumer's output tile (chosen by the library)."""
+        return lib().ag_gemm_tile_rows(self.handle)
+
+    @property
+    def row_tiles(self) -> int:
+        return lib().ag_gemm_row_tiles(self.handle)
+
 
 def ag_gemm_plan(*args, **kw) -> AgGemmPlan:
     return AgGemmPlan(*args, **kw)
@@ -237,9 +252,9 @@ def ag_gemm_plan(*args, **kw) -> AgGemmPlan:
 
 def ag_gemm_run(plan: AgGemmPlan, shards, b, gathered, c, flags, workspace, epoch: int, producer_order=None,
                 mode: int = MODE_FUSED, producers: int = 0, spin_limit: int = 0, stream=None,
-                raise_on_error: bool = True, trace=None) -> int:
+                raise_on_error: bool = True, trace=None, jitter: int = 0) -> int:
     arr = _ptr_array(shards)
-    o = _opts(mode, producers, spin_limit, trace)
+    o = _opts(mode, producers, spin_limit, trace, jitter)
     st = lib().ag_gemm_run(plan.handle, arr, _ptr(b), _ptr(gathered), _ptr(c), _ptr(flags), _ptr(workspace),
                            epoch, _ptr(producer_order), byref(o), _stream(stream))
     return _check(st, "ag_gemm_run", raise_on_error)
@@ -270,8 +285,9 @@ def gemm_rs_run(desc: GemmRsDesc, a, b, peer_out, peer_in, out, out_flags, in_fl
 
 # ------------------------------------------------------------------ dispatch + grouped GEMM
 
-def a2a_desc(ranks, rank, tokens, hidden, n, topk, num_experts, experts_per_rank, flag_stride=8) -> A2aDesc:
-    return A2aDesc(ranks, rank, tokens, hidden, n, topk, num_experts, experts_per_rank, flag_stride)
+def a2a_desc(ranks, rank, tokens, hidden, n, topk, num_experts, experts_per_rank, flag_stride=8,
+             tile_m=0, tile_n=0) -> A2aDesc:
+    return A2aDesc(ranks, rank, tokens, hidden, n, topk, num_experts, experts_per_rank, flag_stride, tile_m, tile_n)
 
 
 def a2a_flags_bytes(desc: A2aDesc) -> int:

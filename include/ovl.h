@@ -87,6 +87,11 @@ typedef struct ovl_opts {
   uint64_t spin_limit;  /* polls before a wait gives up (OVL_ETIMEOUT); 0 = default (~2^22) */
   int64_t* trace;       /* AG-GEMM only: device buffer of ag_gemm_trace_bytes() bytes that the
                            run fills with timestamps (see there), or NULL for none */
+  uint32_t jitter;      /* AG-GEMM only, a test aid: before moving each unit a producer
+                           workgroup sleeps h(unit, epoch) mod (jitter + 1) intervals of about
+                           64 shader clocks (h a fixed integer hash), so that units arrive in
+                           shuffled, uneven order; 0 = off.  Results do not depend on it. */
+  uint32_t reserved;    /* 0 */
 } ovl_opts;
 
 /* Size in bytes of the device-side error record at the start of every
@@ -116,14 +121,23 @@ typedef struct ovl_opts {
  * Swizzling, start on local data); the others follow in the order their
  * first K-batch arrives under `producer_order`.
  * ---------------------------------------------------------------------- */
+/* Tiles: the caller's tile_m x tile_n is the tile of the communication side
+ * (the flag unit's rows, and the K-tile width that tiles_per_flag counts).
+ * The consumer's output tile is chosen by the library from the problem
+ * size: 256 x 256 when M and N are both at least 256 and there are at least
+ * 128 such tiles, else 128 x 128 (then split along K when the tiles would
+ * fill less than half the compute units; see ag_gemm_splits).  Any
+ * consumer tile maps onto whole flag units: a tile waits on every unit its
+ * rows and K-step touch, so the two tilings need not agree.
+ * ag_gemm_tile_rows() reports the choice. */
 typedef struct ag_gemm_desc {
   int32_t ranks;           /* R, 1..16 */
   int32_t rank;            /* this rank, 0 <= rank < R */
   int64_t shard_m;         /* rows per shard, >= 1 */
   int64_t k;               /* >= 8, multiple of 8 */
   int64_t n;               /* >= 8, multiple of 8 */
-  int32_t tile_m;          /* flag-unit rows (capped at shard_m), >= 1 */
-  int32_t tile_n;          /* K-tile width for tiles_per_flag, multiple of 8 */
+  int32_t tile_m;          /* flag-unit rows (capped at shard_m), >= 1; any value */
+  int32_t tile_n;          /* K-tile width for tiles_per_flag, multiple of 8; any such value */
   int32_t tiles_per_flag;  /* K-tiles per flag unit, >= 0 (0 = all of k) */
   int32_t flag_stride;     /* bytes between flag slots, multiple of 8, >= 8 */
 } ag_gemm_desc;
@@ -287,6 +301,12 @@ typedef struct a2a_desc {
   int32_t num_experts;       /* global experts = ranks * experts_per_rank */
   int32_t experts_per_rank;  /* 1..64 */
   int32_t flag_stride;       /* bytes, multiple of 8, >= 8 */
+  int32_t tile_m, tile_n;    /* grouped-GEMM tile: tile_m rows of one expert's received rows
+                                (taken across slices) x tile_n output columns.  0, 0 = the
+                                default; the implemented tiles are 256 x 256 for bf16 rows
+                                (a last column block at most half a tile wide runs as 256 x 128)
+                                and 256 x 128 for FP8 rows.  Any other pair: OVL_EUNSUPPORTED.
+                                The combine does not read them. */
 } a2a_desc;
 
 size_t a2a_flags_bytes(const a2a_desc* desc);      /* ranks * flag_stride */
@@ -440,12 +460,22 @@ ovl_status ovl_flags_reset(int64_t* flags, size_t flag_bytes, void* workspace, s
                            hipStream_t stream);
 
 /* Waits for `stream`, then returns the status recorded on the device in
- * `workspace` (OVL_OK or OVL_ETIMEOUT; the first wait to give up wins).
- * detail (HOST, may be NULL) receives {site, flag index, observed value,
- * awaited value}; sites: 1 AG-GEMM unit flag, 2 AG-GEMM barrier mode,
- * 3 GEMM-RS in flag, 4 dispatch slice flag, 5 GEMM-RS own-tile flag,
- * 6 AG-GEMM split-K range counter (index = tile), 7 combine in flag (index = peer),
- * 8 ring all-reduce tile flag. */
+ * `workspace` (the first error recorded wins):
+ *  - OVL_ETIMEOUT: a wait exceeded its spin limit;
+ *  - OVL_EEPOCH: a wait found a flag ABOVE the awaited epoch (a signal of a
+ *    later run, or a stale epoch: the pages' wait accepts flag >= epoch, and
+ *    producers store exactly the epoch, so a larger value means the epoch
+ *    rule was broken and a consumer may have run ahead of its producer);
+ *  - OVL_ESHAPE (site 9): a dispatch slice would exceed its capacity (routing
+ *    rows that repeat a local expert); the rows past the capacity were dropped.
+ * detail (HOST, may be NULL) receives {site, index, observed value, awaited
+ * value}; sites: 1 AG-GEMM unit flag, 2 AG-GEMM barrier mode, 3 GEMM-RS in
+ * flag, 4 dispatch slice flag, 5 GEMM-RS own-tile flag, 6 AG-GEMM split-K
+ * range counter (index = tile), 7 combine in flag (index = peer), 8 ring
+ * all-reduce tile flag, 9 dispatch slice capacity (index = source; observed =
+ * rows asked for, awaited = capacity).
+ * workspace = NULL reads the record of the allocation-free calls on the
+ * current device (ag_gemm_run_noalloc). */
 ovl_status ovl_check(const void* workspace, int64_t* detail, hipStream_t stream);
 
 const char* ovl_strerror(ovl_status status);

@@ -166,6 +166,38 @@ def test_run_argument_errors_come_before_any_device_work():
     assert st == o.OVL_EALIGN
 
 
+@pytest.mark.parametrize("tile", [(128, 128), (128, 256), (256, 128), (512, 256), (0, 256)])
+def test_gemm_rs_refuses_tiles_it_does_not_implement(tile):
+    """gemm_rs_run implements 256 x 256 tiles only; every other pair is
+    refused with OVL_EUNSUPPORTED before any device work."""
+    o = ovl()
+    desc = o.gemm_rs_desc(8, 0, 8192, 4096, 1792, tile_m=tile[0], tile_n=tile[1])
+    st = o.gemm_rs_run(desc, 16, 16, [16] * 8, [16] * 8, 16, 16, 16, 16, 1, raise_on_error=False, stream=0)
+    assert st == o.OVL_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("f8,tile,ok", [
+    (False, (0, 0), True), (False, (256, 256), True), (False, (256, 128), False), (False, (128, 128), False),
+    (True, (0, 0), True), (True, (256, 128), True), (True, (256, 256), False), (True, (128, 64), False),
+])
+def test_dispatch_tile_arguments(f8, tile, ok):
+    """The grouped-GEMM tile of the dispatch descriptor: 0 x 0 (default) or
+    the implemented one (bf16 256 x 256, FP8 256 x 128) pass the argument
+    checks; any other pair is refused with OVL_EUNSUPPORTED before any device
+    work.  (An accepted tile fails later on the null row buffers, with
+    OVL_EINVAL: no device is touched either way.)"""
+    o = ovl()
+    ad = o.a2a_desc(2, 0, 16, 64, 64, 2, 4, 2, 8, tile[0], tile[1])
+    lib = o.lib()
+    if f8:
+        st = lib.a2a_dispatch_grouped_gemm_fp8_run(ctypes.byref(ad), None, None, None, None, None, None, None,
+                                                   None, None, None, None, None, 1, None, None)
+    else:
+        st = lib.a2a_dispatch_grouped_gemm_run(ctypes.byref(ad), None, None, None, None, None, None, None, None,
+                                               None, 1, None, None)
+    assert st == (o.OVL_EINVAL if ok else o.OVL_EUNSUPPORTED)
+
+
 def test_flag_and_workspace_sizes():
     o = ovl()
     d = o.gemm_rs_desc(8, 0, 8192, 4096, 1792)

@@ -16,6 +16,14 @@ def ovl():
     return _o
 
 
+# A bf16 quiet NaN.  Before every run that copies (every mode but
+# GEMM_ONLY) the gathered buffer is filled with it, so that a consumer that
+# reads a unit before its producer has written it turns its rows of C into
+# NaN, which the comparison with the oracle cannot miss (a gathered buffer
+# left over from an earlier run would hold the right bits already).
+NAN_BF16 = 0x7FC0
+
+
 class AgCase:
     def __init__(self, cfg, kind="normal", tiles_per_flag=0, flag_stride=8, rank=0):
         o = ovl()
@@ -39,12 +47,15 @@ class AgCase:
     def order(self, epoch, kind="panels"):
         return synth.producer_order(self.cfg.seed, epoch, self.cfg.ranks * self.panels, self.batches, True, kind)
 
-    def run(self, epoch, order=None, mode=0, producers=0, spin_limit=0):
+    def run(self, epoch, order=None, mode=0, producers=0, spin_limit=0, jitter=0, poison=True):
         o = ovl()
         d_order = dev(order) if order is not None else None
-        say(f"  ag_gemm_run {self.cfg.name} epoch={epoch} mode={mode} order={'none' if order is None else 'set'}")
+        if poison and mode != o.MODE_GEMM_ONLY:
+            self.g.fill_(NAN_BF16)
+        say(f"  ag_gemm_run {self.cfg.name} epoch={epoch} mode={mode} order={'none' if order is None else 'set'}"
+            f" jitter={jitter}")
         o.ag_gemm_run(self.plan, self.d_shards, self.d_b, self.g, self.c, self.flags, self.ws, epoch, d_order,
-                      mode=mode, producers=producers, spin_limit=spin_limit)
+                      mode=mode, producers=producers, spin_limit=spin_limit, jitter=jitter)
         return o.ovl_check(self.ws, raise_on_error=False)
 
     def check_gathered_and_flags(self, epoch):
@@ -54,13 +65,23 @@ class AgCase:
         assert np.array_equal(fl, oracle.expected_flags(self.units, self.stride, epoch)), "flag bytes differ"
 
 
-def _full_check(case):
-    g_ref, c_ref = oracle.ag_gemm(case.shards, case.b)
+def _full_check(case, c_ref=None):
+    """Every element of C against the oracle's float64 product."""
+    if c_ref is None:
+        _, c_ref = oracle.ag_gemm(case.shards, case.b)
     c = host(case.c)
+    assert np.isfinite(c).all(), "C holds NaN or Inf: a unit was read before it was written"
     tol = gemm_tol(case.cfg.k, float(np.abs(c_ref).max()))
     err = max_err(c, c_ref)
     assert err <= tol, f"max err {err} > tol {tol}"
     return c
+
+
+def _exact_check(case, c_ref=None):
+    """Small-integer inputs: every element of C equals the exact product."""
+    if c_ref is None:
+        _, c_ref = oracle.ag_gemm(case.shards, case.b)
+    assert np.array_equal(host(case.c), c_ref.astype(np.float32))
 
 
 def _small(name, R, Ms, K, N, tm, tn, seed=5):
@@ -209,29 +230,120 @@ def test_modes_compose_to_the_same_bits():
     _full_check(case)
 
 
+# ------------------------------------------------------------------ 256 x 256 consumer tile, ragged
+
+@pytest.mark.parametrize("kind", ["normal", "smallint"])
+def test_ragged_big_tile_orders_and_modes(kind):
+    """The 256 x 256 consumer tile (the headline's) at a ragged size the
+    oracle finishes at once: 4000 x 2056 x 520 is 16 x 9 tiles with short
+    last rows and columns, shards of 1000 rows straddle the tiles, and
+    K-batches of 128 columns end in an 8-column batch.  Every element of C
+    is compared, over random unit orders, producer jitter, BARRIER and
+    COPY_ONLY + GEMM_ONLY, and the bits must not move."""
+    o = ovl()
+    cfg = _small("ragged_big", 4, 1000, 520, 2056, 256, 64, seed=31)
+    case = AgCase(cfg, kind, tiles_per_flag=2)
+    assert case.plan.tile_rows == 256 and case.plan.splits == 1
+    _, c_ref = oracle.ag_gemm(case.shards, case.b)
+    check = _exact_check if kind == "smallint" else _full_check
+    bits = None
+    for epoch, jitter in ((1, 0), (2, 0), (3, 300)):
+        st, det = case.run(epoch, case.order(epoch, "units"), jitter=jitter)
+        assert st == 0, det
+        case.check_gathered_and_flags(epoch)
+        check(case, c_ref)
+        c = host(case.c).view(np.uint32)
+        if bits is None:
+            bits = c.copy()
+        assert np.array_equal(c, bits), "C bits changed with producer order"
+    case.c.zero_()
+    assert case.run(4, mode=o.MODE_BARRIER)[0] == 0
+    assert np.array_equal(host(case.c).view(np.uint32), bits)
+    case.c.zero_()
+    assert case.run(5, case.order(5, "units"), mode=o.MODE_COPY_ONLY)[0] == 0
+    case.check_gathered_and_flags(5)
+    assert case.run(6, mode=o.MODE_GEMM_ONLY)[0] == 0
+    assert np.array_equal(host(case.c).view(np.uint32), bits)
+
+
+def test_producer_jitter_leaves_the_bits_alone():
+    """Producers that pause a hashed, uneven time before every unit (a test
+    aid of the call) deliver units in a shuffled order: the consumers must
+    still produce exactly the bits of an unjittered run."""
+    cfg = _small("jitter", 8, 256, 1024, 1024, 256, 128, seed=32)
+    case = AgCase(cfg, tiles_per_flag=2)
+    assert case.run(1, case.order(1))[0] == 0
+    bits = host(case.c).view(np.uint32).copy()
+    _full_check(case)
+    for epoch, jitter in ((2, 64), (3, 400), (4, 1000)):
+        case.c.zero_()
+        st, det = case.run(epoch, case.order(epoch, "units"), jitter=jitter)
+        assert st == 0, det
+        case.check_gathered_and_flags(epoch)
+        assert np.array_equal(host(case.c).view(np.uint32), bits)
+
+
+def test_more_panels_than_the_bootstrap_table():
+    """16 shards of 65 panels (1040 flag units, more than the bootstrap
+    table holds): the bootstrap is off and every unit is moved by the
+    producers; gathered, flags and C in full."""
+    cfg = _small("many_panels", 16, 1040, 128, 64, 16, 64, seed=33)
+    case = AgCase(cfg)
+    assert case.units == 16 * 65
+    for epoch in (1, 2):
+        st, det = case.run(epoch, case.order(epoch, "units"))
+        assert st == 0, det
+        case.check_gathered_and_flags(epoch)
+        _full_check(case)
+
+
+@pytest.mark.parametrize("mode", [0, 3])
+def test_flag_ahead_of_the_epoch_is_reported_and_parity_catches_the_early_read(mode):
+    """The checker bites on early consumption.  Every unit flag is preset to
+    epoch + 1 (as a signal of a later run would leave it) and the producer
+    order leaves out the units of one peer panel, so they are never copied.
+    The consumers then find their flags already set, do not wait, and read
+    that panel's rows of `gathered` while they still hold the NaN fill: the
+    run reports OVL_EEPOCH (a flag above the awaited epoch), the panel's
+    rows of C are NaN, and the comparison with the oracle fails.  The same
+    order with the flags reset and the units all moved passes."""
+    import torch
+    o = ovl()
+    cfg = _small("early", 4, 256, 512, 512, 64, 64, seed=34)
+    case = AgCase(cfg, tiles_per_flag=2)
+    shard, panel = 2, 1  # rows [576, 640): not the own rank's
+    order = case.order(1, "units")
+    dropped = np.isin(order // case.batches, [shard * case.panels + panel])
+    assert dropped.sum() == case.batches
+    order[dropped] = -1
+    case.flags.view(torch.int64).fill_(2)
+    st, det = case.run(1, order, mode=mode)
+    assert st == o.OVL_EEPOCH, (st, det)
+    assert det[0] == (1 if mode == 0 else 2) and det[2] == 2 and det[3] == 1, det
+    c = host(case.c)
+    r0 = shard * cfg.shard_m + panel * 64
+    assert np.isnan(c[r0:r0 + 64]).all(), "the panel that never moved was not read early"
+    with pytest.raises(AssertionError):
+        _full_check(case)
+    o.ovl_flags_reset(case.flags, case.plan.flags_bytes, case.ws, case.plan.workspace_bytes)
+    case.c.zero_()
+    st, det = case.run(1, case.order(1, "units"), mode=mode)
+    assert st == 0, det
+    _full_check(case)
+
+
 # ------------------------------------------------------------------ full sizes
-
-def _sampled_check(case, count=1500, seed=0, exact=False):
-    cfg = case.cfg
-    rng = np.random.default_rng(seed)
-    rows = rng.integers(0, cfg.m, count)
-    cols = rng.integers(0, cfg.n, count)
-    g = oracle.all_gather(case.shards)
-    ref = oracle.gemm_entries(g, case.b, rows, cols)
-    got = host(case.c)[rows, cols].astype(np.float64)
-    if exact:
-        assert np.array_equal(got, ref)
-    else:
-        # max|ref| over the sample stands in for the full max (never larger).
-        tol = gemm_tol(cfg.k, float(np.abs(ref).max()))
-        assert max_err(got, ref) <= tol
-
 
 @pytest.mark.parametrize("name,tpf", [("ag_r8_8192x3584x4096", 1), ("ag_r8_skinny_128x7168x8192", 4)])
 def test_full_size_random_orders_and_modes(name, tpf):
+    """The workloads at full size, in the bench's launch configuration:
+    gathered and flags bit-exact, every element of C within the bound, and
+    C bit-identical over three seeded producer orders, BARRIER and
+    GEMM_ONLY."""
     o = ovl()
     cfg = synth.CONFIGS[name]
     case = AgCase(cfg, tiles_per_flag=tpf)
+    _, c_ref = oracle.ag_gemm(case.shards, case.b)
     bits = None
     for epoch in range(1, 4):
         st, det = case.run(epoch, case.order(epoch))
@@ -240,7 +352,7 @@ def test_full_size_random_orders_and_modes(name, tpf):
         c = host(case.c)
         if bits is None:
             bits = c.view(np.uint32).copy()
-            _sampled_check(case)
+            _full_check(case, c_ref)
         else:
             assert np.array_equal(c.view(np.uint32), bits)
     case.c.zero_()
@@ -251,12 +363,17 @@ def test_full_size_random_orders_and_modes(name, tpf):
     assert np.array_equal(host(case.c).view(np.uint32), bits)
 
 
-def test_full_size_small_integers_exact():
-    cfg = synth.CONFIGS["ag_r8_8192x3584x4096"]
-    case = AgCase(cfg, "smallint", tiles_per_flag=1)
+@pytest.mark.parametrize("name,tpf", [("ag_r8_8192x3584x4096", 1), ("ag_r8_skinny_128x7168x8192", 4)])
+def test_full_size_small_integers_exact(name, tpf):
+    """Small integers: fp32 accumulation is exact, so every element of C
+    must equal the oracle's product bit for bit (every index, swizzle and
+    tile bug shows)."""
+    cfg = synth.CONFIGS[name]
+    case = AgCase(cfg, "smallint", tiles_per_flag=tpf)
     st, det = case.run(1, case.order(1))
     assert st == 0, det
-    _sampled_check(case, count=3000, exact=True)
+    case.check_gathered_and_flags(1)
+    _exact_check(case)
 
 
 # ------------------------------------------------------------------ device trace

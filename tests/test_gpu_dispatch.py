@@ -16,6 +16,13 @@ def ovl():
     return _o
 
 
+# A bf16 quiet NaN.  Before every run that copies, the receive rows are
+# filled with it, so that a grouped-GEMM tile that reads a row before its
+# slice has landed produces NaN, and rows the dispatch must not write (past a
+# slice's count) are seen to keep it.
+NAN_BF16 = 0x7FC0
+
+
 class A2aCase:
     def __init__(self, cfg, kind="normal", topk=None):
         import torch
@@ -38,13 +45,17 @@ class A2aCase:
         self.flags = zeros_bytes(self.fbytes)
         self.ws = zeros_bytes(o.a2a_workspace_bytes(self.desc))
         o.ovl_flags_reset(self.flags, self.fbytes, self.ws, self.ws.numel())
+        self.fill = 0  # what rows past a slice's count hold
 
-    def run(self, epoch, mode=0, producers=0):
+    def run(self, epoch, mode=0, producers=0, spin_limit=0, poison=True):
         o = ovl()
+        if poison and mode != o.MODE_GEMM_ONLY and self.recv_x.numel():
+            self.recv_x.fill_(NAN_BF16)
+            self.fill = NAN_BF16
         say(f"  a2a_run {self.cfg.name} epoch={epoch} mode={mode}")
         o.a2a_dispatch_grouped_gemm_run(self.desc, self.d_x, self.d_topk, self.d_w, self.recv_x, self.recv_src,
                                         self.recv_count, self.y, self.flags, self.ws, epoch, mode=mode,
-                                        producers=producers)
+                                        producers=producers, spin_limit=spin_limit)
         return o.ovl_check(self.ws, raise_on_error=False)
 
     def oracle_layout(self):
@@ -52,10 +63,16 @@ class A2aCase:
         return oracle.dispatch(self.x, self.topk, c.rank, c.experts_per_rank, c.cap)
 
     def check_layout(self, epoch):
+        """Counts, sources and flags bit-exact; every received row bit-exact,
+        and every row past a slice's count untouched."""
         rx, rs, rc = self.oracle_layout()
         assert np.array_equal(host(self.recv_count), rc), "recv_count differs"
         assert np.array_equal(host(self.recv_src), rs), "recv_src differs"
-        assert np.array_equal(host(self.recv_x, np.uint16), rx), "recv_x differs"
+        got = host(self.recv_x, np.uint16)
+        for s in range(self.cfg.ranks):
+            n = int(rc[s].sum())
+            assert np.array_equal(got[s, :n], rx[s, :n]), f"recv_x of slice {s} differs"
+            assert (got[s, n:] == self.fill).all(), f"rows past the count of slice {s} were written"
         fl = host(self.flags)[: self.fbytes]
         assert np.array_equal(fl, oracle.expected_flags(self.cfg.ranks, 8, epoch)), "flags differ"
         return rx, rs, rc
@@ -90,7 +107,6 @@ def test_small_integers_bit_exact_and_modes_agree():
     y_ref = oracle.grouped_gemm(rx, rc, case.w)
     first = host(case.y).copy()
     assert np.array_equal(first, y_ref.astype(np.float32))
-    case.recv_x.zero_()
     case.y.zero_()
     assert case.run(2, mode=o.MODE_COPY_ONLY)[0] == 0
     case.check_layout(2)
@@ -147,20 +163,80 @@ def test_zero_tokens():
     assert not host(case.recv_count).any()
 
 
-def test_full_size_layout_exact_and_rows_sampled():
+def test_full_size_layout_and_outputs_exact():
+    """The MoE workload at full size, in the bench's launch configuration:
+    layout bit-exact, every received row of y compared with the oracle's
+    grouped GEMM, rows past each slice's count never written, and a second
+    run gives the same bits."""
     cfg = synth.CONFIGS["a2a_r8_t4096_h4096_e64"]
     case = A2aCase(cfg)
+    case.y.fill_(float("nan"))
     st, det = case.run(1)
     assert st == 0, det
     rx, rs, rc = case.check_layout(1)
     y = host(case.y)
-    rng = np.random.default_rng(2)
-    for s in (0, 3, 7):
-        n_valid = int(rc[s].sum())
-        rows = rng.choice(n_valid, size=min(48, n_valid), replace=False)
-        ref = oracle.grouped_gemm_rows(rx, rc, case.w, s, rows)
-        assert max_err(y[s, rows], ref) <= gemm_tol(cfg.hidden, float(np.abs(ref).max()))
-        assert not y[s, n_valid:].any()
+    y_ref = oracle.grouped_gemm(rx, rc, case.w)
+    tol = gemm_tol(cfg.hidden, float(np.abs(y_ref).max()))
+    for s in range(cfg.ranks):
+        n = int(rc[s].sum())
+        assert np.isfinite(y[s, :n]).all(), f"slice {s}: a row read before it landed"
+        assert max_err(y[s, :n], y_ref[s, :n]) <= tol, f"slice {s}"
+        assert np.isnan(y[s, n:]).all(), f"slice {s}: rows past the count written"
     first = y.view(np.uint32).copy()
     assert case.run(2)[0] == 0
     assert np.array_equal(host(case.y).view(np.uint32), first)
+
+
+def test_full_size_small_integers_exact():
+    cfg = synth.CONFIGS["a2a_r8_t4096_h4096_e64"]
+    case = A2aCase(cfg, "smallint")
+    st, det = case.run(1)
+    assert st == 0, det
+    rx, rs, rc = case.check_layout(1)
+    y_ref = oracle.grouped_gemm(rx, rc, case.w)
+    assert np.array_equal(host(case.y), y_ref.astype(np.float32))
+
+
+def test_tiny_spin_limit_gives_up_and_every_kernel_exits():
+    """A spin limit of one poll: a consumer whose slice is not complete when
+    it runs out of chunks to copy gives up (OVL_ETIMEOUT at a slice flag) and
+    the launch still ends; the run's outputs are then not trusted.  A reset
+    and a normal run afterwards give the oracle's layout and rows."""
+    o = ovl()
+    cfg = _cfg("a2a_spin", R=8, T=1024, H=512, N=256, E=4, rank=0, seed=41)
+    case = A2aCase(cfg)
+    st, det = case.run(1, spin_limit=1)
+    say(f"  tiny spin limit: status {st} detail {det}")
+    assert st in (0, o.OVL_ETIMEOUT)
+    if st == o.OVL_ETIMEOUT:
+        assert det[0] == 4 and 0 <= det[1] < cfg.ranks and det[3] == 1, det
+    o.ovl_flags_reset(case.flags, case.fbytes, case.ws, case.ws.numel())
+    st, det = case.run(1)
+    assert st == 0, det
+    rx, rs, rc = case.check_layout(1)
+    y_ref = oracle.grouped_gemm(rx, rc, case.w)
+    assert max_err(host(case.y), y_ref) <= gemm_tol(cfg.hidden, float(np.abs(y_ref).max()))
+
+
+def test_repeated_local_expert_overflow_is_clipped_and_reported():
+    """Routing rows that repeat a local expert (outside the call's contract)
+    can ask for more rows than a slice holds when topk > experts per rank:
+    here every token of every source picks local expert 0 three times, 3T
+    rows for a capacity of 2T.  The layout clips the counts at the capacity,
+    nothing is written past a slice, and the run reports OVL_ESHAPE (site 9)
+    with the rows asked for and the capacity."""
+    o = ovl()
+    cfg = _cfg("a2a_overflow", R=2, T=40, H=64, N=128, topk=3, E=2, rank=1, seed=42)
+    assert cfg.cap == 2 * cfg.tokens
+    topk = [np.full((cfg.tokens, 3), 2, dtype=np.int32) for _ in range(2)]  # expert 2 = rank 1's expert 0
+    case = A2aCase(cfg, topk=topk)
+    case.y.fill_(float("nan"))
+    st, det = case.run(1)
+    assert st == o.OVL_ESHAPE, (st, det)
+    assert det[0] == 9 and det[2] == 3 * cfg.tokens and det[3] == cfg.cap, det
+    rc = host(case.recv_count)
+    assert rc[:, 0].tolist() == [cfg.cap, cfg.cap] and not rc[:, 1].any()
+    src = host(case.recv_src)
+    assert np.array_equal(src, np.repeat(np.arange(cfg.tokens, dtype=np.int32), 3)[None, :cfg.cap].repeat(2, 0))
+    with pytest.raises(ValueError):
+        oracle.dispatch(case.x, topk, cfg.rank, cfg.experts_per_rank, cfg.cap)

@@ -187,3 +187,18 @@ def test_grouped_gemm_small_integers_exact():
             r1 = r0 + int(rc[s, e])
             assert np.array_equal(y[s, r0:r1], (xi[s, r0:r1] @ wi[e]).astype(np.float64))
             r0 = r1
+
+
+def test_dispatch_refuses_rows_past_the_slice_capacity():
+    """A slice holds tokens * min(topk, experts_per_rank) rows, which is every
+    routed pair when a token's choices are distinct experts.  Routing that
+    repeats a local expert with topk > experts_per_rank asks for more: the
+    oracle refuses it (the library clips it and reports OVL_ESHAPE)."""
+    T = 6
+    x = [np.zeros((T, 8), np.uint16)] * 2
+    ok = [np.array([[2, 3, 0]] * T, np.int32)] * 2        # 2 local rows per token: 2T = cap
+    recv_x, src, cnt = oracle.dispatch(x, ok, 1, 2, 2 * T)
+    assert cnt.sum() == 2 * 2 * T
+    bad = [np.array([[2, 2, 2]] * T, np.int32)] * 2       # 3 rows per token for expert 2
+    with pytest.raises(ValueError):
+        oracle.dispatch(x, bad, 1, 2, 2 * T)
