@@ -13,6 +13,7 @@
 // gathered buffer.  Tiles whose rows are all the own rank's read the own
 // shard directly and never wait.
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -75,6 +76,17 @@ enum { kModeFused = 0, kModeBarrier = 1, kModeGemmOnly = 2 };
 // measured faster than 4), 128 x 128 tiles 4.
 constexpr int ag_waves(int bm) { return bm == 256 ? 8 : 4; }
 constexpr int kMaxWaves = 8;
+
+}  // namespace ovl
+
+// The allocation-free variant's workspace (ag_gemm_run_noalloc): a file-scope
+// device array, one copy per GPU, kept until the process ends.  Every plan
+// fits: a K split runs at most 224 tile ranges of 128 x 128 fp32 partials
+// (14 MiB), and an unsplit plan needs only the 256-byte error record.
+constexpr size_t kScratchBytes = 16u << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace ovl {
 
 // ---------------------------------------------------------------- producer
 
@@ -810,9 +822,19 @@ extern "C" size_t ag_gemm_trace_bytes(ag_gemm_plan_t p) {
   return 8 * ((size_t)p->num_units + kTraceItem * (size_t)p->tiles_m * (size_t)p->tiles_n * (size_t)p->splits);
 }
 
-extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, const void* b, void* gathered,
-                                  float* c, int64_t* flags, void* workspace, int64_t epoch,
-                                  const int32_t* producer_order, const ovl_opts* opts, hipStream_t stream) {
+namespace {
+
+// Bytes at the start of a plan's workspace that must be zero when a run
+// starts: the error record and, with a K split, the arrival counters (the
+// partial products need no clearing).
+size_t ag_state_bytes(const ag_gemm_plan_s* p) { return p->splits == 1 ? 256 : ag_partial_offset(p); }
+
+// ag_gemm_run, and its allocation-free variant: clear_state zeroes the
+// workspace's run state with a fill kernel on `stream` once every argument
+// has been accepted, right before the launch.
+ovl_status ag_gemm_launch(ag_gemm_plan_t p, const void* const* shards, const void* b, void* gathered, float* c,
+                          int64_t* flags, void* workspace, bool clear_state, int64_t epoch,
+                          const int32_t* producer_order, const ovl_opts* opts, hipStream_t stream) {
   if (!p || !shards || !workspace) return OVL_EINVAL;
   const uint32_t mode = opts ? opts->mode : OVL_MODE_FUSED;
   if (mode > OVL_MODE_BARRIER) return OVL_EINVAL;
@@ -883,6 +905,7 @@ extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, c
     P = (int)std::max<int64_t>(1, std::min<int64_t>(P, a.num_units));
     a.producers = P;
     a.consumers = 0;
+    if (clear_state && (st = zero_async(workspace, ag_state_bytes(p), stream))) return st;
     hipLaunchKernelGGL(ag_produce_kernel, dim3(P), dim3(kThreads), 0, stream, a);
     OVL_HIP_TRY(hipGetLastError());
     return OVL_OK;
@@ -909,7 +932,52 @@ extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, c
     st = epoch_accept(flags, epoch);
     if (st) return st;
   }
+  if (clear_state && (st = zero_async(workspace, ag_state_bytes(p), stream))) return st;
   return kind == kBig ? dispatch_mode<256, 256, 2>(a, mode, stream)
                       : (kind == kSmall ? dispatch_mode<128, 128, 2>(a, mode, stream)
                                         : dispatch_mode<128, 128, kSplitStages>(a, mode, stream));
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+}  // namespace
+
+namespace ovl {
+
+// The array's name is a host-side stand-in in host code; its device address
+// on the current device comes from the runtime, once per device, with that
+// device current.
+ovl_status noalloc_scratch(void** out) {
+  int dev = 0;
+  OVL_HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return OVL_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return OVL_EHIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return OVL_OK;
+}
+
+}  // namespace ovl
+
+extern "C" ovl_status ag_gemm_run(ag_gemm_plan_t p, const void* const* shards, const void* b, void* gathered,
+                                  float* c, int64_t* flags, void* workspace, int64_t epoch,
+                                  const int32_t* producer_order, const ovl_opts* opts, hipStream_t stream) {
+  return ag_gemm_launch(p, shards, b, gathered, c, flags, workspace, false, epoch, producer_order, opts, stream);
+}
+
+extern "C" ovl_status ag_gemm_run_noalloc(ag_gemm_plan_t p, const void* const* shards, const void* b,
+                                          void* gathered, float* c, int64_t* flags, int64_t epoch,
+                                          const int32_t* producer_order, const ovl_opts* opts, hipStream_t stream) {
+  if (!p) return OVL_EINVAL;
+  if (ag_gemm_workspace_bytes(p) > kScratchBytes) return OVL_EUNSUPPORTED;
+  void* ws = nullptr;
+  const ovl_status st = noalloc_scratch(&ws);
+  if (st) return st;
+  return ag_gemm_launch(p, shards, b, gathered, c, flags, ws, true, epoch, producer_order, opts, stream);
 }

@@ -39,6 +39,8 @@ __global__ __launch_bounds__(256) void copy_kernel(u32x4* __restrict__ dst, cons
   for (; i < vecs; i += stride) dst[i] = src[i];
 }
 
+}  // namespace
+
 ovl_status zero_async(void* p, size_t bytes, hipStream_t stream) {
   if (!bytes) return OVL_OK;
   if (!p) return OVL_EINVAL;
@@ -49,8 +51,6 @@ ovl_status zero_async(void* p, size_t bytes, hipStream_t stream) {
   OVL_HIP_TRY(hipGetLastError());
   return OVL_OK;
 }
-
-}  // namespace
 
 ovl_status current_device_info(DeviceInfo* out) {
   int dev = 0;
@@ -118,7 +118,13 @@ extern "C" ovl_status ovl_flags_reset(int64_t* flags, size_t flag_bytes, void* w
 }
 
 extern "C" ovl_status ovl_check(const void* workspace, int64_t* detail, hipStream_t stream) {
-  if (!workspace) return OVL_EINVAL;
+  if (!workspace) {
+    // The allocation-free calls keep their error record in the device's scratch.
+    void* p = nullptr;
+    const ovl_status st = noalloc_scratch(&p);
+    if (st) return st;
+    workspace = p;
+  }
   OVL_HIP_TRY(hipStreamSynchronize(stream));
   ErrRec rec;
   OVL_HIP_TRY(hipMemcpy(&rec, workspace, sizeof(rec), hipMemcpyDeviceToHost));

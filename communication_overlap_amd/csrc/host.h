@@ -35,6 +35,15 @@ ovl_status epoch_accept(const void* flags, int64_t epoch);
 ovl_status epoch_check(const void* flags, int64_t epoch);
 void epoch_forget(const void* flags);
 
+// Zeroes `bytes` bytes at p (16-byte aligned) on `stream` with a fill kernel
+// (not a memset node, so that the work may be captured in a graph).
+ovl_status zero_async(void* p, size_t bytes, hipStream_t stream);
+
+// Device address of the current device's scratch array, which the
+// allocation-free entry point uses as its workspace (looked up once per
+// device, with that device current).
+ovl_status noalloc_scratch(void** out);
+
 // Raises the dynamic-LDS limit of `kernel` to `bytes` once per process.
 ovl_status allow_lds(const void* kernel, int bytes);
 

@@ -40,7 +40,7 @@ EXPORTS = (
     "ovl_flags_reset", "ovl_check", "ovl_strerror", "ovl_copy",
     "ring_allreduce_flags_bytes", "ring_allreduce_workspace_bytes", "ring_allreduce_run",
     "fp8_quantize_rows", "a2a_dispatch_grouped_gemm_fp8_run", "ag_gemm_trace_bytes",
-    "ag_gemm_row_tiles", "ag_gemm_tile_rows", "ag_gemm_consumer_order",
+    "ag_gemm_row_tiles", "ag_gemm_tile_rows", "ag_gemm_consumer_order", "ag_gemm_run_noalloc",
 )
 
 
@@ -109,6 +109,9 @@ def lib() -> ctypes.CDLL:
     L.ag_gemm_run.argtypes = [c_void_p, POINTER(c_void_p), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                               c_int64, c_void_p, POINTER(Opts), c_void_p]
     L.ag_gemm_run.restype = st
+    L.ag_gemm_run_noalloc.argtypes = [c_void_p, POINTER(c_void_p), c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_int64, c_void_p, POINTER(Opts), c_void_p]
+    L.ag_gemm_run_noalloc.restype = st
     L.gemm_rs_flags_bytes.argtypes = [POINTER(GemmRsDesc)]
     L.gemm_rs_flags_bytes.restype = c_size_t
     L.gemm_rs_workspace_bytes.argtypes = [POINTER(GemmRsDesc)]
@@ -258,6 +261,16 @@ def ag_gemm_run(plan: AgGemmPlan, shards, b, gathered, c, flags, workspace, epoc
     st = lib().ag_gemm_run(plan.handle, arr, _ptr(b), _ptr(gathered), _ptr(c), _ptr(flags), _ptr(workspace),
                            epoch, _ptr(producer_order), byref(o), _stream(stream))
     return _check(st, "ag_gemm_run", raise_on_error)
+
+
+def ag_gemm_run_noalloc(plan: AgGemmPlan, shards, b, gathered, c, flags, epoch: int, producer_order=None,
+                        mode: int = MODE_FUSED, producers: int = 0, spin_limit: int = 0, stream=None,
+                        raise_on_error: bool = True, trace=None, jitter: int = 0) -> int:
+    arr = _ptr_array(shards)
+    o = _opts(mode, producers, spin_limit, trace, jitter)
+    st = lib().ag_gemm_run_noalloc(plan.handle, arr, _ptr(b), _ptr(gathered), _ptr(c), _ptr(flags), epoch,
+                                   _ptr(producer_order), byref(o), _stream(stream))
+    return _check(st, "ag_gemm_run_noalloc", raise_on_error)
 
 
 # ------------------------------------------------------------------ GEMM-RS

@@ -221,6 +221,24 @@ ovl_status ag_gemm_run(ag_gemm_plan_t plan, const void* const* shards, const voi
                        int64_t epoch, const int32_t* producer_order,
                        const ovl_opts* opts, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): ag_gemm_run
+ * without the workspace argument.  Its workspace is a 16 MiB array inside the
+ * library, one per GPU, held from the library's first use on that GPU until
+ * the process ends; every plan's workspace fits in it (ag_gemm_workspace_bytes
+ * is at most 14 MiB), and a plan that did not would be refused with
+ * OVL_EUNSUPPORTED.  Before the launch the call clears the array's run state
+ * (error record, split counters) with a fill kernel on `stream`; it calls no
+ * allocator.  Device errors are read with ovl_check(NULL, ...).  Every call on
+ * one GPU shares its array: calls that overlap in time on one GPU (on
+ * different streams, or from several threads) race and must not be issued.
+ * Arguments, modes, results and errors as ag_gemm_run; the same kernels run,
+ * so the outputs are bit-identical to ag_gemm_run's. */
+ovl_status ag_gemm_run_noalloc(ag_gemm_plan_t plan, const void* const* shards, const void* b,
+                               void* gathered, float* c, int64_t* flags, int64_t epoch,
+                               const int32_t* producer_order, const ovl_opts* opts,
+                               hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * GEMM -> ReduceScatter ("Triton-distributed Semantics", Kernel Design
  * Patterns, "GEMM and ReduceScatter Overlapping").
