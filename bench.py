@@ -104,7 +104,7 @@ def timed_reps(fn, reps, flush=None, warm=5):
 
 
 class AgBench:
-    def __init__(self, cfg, tiles_per_flag):
+    def __init__(self, cfg, tiles_per_flag, unit_producers=1):
         import torch
         import synth
         from communication_overlap_amd import ovl
@@ -112,7 +112,7 @@ class AgBench:
         self.cfg = cfg
         shards, b = synth.ag_inputs(cfg)
         self.plan = ovl.ag_gemm_plan(cfg.ranks, 0, cfg.shard_m, cfg.k, cfg.n, cfg.tile_m, cfg.tile_n,
-                                     tiles_per_flag, 8)
+                                     tiles_per_flag, 8, unit_producers)
         units = self.plan.num_units
         pps = -(-cfg.shard_m // min(cfg.tile_m, cfg.shard_m))  # panels per shard
         batches = units // (cfg.ranks * pps)
@@ -171,8 +171,32 @@ def trace_summary(ag, flush):
             "note": "times from the first item's start; waits = wave-0 flag polling inside the tiles"}
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _repeat(fn, seconds):
+    """Runs fn whole, repeatedly, until `seconds` of wall time; (runs, s per run)."""
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds or runs >= 200:
+            return runs, dt / runs
+
+
 def cpu_baseline(cfg):
-    """The oracle (gather + float64 GEMM) on the full workload, on host cores."""
+    """The oracle on the host cores: the headline workload (gather + float64
+    GEMM) repeated whole for about 10 s, and every other workload timed whole
+    for about 2 s each (the oracle as it is, untuned)."""
     import oracle
     import synth
     try:
@@ -181,17 +205,31 @@ def cpu_baseline(cfg):
     except Exception:
         cores = os.cpu_count() or 1
     shards, b = synth.ag_inputs(cfg)
-    # Whole runs of the workload, repeated until about 10 s of CPU work.
-    runs, t0 = 0, time.perf_counter()
-    while True:
-        g, c = oracle.ag_gemm(shards, b)
-        runs += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or runs >= 200:
-            break
-    return {"value": runs * cfg.flops() / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    runs, per = _repeat(lambda: oracle.ag_gemm(shards, b), 10.0)
+    per_config = {cfg.name: {"s_per_run": round(per, 4), "runs": runs,
+                             "TFLOPs": round(cfg.flops() / per / 1e12, 4)}}
+    for name in ("ag_r2_128x256x256", "ag_r8_skinny_128x7168x8192"):
+        c = synth.CONFIGS[name]
+        sh, bb = synth.ag_inputs(c)
+        n, t = _repeat(lambda: oracle.ag_gemm(sh, bb), 2.0)
+        per_config[name] = {"s_per_run": round(t, 5), "runs": n, "TFLOPs": round(c.flops() / t / 1e12, 4)}
+    c = synth.CONFIGS["rs_r8_8192x4096x1792"]
+    a, bb, parts = synth.rs_inputs(c)
+    n, t = _repeat(lambda: oracle.gemm_rs(a, bb, parts, c.rank, c.ranks), 2.0)
+    per_config[c.name] = {"s_per_run": round(t, 4), "runs": n, "TFLOPs": round(c.flops() / t / 1e12, 4)}
+    c = synth.CONFIGS["a2a_r8_t4096_h4096_e64"]
+    x, topk, w = synth.dispatch_inputs(c)
+
+    def moe():
+        rx, rs, rc = oracle.dispatch(x, topk, c.rank, c.experts_per_rank, c.cap)
+        oracle.grouped_gemm(rx, rc, w)
+
+    n, t = _repeat(moe, 2.0)
+    per_config[c.name] = {"s_per_run": round(t, 4), "runs": n, "what": "dispatch layout + copy + float64 grouped GEMM"}
+    return {"value": cfg.flops() / per / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{runs} runs of the whole {cfg.m}x{cfg.n}x{cfg.k} workload (gather + float64 GEMM), "
-                      f"{dt:.1f} s"}
+                      f"{runs * per:.1f} s",
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count(), "per_config": per_config}
 
 
 def main():
@@ -202,6 +240,9 @@ def main():
     ap.add_argument("--reps", type=int, default=20, help="repetitions of each side measurement")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the side workloads")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="skip the flushed overlap measurements (then every launch of the headline kernel runs "
+                         "back to back, as in the timed region: the run to profile for its average duration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the other ranks "
@@ -247,24 +288,26 @@ def main():
     b2b_trace = trace_summary(ag, lambda: None)
     ag.check()
 
-    log("[bench] overlap: fused / copy-only / gemm-only, cache flushed")
-    fused = timed_reps(lambda: ag.run(ovl.MODE_FUSED), args.reps, flush)
-    copy_only = timed_reps(lambda: ag.run(ovl.MODE_COPY_ONLY), args.reps, flush)
-    gemm_only = timed_reps(lambda: ag.run(ovl.MODE_GEMM_ONLY), args.reps, flush)
-    ag.check()
-    copy_bytes = 2 * cfg.m * cfg.k * 2
-    overlap = {
-        "fused_us": fused, "copy_only_us": copy_only, "gemm_only_us": gemm_only,
-        "fused_over_copy_plus_gemm": fused["median_us"] / (copy_only["median_us"] + gemm_only["median_us"]),
-        "fused_over_gemm_only": fused["median_us"] / gemm_only["median_us"],
-        "copy_only_GBps": copy_bytes / (copy_only["median_us"] * 1e-6) / 1e9,
-        "gemm_only_TFLOPs": cfg.flops() / (gemm_only["median_us"] * 1e-6) / 1e12,
-        "fused_flushed_TFLOPs": cfg.flops() / (fused["median_us"] * 1e-6) / 1e12,
-        "trace": trace_summary(ag, flush),
-    }
+    overlap = None
+    if not args.no_overlap:
+        log("[bench] overlap: fused / copy-only / gemm-only, cache flushed")
+        fused = timed_reps(lambda: ag.run(ovl.MODE_FUSED), args.reps, flush)
+        copy_only = timed_reps(lambda: ag.run(ovl.MODE_COPY_ONLY), args.reps, flush)
+        gemm_only = timed_reps(lambda: ag.run(ovl.MODE_GEMM_ONLY), args.reps, flush)
+        ag.check()
+        copy_bytes = 2 * cfg.m * cfg.k * 2
+        overlap = {
+            "fused_us": fused, "copy_only_us": copy_only, "gemm_only_us": gemm_only,
+            "fused_over_copy_plus_gemm": fused["median_us"] / (copy_only["median_us"] + gemm_only["median_us"]),
+            "fused_over_gemm_only": fused["median_us"] / gemm_only["median_us"],
+            "copy_only_GBps": copy_bytes / (copy_only["median_us"] * 1e-6) / 1e9,
+            "gemm_only_TFLOPs": cfg.flops() / (gemm_only["median_us"] * 1e-6) / 1e12,
+            "fused_flushed_TFLOPs": cfg.flops() / (fused["median_us"] * 1e-6) / 1e12,
+            "trace": trace_summary(ag, flush),
+        }
 
     extra = {}
-    if not args.no_extra:
+    if not args.no_extra and overlap is not None:
         # Flag batching on the same workload: one flag per 256-column K-batch
         # (the headline setting), per 4 or 16 K-tiles, or per whole panel.
         batching = {"1": round(fused["median_us"], 1)}
@@ -275,9 +318,23 @@ def main():
             batching[str(tpf)] = round(timed_reps(lambda: agb.run(ovl.MODE_FUSED), args.reps, flush)["median_us"], 1)
             agb.check()
             del agb
+        # Split-unit arrivals (signal ADD): each 256 x 256 flag unit moved by W
+        # producer workgroups that add to its counter; the last publishes.
+        split_units = {"1": round(fused["median_us"], 1)}
+        for W in (2, 4):
+            log(f"[bench] unit producers: {W}")
+            agw = AgBench(cfg, tiles_per_flag=1, unit_producers=W)
+            agw.run()
+            split_units[str(W)] = round(timed_reps(lambda: agw.run(ovl.MODE_FUSED), args.reps, flush)["median_us"], 1)
+            agw.check()
+            del agw
         extra = side_workloads(args.reps, flush)
         extra["ag_flag_batching_fused_us"] = {"by_tiles_per_flag": batching,
                                               "note": "0 = one flag per 256-row panel (all of K)"}
+        extra["ag_unit_producers_fused_us"] = {
+            "by_producers_per_unit": split_units,
+            "note": "one flag per 256x256 unit; W > 1: W workgroups copy a unit's rows, each adds an arrival, "
+                    "the arrival completing a multiple of W sets the flag"}
 
     out = {
         "metric": METRIC,
@@ -312,9 +369,10 @@ def main():
             "sclk_GHz": round(b2b_trace["sclk_GHz"], 3),
             "peak": round(PEAK_BF16_TFLOPS * b2b_trace["sclk_GHz"] / 2.4, 1),
             "frac": round(achieved / (PEAK_BF16_TFLOPS * b2b_trace["sclk_GHz"] / 2.4), 4),
-            "flushed_sclk_GHz": round(overlap["trace"]["sclk_GHz"], 3),
-            "flushed_frac": round(cfg.flops() / (fused["median_us"] * 1e-6) / 1e12
-                                  / (PEAK_BF16_TFLOPS * overlap["trace"]["sclk_GHz"] / 2.4), 4)},
+            "flushed_sclk_GHz": round(overlap["trace"]["sclk_GHz"], 3) if overlap else None,
+            "flushed_frac": (round(cfg.flops() / (overlap["fused_us"]["median_us"] * 1e-6) / 1e12
+                                   / (PEAK_BF16_TFLOPS * overlap["trace"]["sclk_GHz"] / 2.4), 4)
+                             if overlap else None)},
         "side": extra,
     }
     if not args.no_cpu:
@@ -371,18 +429,24 @@ def side_workloads(reps, flush):
     out = torch.zeros(bm, cfg.n, device="cuda")
     out_flags = torch.zeros(fb, dtype=torch.uint8, device="cuda")
     in_flags = torch.zeros(fb, dtype=torch.uint8, device="cuda")
-    in_flags.view(torch.int64).fill_(1 << 40)
     ws = torch.zeros(ovl.gemm_rs_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
     ovl.ovl_flags_reset(out_flags, fb, ws, ws.numel())
     ep = [0]
+
+    def rs_ready():
+        """The peers' partials are pre-resident: their flags are set to the
+        coming run's epoch (outside the timed region, after the flush)."""
+        flush()
+        in_flags.view(torch.int64).fill_(ep[0] + 1)
 
     def rs(mode=0):
         ep[0] += 1
         ovl.gemm_rs_run(desc, d_a, d_b, peer_out, peer_in, out, out_flags, in_flags, ws, ep[0], mode=mode)
 
+    rs_ready()
     rs()
-    t = timed_reps(rs, reps, flush)
-    g = timed_reps(lambda: rs(ovl.MODE_GEMM_ONLY), reps, flush)
+    t = timed_reps(rs, reps, rs_ready)
+    g = timed_reps(lambda: rs(ovl.MODE_GEMM_ONLY), reps, rs_ready)
     ovl.ovl_check(ws)
     res[cfg.name] = {"fused_us": t, "gemm_only_us": g,
                      "TFLOPs": cfg.flops() / (t["median_us"] * 1e-6) / 1e12,
@@ -486,20 +550,26 @@ def side_workloads(reps, flush):
     cfb = ovl.a2a_combine_flags_bytes(desc)
     c_out_flags = torch.zeros(cfb, dtype=torch.uint8, device="cuda")
     c_in_flags = torch.zeros(cfb, dtype=torch.uint8, device="cuda")
-    c_in_flags.view(torch.int64).fill_(1 << 40)
     c_ws = torch.zeros(ovl.a2a_combine_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
     ovl.ovl_flags_reset(c_out_flags, cfb, c_ws, c_ws.numel())
     cep = [0]
+
+    def comb_ready():
+        """The peers' returned rows are pre-resident: their flags hold the
+        coming run's epoch (outside the timed region, after the flush)."""
+        flush()
+        c_in_flags.view(torch.int64).fill_(cep[0] + 1)
 
     def comb(mode=0):
         cep[0] += 1
         ovl.a2a_combine_run(desc, y, recv_count, ret_out, d_ret_in, d_topk[cfg.rank], d_gates, out, c_out_flags,
                             c_in_flags, c_ws, cep[0], mode=mode)
 
+    comb_ready()
     comb()
-    t = timed_reps(comb, reps, flush)
-    put = timed_reps(lambda: comb(ovl.MODE_COPY_ONLY), reps, flush)
-    sm = timed_reps(lambda: comb(ovl.MODE_GEMM_ONLY), reps, flush)
+    t = timed_reps(comb, reps, comb_ready)
+    put = timed_reps(lambda: comb(ovl.MODE_COPY_ONLY), reps, comb_ready)
+    sm = timed_reps(lambda: comb(ovl.MODE_GEMM_ONLY), reps, comb_ready)
     ovl.ovl_check(c_ws)
     rc = recv_count.cpu().numpy()
     rows_back = int(sum(rc[s].sum() for s in range(R) if s != cfg.rank))

@@ -24,6 +24,7 @@
 namespace ovl {
 
 constexpr int kMaxRanks = 16;
+constexpr int kMaxUnitProducers = 16;
 constexpr int kMaxRowTiles = 1024;  // consumer-order table held in LDS
 constexpr int kXcds = 8;            // MI355X: 8 accelerator complex dies, each with its own L2
 
@@ -55,6 +56,8 @@ struct AgArgs {
   int64_t* counters;  // [tiles][2], zero between launches
   int64_t* trace;     // optional timestamps: [num_units] publishes, then [items][kTraceItem]
   uint32_t jitter;    // producers sleep up to this many intervals before each unit (test aid)
+  int32_t unit_producers;  // W: workgroups that move one unit together (1: one publisher)
+  int64_t* arrivals;       // [num_units] monotone arrival counters (W > 1)
 };
 
 // The constant-rate (100 MHz) real-time counter, common to all compute units.
@@ -80,9 +83,10 @@ constexpr int kMaxWaves = 8;
 }  // namespace ovl
 
 // The allocation-free variant's workspace (ag_gemm_run_noalloc): a file-scope
-// device array, one copy per GPU, kept until the process ends.  Every plan
-// fits: a K split runs at most 224 tile ranges of 128 x 128 fp32 partials
-// (14 MiB), and an unsplit plan needs only the 256-byte error record.
+// device array, one copy per GPU, kept until the process ends.  A plan with
+// one producer per unit always fits: a K split runs at most 224 tile ranges
+// of 128 x 128 fp32 partials (14 MiB), and an unsplit plan needs only the
+// 256-byte error record; several producers per unit add 8 bytes per unit.
 constexpr size_t kScratchBytes = 16u << 20;
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
@@ -163,6 +167,37 @@ struct Sched {
 
 constexpr int kBootBits = 2048 * 32;  // presence bitmap: n_boot * batches <= this
 
+// Geometry of flag unit u: rows [r0, r0 + rows) of shard s, columns
+// [c0, c0 + cols).
+struct UnitBox {
+  int s;
+  int64_t r0, rows, c0, cols;
+};
+
+__device__ inline UnitBox unit_box(const AgArgs& a, int u) {
+  const int bt = u % a.batches;
+  const int sp = u / a.batches;
+  const int p = sp % a.panels;
+  UnitBox x;
+  x.s = sp / a.panels;
+  x.r0 = (int64_t)p * a.unit_rows;
+  x.rows = min((int64_t)a.unit_rows, a.shard_m - x.r0);
+  x.c0 = (int64_t)bt * a.batch_cols;
+  x.cols = min((int64_t)a.batch_cols, a.k - x.c0);
+  return x;
+}
+
+// Copies rows [r0, r0 + rows) of unit box x (agent: with agent-scope stores).
+template <int NT>
+__device__ inline void copy_unit_rows(const AgArgs& a, const UnitBox& x, int64_t r0, int64_t rows, bool agent) {
+  const uint16_t* src = a.shards[x.s] + r0 * a.k + x.c0;
+  uint16_t* dst = a.g + ((int64_t)x.s * a.shard_m + r0) * a.k + x.c0;
+  if (agent)
+    copy_block<NT, true>(src, dst, rows, x.cols, a.k);
+  else
+    copy_block<NT>(src, dst, rows, x.cols, a.k);
+}
+
 // Copies one flag unit into the gathered buffer and publishes its flag (NT
 // threads per workgroup).
 // `agent`: the unit is written with agent-scope stores and published
@@ -174,34 +209,70 @@ constexpr int kBootBits = 2048 * 32;  // presence bitmap: n_boot * batches <= th
 // producers keep plain stores and the fence: with agent-scope stores there
 // the copy ran beside the GEMM's traffic slower (last unit published at
 // 146 against 127 us) and the fused launch took 250-253 against 240-242 us.
+// With several producers per unit (unit_producers = W > 1) a unit moved
+// whole by one workgroup also adds W to its arrival counter, which keeps the
+// counter at a multiple of W after every run.
 template <int NT>
 __device__ inline void move_unit(const AgArgs& a, int u, bool agent_hint = false) {
-  const int bt = u % a.batches;
-  const int sp = u / a.batches;
-  const int p = sp % a.panels;
-  const int s = sp / a.panels;
-  const int64_t r0 = (int64_t)p * a.unit_rows;
-  const int64_t rows = min((int64_t)a.unit_rows, a.shard_m - r0);
-  const int64_t c0 = (int64_t)bt * a.batch_cols;
-  const int64_t cols = min((int64_t)a.batch_cols, a.k - c0);
-  const bool agent = agent_hint || rows * cols * 2 <= 64 * 1024;
+  const UnitBox x = unit_box(a, u);
+  const bool agent = agent_hint || x.rows * x.cols * 2 <= 64 * 1024;
   int64_t* flag = a.flags + (int64_t)u * a.flag_stride;
+  copy_unit_rows<NT>(a, x, x.r0, x.rows, agent);
   if (agent) {
-    copy_block<NT, true>(a.shards[s] + r0 * a.k + c0, a.g + ((int64_t)s * a.shard_m + r0) * a.k + c0, rows, cols,
-                         a.k);
     wave_drain();
     __syncthreads();
     if (threadIdx.x == 0) __hip_atomic_store(flag, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
-    copy_block<NT>(a.shards[s] + r0 * a.k + c0, a.g + ((int64_t)s * a.shard_m + r0) * a.k + c0, rows, cols, a.k);
     wg_publish(flag, a.epoch);
   }
-  if (a.trace && threadIdx.x == 0) a.trace[u] = now_ticks();
+  if (threadIdx.x == 0) {
+    if (a.unit_producers > 1)
+      __hip_atomic_fetch_add(a.arrivals + u, (int64_t)a.unit_producers, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.trace) a.trace[u] = now_ticks();
+  }
+}
+
+// Piece `piece` of W of unit u (rows split evenly; a piece may be empty):
+// the split-unit signal ADD ("Triton-distributed Semantics", Runtime
+// Implementation of Communication Primitives: signal SET and ADD).  The
+// workgroup copies its rows, then arrives once on the unit's counter; the
+// counter is never reset (it only grows, by exactly W per run), so the
+// arrival that brings it to a multiple of W is the unit's last, whatever
+// the epoch, and that workgroup publishes the flag.  Ordering: plain stores
+// are released by an agent-scope fence before the add and the last
+// arriver acquires the others' releases before its release store of the
+// flag; agent-scope stores are complete once drained, so those pieces add
+// and publish without fences (as move_unit's agent path).
+template <int NT>
+__device__ inline void move_piece(const AgArgs& a, int u, int piece, bool agent_hint) {
+  const UnitBox x = unit_box(a, u);
+  const int W = a.unit_producers;
+  const int64_t lo = x.r0 + x.rows * piece / W, hi = x.r0 + x.rows * (piece + 1) / W;
+  const bool agent = agent_hint || (hi - lo) * x.cols * 2 <= 64 * 1024;
+  copy_unit_rows<NT>(a, x, lo, hi - lo, agent);
+  wave_drain();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t* flag = a.flags + (int64_t)u * a.flag_stride;
+    if (!agent) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int64_t old = __hip_atomic_fetch_add(a.arrivals + u, (int64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old % W == W - 1) {
+      if (agent) {
+        __hip_atomic_store(flag, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(flag, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (a.trace) a.trace[u] = now_ticks();
+    }
+  }
+  // Separates this thread-0 branch from the caller's next one.
+  __syncthreads();
 }
 
 // Test aid: a pause of h(u, epoch) mod (jitter + 1) sleeps of about 64
-// clocks before unit u is moved, h a fixed integer hash, so that units land
-// in an uneven, shuffled order.
+// clocks before unit u (or piece u of the split units' pieces) is moved, h
+// a fixed integer hash, so that units land in an uneven, shuffled order.
 __device__ inline void jitter_pause(const AgArgs& a, int u) {
   uint32_t h = (uint32_t)u * 0x9E3779B1u ^ (uint32_t)a.epoch * 0x85EBCA77u;
   h ^= h >> 15;
@@ -212,18 +283,26 @@ __device__ inline void jitter_pause(const AgArgs& a, int u) {
 }
 
 // Moves the units at producer-order positions w, w + P, ..., skipping the
-// bootstrap panels' units when sc is given (those were moved already).
+// bootstrap panels' units when sc is given (those were moved already).  With
+// W producers per unit the work items are (position, piece) pairs, the W
+// pieces of a unit consecutive, so that W producers move a unit at once.
 template <int NT>
 __device__ inline void produce(const AgArgs& a, int w, int P, const Sched* sc, bool agent = false) {
-  for (int i = w; i < a.num_units; i += P) {
-    const int u = uniform(a.order ? a.order[i] : i);
+  const int W = a.unit_producers;
+  const int items = a.num_units * W;
+  for (int i = w; i < items; i += P) {
+    const int pos = W == 1 ? i : i / W;
+    const int u = uniform(a.order ? a.order[pos] : pos);
     if (u < 0 || u >= a.num_units) continue;  // not a unit index: nothing to move
-    if (a.jitter) jitter_pause(a, u);
     // Bootstrap units were moved already.  The bootstrap is off (n_boot = 0)
     // when the panels outnumber the bidx table, which then holds no entry for
     // most panels.
     if (sc && sc->n_boot > 0 && uniform(sc->bidx[u / a.batches]) >= 0) continue;
-    move_unit<NT>(a, u, agent);
+    if (a.jitter) jitter_pause(a, W == 1 ? u : u * W + i % W);
+    if (W == 1)
+      move_unit<NT>(a, u, agent);
+    else
+      move_piece<NT>(a, u, i % W, agent);
   }
 }
 
@@ -645,6 +724,7 @@ struct ag_gemm_plan_s {
   int bm, bn;
   int tiles_m, tiles_n;
   int splits, split_cols;  // K split (1: none)
+  int unit_producers;      // W >= 1
 };
 
 namespace {
@@ -703,6 +783,7 @@ extern "C" ovl_status ag_gemm_plan(const ag_gemm_desc* d, ag_gemm_plan_t* out) {
   if (d->ranks > kMaxRanks) return OVL_EUNSUPPORTED;
   if (d->shard_m < 1 || d->k < 8 || d->n < 8 || d->tile_m < 1 || d->tile_n < 8 || d->tiles_per_flag < 0)
     return OVL_ESHAPE;
+  if (d->unit_producers < 0 || d->unit_producers > kMaxUnitProducers) return OVL_EINVAL;
   if (d->k % 8 || d->n % 8 || d->tile_n % 8) return OVL_EALIGN;
   if (d->flag_stride < 8 || d->flag_stride % 8) return OVL_EALIGN;
   const int64_t m = (int64_t)d->ranks * d->shard_m;
@@ -721,6 +802,7 @@ extern "C" ovl_status ag_gemm_plan(const ag_gemm_desc* d, ag_gemm_plan_t* out) {
   p->batch_cols = (int32_t)std::min<int64_t>(width, d->k);
   p->batches = (int32_t)ceil_div(d->k, p->batch_cols);
   p->num_units = (int64_t)d->ranks * p->panels * p->batches;
+  p->unit_producers = std::max(1, d->unit_producers);
   if (p->num_units > (1 << 24)) {
     delete p;
     return OVL_EUNSUPPORTED;
@@ -801,17 +883,21 @@ extern "C" size_t ag_gemm_flags_bytes(ag_gemm_plan_t p) {
 }
 
 // Error record (256 bytes reserved); with a K split, two arrival counters
-// per tile (padded to 256 bytes), then the fp32 partial products
-// [splits][m][n].
+// per tile (padded to 256 bytes); with several producers per unit, one
+// arrival counter per unit (padded to 256 bytes); then, with a K split, the
+// fp32 partial products [splits][m][n].
 static size_t ag_counters_offset() { return 256; }
+static size_t ag_arrivals_offset(const ag_gemm_plan_s* p) {
+  return ag_counters_offset() +
+         (p->splits > 1 ? (size_t)ceil_div((int64_t)p->tiles_m * p->tiles_n * 16, 256) * 256 : 0);
+}
 static size_t ag_partial_offset(const ag_gemm_plan_s* p) {
-  return ag_counters_offset() + (size_t)ceil_div((int64_t)p->tiles_m * p->tiles_n * 16, 256) * 256;
+  return ag_arrivals_offset(p) + (p->unit_producers > 1 ? (size_t)ceil_div(p->num_units * 8, 256) * 256 : 0);
 }
 
 extern "C" size_t ag_gemm_workspace_bytes(ag_gemm_plan_t p) {
   if (!p) return 0;
-  if (p->splits == 1) return 256;
-  return ag_partial_offset(p) + (size_t)p->splits * p->m * p->d.n * 4;
+  return ag_partial_offset(p) + (p->splits > 1 ? (size_t)p->splits * p->m * p->d.n * 4 : 0);
 }
 
 extern "C" int32_t ag_gemm_splits(ag_gemm_plan_t p) { return p ? p->splits : 0; }
@@ -824,10 +910,11 @@ extern "C" size_t ag_gemm_trace_bytes(ag_gemm_plan_t p) {
 
 namespace {
 
-// Bytes at the start of a plan's workspace that must be zero when a run
-// starts: the error record and, with a K split, the arrival counters (the
-// partial products need no clearing).
-size_t ag_state_bytes(const ag_gemm_plan_s* p) { return p->splits == 1 ? 256 : ag_partial_offset(p); }
+// Bytes at the start of a plan's workspace that the allocation-free call
+// clears before each run: the error record, the split counters and the unit
+// arrival counters (the partial products need no clearing).  Arrival
+// counters that start at zero count as if the workspace had just been reset.
+size_t ag_state_bytes(const ag_gemm_plan_s* p) { return ag_partial_offset(p); }
 
 // ag_gemm_run, and its allocation-free variant: clear_state zeroes the
 // workspace's run state with a fill kernel on `stream` once every argument
@@ -892,6 +979,8 @@ ovl_status ag_gemm_launch(ag_gemm_plan_t p, const void* const* shards, const voi
   a.splits = p->splits;
   a.split_cols = p->split_cols;
   a.counters = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(workspace) + ag_counters_offset());
+  a.unit_producers = p->unit_producers;
+  a.arrivals = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(workspace) + ag_arrivals_offset(p));
   a.partial = p->splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ag_partial_offset(p))
                             : nullptr;
 
@@ -902,7 +991,7 @@ ovl_status ag_gemm_launch(ag_gemm_plan_t p, const void* const* shards, const voi
     ovl_status st = epoch_accept(flags, epoch);
     if (st) return st;
     int P = req_prod ? (int)req_prod : di.cus * 4;
-    P = (int)std::max<int64_t>(1, std::min<int64_t>(P, a.num_units));
+    P = (int)std::max<int64_t>(1, std::min<int64_t>(P, (int64_t)a.num_units * a.unit_producers));
     a.producers = P;
     a.consumers = 0;
     if (clear_state && (st = zero_async(workspace, ag_state_bytes(p), stream))) return st;
@@ -920,7 +1009,7 @@ ovl_status ag_gemm_launch(ag_gemm_plan_t p, const void* const* shards, const voi
   int P = 0;
   if (needs_copy) {
     P = req_prod ? (int)req_prod : std::max(kXcds, di.cus / 8);
-    P = (int)std::min<int64_t>(P, a.num_units);
+    P = (int)std::min<int64_t>(P, (int64_t)a.num_units * a.unit_producers);
     if (P >= resident) return OVL_EINVAL;
   }
   int64_t Cn = std::min<int64_t>(tiles * p->splits, resident - P);

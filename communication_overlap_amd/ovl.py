@@ -57,7 +57,8 @@ class Opts(Structure):
 
 class AgGemmDesc(Structure):
     _fields_ = [("ranks", c_int32), ("rank", c_int32), ("shard_m", c_int64), ("k", c_int64), ("n", c_int64),
-                ("tile_m", c_int32), ("tile_n", c_int32), ("tiles_per_flag", c_int32), ("flag_stride", c_int32)]
+                ("tile_m", c_int32), ("tile_n", c_int32), ("tiles_per_flag", c_int32), ("flag_stride", c_int32),
+                ("unit_producers", c_int32)]
 
 
 class GemmRsDesc(Structure):
@@ -207,8 +208,10 @@ def _ptr_array(ts):
 class AgGemmPlan:
     """Owns an ag_gemm_plan_t."""
 
-    def __init__(self, ranks, rank, shard_m, k, n, tile_m, tile_n, tiles_per_flag=0, flag_stride=8):
-        self.desc = AgGemmDesc(ranks, rank, shard_m, k, n, tile_m, tile_n, tiles_per_flag, flag_stride)
+    def __init__(self, ranks, rank, shard_m, k, n, tile_m, tile_n, tiles_per_flag=0, flag_stride=8,
+                 unit_producers=1):
+        self.desc = AgGemmDesc(ranks, rank, shard_m, k, n, tile_m, tile_n, tiles_per_flag, flag_stride,
+                               unit_producers)
         h = c_void_p()
         _check(lib().ag_gemm_plan(byref(self.desc), byref(h)), "ag_gemm_plan", True)
         self.handle = h

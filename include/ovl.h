@@ -140,6 +140,14 @@ typedef struct ag_gemm_desc {
   int32_t tile_n;          /* K-tile width for tiles_per_flag, multiple of 8; any such value */
   int32_t tiles_per_flag;  /* K-tiles per flag unit, >= 0 (0 = all of k) */
   int32_t flag_stride;     /* bytes between flag slots, multiple of 8, >= 8 */
+  int32_t unit_producers;  /* W, 0..16 (0 and 1: one producer workgroup moves and publishes
+                              each unit).  W > 1: the unit's rows are split evenly over W
+                              producer workgroups, each of which adds one arrival to the unit's
+                              counter in the workspace after its rows (signal ADD); the arrival
+                              that brings the counter to a multiple of W publishes the flag
+                              (signal SET).  The counter only grows (by W per run), so it needs
+                              no reset between runs; after a run that ended in an error, or a
+                              change of plan on the same workspace, reset the workspace. */
 } ag_gemm_desc;
 
 typedef struct ag_gemm_plan_s* ag_gemm_plan_t;
@@ -225,11 +233,12 @@ ovl_status ag_gemm_run(ag_gemm_plan_t plan, const void* const* shards, const voi
  * capture, tight serving loops, harnesses that forbid allocation): ag_gemm_run
  * without the workspace argument.  Its workspace is a 16 MiB array inside the
  * library, one per GPU, held from the library's first use on that GPU until
- * the process ends; every plan's workspace fits in it (ag_gemm_workspace_bytes
- * is at most 14 MiB), and a plan that did not would be refused with
- * OVL_EUNSUPPORTED.  Before the launch the call clears the array's run state
- * (error record, split counters) with a fill kernel on `stream`; it calls no
- * allocator.  Device errors are read with ovl_check(NULL, ...).  Every call on
+ * the process ends.  A plan whose ag_gemm_workspace_bytes exceeds it is
+ * refused with OVL_EUNSUPPORTED; every plan with one producer per unit fits
+ * (at most 14 MiB), and unit_producers > 1 adds 8 bytes per flag unit.
+ * Before the launch the call clears the array's run state (error record,
+ * split counters, unit arrival counters) with a fill kernel on `stream`; it
+ * calls no allocator.  Device errors are read with ovl_check(NULL, ...).  Every call on
  * one GPU shares its array: calls that overlap in time on one GPU (on
  * different streams, or from several threads) race and must not be issued.
  * Arguments, modes, results and errors as ag_gemm_run; the same kernels run,

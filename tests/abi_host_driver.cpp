@@ -44,6 +44,7 @@ void plans(std::mt19937_64& rng) {
     d.tile_n = 8 * (int)(rng() % 40);
     d.tiles_per_flag = (int)(rng() % 6) - 1;
     d.flag_stride = 8 * (int)(rng() % 20);
+    d.unit_producers = (int)(rng() % 19) - 1;
     ag_gemm_plan_t p = nullptr;
     const ovl_status st = ag_gemm_plan(&d, &p);
     if (st != OVL_OK) {
@@ -54,7 +55,7 @@ void plans(std::mt19937_64& rng) {
     const int64_t units = ag_gemm_num_units(p);
     EXPECT(units >= d.ranks);
     EXPECT(ag_gemm_flags_bytes(p) == (size_t)units * (size_t)d.flag_stride);
-    EXPECT(ag_gemm_workspace_bytes(p) >= OVL_ERROR_RECORD_BYTES);
+    EXPECT(ag_gemm_workspace_bytes(p) >= OVL_ERROR_RECORD_BYTES + (d.unit_producers > 1 ? 8 * (size_t)units : 0));
     EXPECT(ag_gemm_splits(p) >= 1);
     EXPECT(ag_gemm_trace_bytes(p) >= 8 * (size_t)units);
     const int T = ag_gemm_row_tiles(p), bm = ag_gemm_tile_rows(p);

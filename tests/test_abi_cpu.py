@@ -61,6 +61,8 @@ def test_strerror():
     ((2, 0, 64, 256, 256, 32, 32, 0, 12), "OVL_EALIGN"),       # flag stride
     ((2, 0, 64, 256, 256, 32, 32, -1, 8), "OVL_ESHAPE"),       # negative tiles per flag
     ((8, 0, 1 << 18, 4096, 256, 256, 256, 0, 8), "OVL_EUNSUPPORTED"),  # gathered operand > 1 GiB
+    ((2, 0, 64, 256, 256, 32, 32, 0, 8, 17), "OVL_EINVAL"),     # more than 16 producers per unit
+    ((2, 0, 64, 256, 256, 32, 32, 0, 8, -1), "OVL_EINVAL"),     # negative producers per unit
 ])
 def test_plan_rejects(args, status):
     o = ovl()
@@ -80,6 +82,17 @@ def test_plan_sizes_match_the_flag_unit_definition(name, tpf, stride):
     assert p.num_units == units
     assert p.flags_bytes == units * stride
     assert p.workspace_bytes >= ovl().ERROR_RECORD_BYTES
+
+
+@pytest.mark.parametrize("name,tpf,W", [("ag_r8_8192x3584x4096", 1, 4), ("ag_r8_skinny_128x7168x8192", 4, 2),
+                                        ("ag_r2_128x256x256", 1, 16)])
+def test_split_unit_plans_add_one_counter_per_unit(name, tpf, W):
+    cfg = synth.CONFIGS[name]
+    o = ovl()
+    one = o.ag_gemm_plan(cfg.ranks, 0, cfg.shard_m, cfg.k, cfg.n, cfg.tile_m, cfg.tile_n, tpf, 8)
+    many = o.ag_gemm_plan(cfg.ranks, 0, cfg.shard_m, cfg.k, cfg.n, cfg.tile_m, cfg.tile_n, tpf, 8, W)
+    assert many.num_units == one.num_units and many.flags_bytes == one.flags_bytes
+    assert many.workspace_bytes == one.workspace_bytes + -(-one.num_units * 8 // 256) * 256
 
 
 def test_ragged_plan_sizes():

@@ -25,12 +25,12 @@ NAN_BF16 = 0x7FC0
 
 
 class AgCase:
-    def __init__(self, cfg, kind="normal", tiles_per_flag=0, flag_stride=8, rank=0):
+    def __init__(self, cfg, kind="normal", tiles_per_flag=0, flag_stride=8, rank=0, unit_producers=1):
         o = ovl()
         self.cfg = cfg
         self.shards, self.b = synth.ag_inputs(cfg, kind)
         self.plan = o.ag_gemm_plan(cfg.ranks, rank, cfg.shard_m, cfg.k, cfg.n, cfg.tile_m, cfg.tile_n,
-                                   tiles_per_flag, flag_stride)
+                                   tiles_per_flag, flag_stride, unit_producers)
         self.units, self.panels, self.batches = oracle.ag_flag_units(cfg.ranks, cfg.shard_m, cfg.k, cfg.tile_m,
                                                                      cfg.tile_n, tiles_per_flag)
         assert self.plan.num_units == self.units
@@ -330,6 +330,60 @@ def test_flag_ahead_of_the_epoch_is_reported_and_parity_catches_the_early_read(m
     st, det = case.run(1, case.order(1, "units"), mode=mode)
     assert st == 0, det
     _full_check(case)
+
+
+# ------------------------------------------------------------------ split units (signal ADD)
+
+@pytest.mark.parametrize("W", [2, 4, 7])
+def test_split_unit_arrivals_match_one_publisher(W):
+    """Each flag unit moved by W producer workgroups that each add an arrival
+    to the unit's counter, the arrival completing a multiple of W setting the
+    flag: gathered and flags bit-exact and C bit-identical to the
+    one-publisher plan, over epochs that skip values (the counter is never
+    reset), random orders, jitter, BARRIER and COPY_ONLY + GEMM_ONLY."""
+    o = ovl()
+    cfg = _small("split_units", 4, 1000, 520, 2056, 256, 64, seed=35)
+    one = AgCase(cfg, tiles_per_flag=2)
+    assert one.run(1, one.order(1, "units"))[0] == 0
+    bits = host(one.c).view(np.uint32).copy()
+    _full_check(one)
+    case = AgCase(cfg, tiles_per_flag=2, unit_producers=W)
+    assert case.plan.workspace_bytes > one.plan.workspace_bytes
+    for epoch, jitter in ((1, 0), (2, 0), (5, 200), (9, 0)):
+        case.c.zero_()
+        st, det = case.run(epoch, case.order(epoch, "units"), jitter=jitter)
+        assert st == 0, det
+        case.check_gathered_and_flags(epoch)
+        assert np.array_equal(host(case.c).view(np.uint32), bits), f"epoch {epoch}"
+    case.c.zero_()
+    assert case.run(10, mode=o.MODE_BARRIER)[0] == 0
+    case.check_gathered_and_flags(10)
+    assert np.array_equal(host(case.c).view(np.uint32), bits)
+    assert case.run(11, case.order(11, "units"), mode=o.MODE_COPY_ONLY)[0] == 0
+    case.check_gathered_and_flags(11)
+    case.c.zero_()
+    assert case.run(12, mode=o.MODE_GEMM_ONLY)[0] == 0
+    assert np.array_equal(host(case.c).view(np.uint32), bits)
+    # every counter holds W arrivals per run that moved units (6 runs); the
+    # plan has no K split, so the counters follow the 256-byte error record
+    assert case.plan.splits == 1
+    cnt = host(case.ws)[256: 256 + case.units * 8].view(np.int64)
+    assert (cnt == 6 * W).all(), np.unique(cnt)
+
+
+def test_full_size_split_units_match_one_publisher():
+    """The headline workload with 4 producers per 256 x 256 flag unit: the
+    same gathered, flags and C bits as one publisher per unit."""
+    cfg = synth.CONFIGS["ag_r8_8192x3584x4096"]
+    one = AgCase(cfg, tiles_per_flag=1)
+    assert one.run(1, one.order(1))[0] == 0
+    bits = host(one.c).view(np.uint32).copy()
+    case = AgCase(cfg, tiles_per_flag=1, unit_producers=4)
+    for epoch in (1, 2):
+        st, det = case.run(epoch, case.order(epoch))
+        assert st == 0, det
+        case.check_gathered_and_flags(epoch)
+        assert np.array_equal(host(case.c).view(np.uint32), bits)
 
 
 # ------------------------------------------------------------------ full sizes

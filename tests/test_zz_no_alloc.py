@@ -24,12 +24,12 @@ def _cfg(name, R, Ms, K, N, tm, tn, seed):
     return synth.AgGemmCfg(name, R, Ms, K, N, tm, tn, 1.0, 1.0 / 16, seed, True)
 
 
-def _run_both(cfg, tpf, epoch=1):
+def _run_both(cfg, tpf, epoch=1, unit_producers=1):
     """Runs the workspace call and the allocation-free call on the same
     inputs and order; returns both results and the oracle's C."""
     o = ovl()
     shards, b = synth.ag_inputs(cfg)
-    plan = o.ag_gemm_plan(cfg.ranks, 0, cfg.shard_m, cfg.k, cfg.n, cfg.tile_m, cfg.tile_n, tpf, 8)
+    plan = o.ag_gemm_plan(cfg.ranks, 0, cfg.shard_m, cfg.k, cfg.n, cfg.tile_m, cfg.tile_n, tpf, 8, unit_producers)
     units, panels, batches = oracle.ag_flag_units(cfg.ranks, cfg.shard_m, cfg.k, cfg.tile_m, cfg.tile_n, tpf)
     order = dev(synth.producer_order(cfg.seed, epoch, cfg.ranks * panels, batches, True, "units"))
     d_shards, d_b = [dev(s) for s in shards], dev(b)
@@ -39,6 +39,7 @@ def _run_both(cfg, tpf, epoch=1):
         g.fill_(0x7FC0)  # NaN: an early read shows
         c = zeros_f32(cfg.m, cfg.n)
         flags = zeros_bytes(plan.flags_bytes)
+        o.ovl_flags_reset(flags, plan.flags_bytes, None, 0)  # a new flag buffer: epochs start at 1
         say(f"  {cfg.name} splits={plan.splits} noalloc={noalloc}")
         if noalloc:
             o.ag_gemm_run_noalloc(plan, d_shards, d_b, g, c, flags, epoch, order)
@@ -94,6 +95,7 @@ def test_noalloc_reports_a_timeout_in_its_own_record_and_recovers():
     order[-1] = -1
     g, c = zeros_u16(cfg.m, cfg.k), zeros_f32(cfg.m, cfg.n)
     flags = zeros_bytes(plan.flags_bytes)
+    o.ovl_flags_reset(flags, plan.flags_bytes, None, 0)
     d_shards, d_b = [dev(s) for s in shards], dev(b)
     say("  noalloc with a missing unit")
     o.ag_gemm_run_noalloc(plan, d_shards, d_b, g, c, flags, 1, dev(order), spin_limit=2000)
@@ -105,3 +107,14 @@ def test_noalloc_reports_a_timeout_in_its_own_record_and_recovers():
     assert st == 0, det
     _, c_ref = oracle.ag_gemm(shards, b)
     assert max_err(host(c), c_ref) <= gemm_tol(cfg.k, float(np.abs(c_ref).max()))
+
+
+def test_noalloc_split_units_start_their_counters_at_zero():
+    """Several producers per unit: the arrival counters live in the scratch,
+    which the previous call (with another producer count) left behind; each
+    call clears them, so calls with 4, then 3 producers per unit both match
+    the workspace call."""
+    cfg = _cfg("noalloc_units", 4, 300, 512, 768, 64, 128, seed=53)
+    for W in (4, 3):
+        plan, out, c_ref, g_ref, f_ref = _run_both(cfg, tpf=1, unit_producers=W)
+        _check(cfg, plan, out, c_ref, g_ref, f_ref)
