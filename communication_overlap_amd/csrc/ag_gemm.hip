@@ -67,17 +67,27 @@ __device__ inline int64_t now_cycles() { return (int64_t)__builtin_amdgcn_s_memt
 constexpr int kTraceItem = 6;  // int64 per traced work item
 
 constexpr int kMaxSplits = 8;
-// Split-K plans run the 128x128 tile with this many LDS stages, and only
-// that configuration carries the split epilogue (the others keep their
-// registers for the main loop).
-constexpr int kSplitStages = 4;
 
 enum { kModeFused = 0, kModeBarrier = 1, kModeGemmOnly = 2 };
 
-// Wavefronts per workgroup of the fused kernel: 256 x 256 tiles run 8 (a
-// 2 x 4 grid, two waves per SIMD: one's MFMAs cover the other's LDS reads;
-// measured faster than 4), 128 x 128 tiles 4.
-constexpr int ag_waves(int bm) { return bm == 256 ? 8 : 4; }
+// The consumer tile configurations: BM x BN output tile, K step BK, NS LDS
+// stages, NW wavefronts; SPLIT marks the one that carries the split-K
+// epilogue (the others keep their registers for the main loop).
+//  - big: 256 x 256, 8 waves in a 2 x 4 grid, two per SIMD (one's MFMAs
+//    cover the other's LDS reads; measured faster than 4);
+//  - small: 128 x 128, 4 waves;
+//  - split (skinny, bandwidth-bound shapes, K split over workgroups): short
+//    K steps through a deep ring, so that more of B is in flight when a
+//    step waits for its stage.
+template <int BM_, int BN_, int BK_, int NS_, int NW_, bool SPLIT_>
+struct AgTile {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_, NW = NW_;
+  static constexpr bool SPLIT = SPLIT_;
+};
+using TileBig = AgTile<256, 256, 64, 2, 8, false>;
+using TileSmall = AgTile<128, 128, 64, 2, 4, false>;
+constexpr int kSplitBN = 128, kSplitBK = 64, kSplitStages = 4, kSplitWaves = 4;
+using TileSplit = AgTile<128, kSplitBN, kSplitBK, kSplitStages, kSplitWaves, true>;
 constexpr int kMaxWaves = 8;
 
 }  // namespace ovl
@@ -483,8 +493,9 @@ __device__ void reduce_splits(const AgArgs& a, int64_t m0, int64_t n0, int64_t l
   }
 }
 
-template <int BM, int BN, int NS, int NW, int MODE>
+template <class T, int MODE>
 __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* lds) {
+  constexpr int BM = T::BM, BN = T::BN, NW = T::NW;
 
   bool timed_out = false;
   if (MODE == kModeBarrier) {
@@ -643,15 +654,21 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
     };
 
     Acc<BM, BN, NW> acc;
-    gemm_tile<BM, BN, 64, NS, false, NW>(acc, op, m0_op, lds, before_step);
-    if (BM != 128 || NS != kSplitStages || a.splits == 1) {
+    gemm_tile<BM, BN, T::BK, T::NS, false, NW>(acc, op, m0_op, lds, before_step);
+    if (!T::SPLIT || a.splits == 1) {
       acc_store<BM, BN, 0, NW>(acc, a.c, a.n, m0, n0, a.m, a.n);
       trace_item();
       continue;
     }
-    acc_store<BM, BN, 0, NW>(acc, a.partial + (int64_t)sp * a.m * a.n, a.n, m0, n0, a.m, a.n);
+    // The range's partial goes out with agent-scope stores (complete at the
+    // device's point of coherence once drained), so its arrival is a drain,
+    // a barrier and a relaxed add: no release fence, whose L2 writeback of
+    // the die (about 0.5 us, serialised per die) cost two per item here
+    // (skinny 128x7168x8192 GEMM only: 50 us with the fences, 30 us with no
+    // epilogue at all).
+    acc_store<BM, BN, kAuxAgent, NW>(acc, a.partial + (int64_t)sp * a.m * a.n, a.n, m0, n0, a.m, a.n);
     int64_t* cnt = a.counters + 2 * tl;
-    const int64_t before = wg_arrive(cnt);  // releases this range's partial
+    const int64_t before = wg_arrive_agent(cnt);
     if (a.split_sync) {
       // Wait for the tile's other ranges, then sum stripe sp of its rows.
       if (threadIdx.x < 64 && !timed_out) {
@@ -661,8 +678,13 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
       __syncthreads();
       const int64_t rs = (BM + a.splits - 1) / a.splits;
       reduce_splits<BM, BN, 64 * NW>(a, m0, n0, sp * rs, min((int64_t)BM, (sp + 1) * rs));
-      // The last range out returns both counters to zero for the next launch.
-      const int64_t out = wg_arrive(cnt + 1);
+      // The last range out returns both counters to zero for the next launch
+      // (bookkeeping only: this arrival publishes no data, so it needs no
+      // release; every range has passed its wait on cnt before it arrives).
+      __syncthreads();
+      int64_t out = 0;
+      if (threadIdx.x == 0)
+        out = __hip_atomic_fetch_add(cnt + 1, (int64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (threadIdx.x == 0 && out == a.splits - 1) {
         __hip_atomic_store(cnt, (int64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(cnt + 1, (int64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -690,26 +712,26 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
 // units the first round of consumer tiles reads (the bootstrap: the whole
 // chip copies what is needed first); then producers move the remaining units
 // in the caller's order while consumers compute.
-template <int BM, int BN, int NS, int MODE>
-__global__ __launch_bounds__(64 * ag_waves(BM), 1) void ag_gemm_kernel(AgArgs a) {
+template <class T, int MODE>
+__global__ __launch_bounds__(64 * T::NW, 1) void ag_gemm_kernel(AgArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
-  constexpr int NW = ag_waves(BM);
-  using C = TileCfg<BM, BN, 64, NS, NW>;
+  constexpr int NW = T::NW;
+  using C = TileCfg<T::BM, T::BN, T::BK, T::NS, NW>;
   static_assert(kBootTabBytes <= C::LDS_BYTES, "bootstrap tables alias the stage area");
   int* sorted = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(lds) + C::LDS_BYTES);
-  const Sched sc = build_schedule(a, BM, sorted, reinterpret_cast<int*>(lds), MODE != kModeGemmOnly);
+  const Sched sc = build_schedule(a, T::BM, sorted, reinterpret_cast<int*>(lds), MODE != kModeGemmOnly);
   if (MODE != kModeGemmOnly) produce_boot<64 * NW>(a, blockIdx.x, gridDim.x, sc);
   if ((int)blockIdx.x < a.producers) {
     produce<64 * NW>(a, blockIdx.x, a.producers, &sc);
     return;
   }
   __syncthreads();  // every read of the bootstrap tables is done: the stages may be written
-  consume<BM, BN, NS, NW, MODE>(a, (int)blockIdx.x - a.producers, sc.sorted, lds);
+  consume<T, MODE>(a, (int)blockIdx.x - a.producers, sc.sorted, lds);
 }
 
-template <int BM, int BN, int NS>
+template <class T>
 constexpr int ag_lds_bytes() {
-  return TileCfg<BM, BN, 64, NS>::LDS_BYTES + kOrderBytes;
+  return TileCfg<T::BM, T::BN, T::BK, T::NS, T::NW>::LDS_BYTES + kOrderBytes;
 }
 
 }  // namespace ovl
@@ -729,41 +751,37 @@ struct ag_gemm_plan_s {
 
 namespace {
 
-template <int BM, int BN, int NS, int MODE>
+template <class T, int MODE>
 ovl_status launch_fused(const AgArgs& a, hipStream_t stream) {
-  const void* fn = reinterpret_cast<const void*>(&ag_gemm_kernel<BM, BN, NS, MODE>);
-  const int lds = ag_lds_bytes<BM, BN, NS>();
+  const void* fn = reinterpret_cast<const void*>(&ag_gemm_kernel<T, MODE>);
+  const int lds = ag_lds_bytes<T>();
   ovl_status st = allow_lds(fn, lds);
   if (st) return st;
-  hipLaunchKernelGGL((ag_gemm_kernel<BM, BN, NS, MODE>), dim3(a.producers + a.consumers), dim3(64 * ag_waves(BM)),
-                     lds, stream, a);
+  hipLaunchKernelGGL((ag_gemm_kernel<T, MODE>), dim3(a.producers + a.consumers), dim3(64 * T::NW), lds, stream, a);
   OVL_HIP_TRY(hipGetLastError());
   return OVL_OK;
 }
 
-template <int BM, int BN, int NS>
+template <class T>
 ovl_status occupancy(int* out) {
-  const int lds = ag_lds_bytes<BM, BN, NS>();
-  ovl_status st = allow_lds(reinterpret_cast<const void*>(&ag_gemm_kernel<BM, BN, NS, kModeFused>), lds);
+  const int lds = ag_lds_bytes<T>();
+  ovl_status st = allow_lds(reinterpret_cast<const void*>(&ag_gemm_kernel<T, kModeFused>), lds);
   if (st) return st;
-  OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(out, ag_gemm_kernel<BM, BN, NS, kModeFused>,
-                                                           64 * ag_waves(BM), lds));
+  OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(out, ag_gemm_kernel<T, kModeFused>, 64 * T::NW, lds));
   return OVL_OK;
 }
 
-template <int BM, int BN, int NS>
+template <class T>
 ovl_status dispatch_mode(const AgArgs& a, uint32_t mode, hipStream_t stream) {
   switch (mode) {
-    case OVL_MODE_FUSED: return launch_fused<BM, BN, NS, kModeFused>(a, stream);
-    case OVL_MODE_BARRIER: return launch_fused<BM, BN, NS, kModeBarrier>(a, stream);
-    case OVL_MODE_GEMM_ONLY: return launch_fused<BM, BN, NS, kModeGemmOnly>(a, stream);
+    case OVL_MODE_FUSED: return launch_fused<T, kModeFused>(a, stream);
+    case OVL_MODE_BARRIER: return launch_fused<T, kModeBarrier>(a, stream);
+    case OVL_MODE_GEMM_ONLY: return launch_fused<T, kModeGemmOnly>(a, stream);
     default: return OVL_EINVAL;
   }
 }
 
-// The three tile configurations: 256x256 with a 2-stage ring; 128x128 with
-// a 2-stage ring; 128x128 with a 4-stage ring for split-K plans (skinny,
-// bandwidth-bound: more of B in flight per workgroup).
+// The three tile configurations (TileBig, TileSmall, TileSplit above).
 enum TileKind { kBig = 0, kSmall = 1, kSplit = 2 };
 
 inline TileKind tile_kind(const ag_gemm_plan_s* p) {
@@ -830,8 +848,14 @@ extern "C" ovl_status ag_gemm_plan(const ag_gemm_desc* d, ag_gemm_plan_t* out) {
   const int64_t tiles = (int64_t)p->tiles_m * p->tiles_n;
   const int64_t consumers = kPlanCus - std::max(kXcds, kPlanCus / 8);
   if (p->bm == 128) {
-    const int64_t s = std::min<int64_t>({consumers / tiles, ceil_div(d->k, 256), kMaxSplits});
+    int64_t s = std::min<int64_t>({consumers / tiles, ceil_div(d->k, 256), kMaxSplits});
     if (s >= 2) {
+      // The split tile may be wider: recount its tiles and ranges.
+      p->bn = kSplitBN;
+      p->tiles_n = (int)ceil_div(d->n, p->bn);
+      const int64_t split_tiles = (int64_t)p->tiles_m * p->tiles_n;
+      s = std::min<int64_t>({consumers / split_tiles, ceil_div(d->k, 256), kMaxSplits});
+      if (s < 2) s = 2;
       p->split_cols = (int32_t)(ceil_div(ceil_div(d->k, s), 64) * 64);
       p->splits = (int)ceil_div(d->k, p->split_cols);
     }
@@ -1002,8 +1026,8 @@ ovl_status ag_gemm_launch(ag_gemm_plan_t p, const void* const* shards, const voi
 
   int occ = 0;
   const TileKind kind = tile_kind(p);
-  st = kind == kBig ? occupancy<256, 256, 2>(&occ)
-                    : (kind == kSmall ? occupancy<128, 128, 2>(&occ) : occupancy<128, 128, kSplitStages>(&occ));
+  st = kind == kBig ? occupancy<TileBig>(&occ)
+                    : (kind == kSmall ? occupancy<TileSmall>(&occ) : occupancy<TileSplit>(&occ));
   if (st) return st;
   const int64_t resident = (int64_t)std::max(occ, 1) * di.cus;
   int P = 0;
@@ -1022,9 +1046,9 @@ ovl_status ag_gemm_launch(ag_gemm_plan_t p, const void* const* shards, const voi
     if (st) return st;
   }
   if (clear_state && (st = zero_async(workspace, ag_state_bytes(p), stream))) return st;
-  return kind == kBig ? dispatch_mode<256, 256, 2>(a, mode, stream)
-                      : (kind == kSmall ? dispatch_mode<128, 128, 2>(a, mode, stream)
-                                        : dispatch_mode<128, 128, kSplitStages>(a, mode, stream));
+  return kind == kBig ? dispatch_mode<TileBig>(a, mode, stream)
+                      : (kind == kSmall ? dispatch_mode<TileSmall>(a, mode, stream)
+                                        : dispatch_mode<TileSplit>(a, mode, stream));
 }
 
 constexpr int kMaxDevices = 64;

@@ -460,17 +460,25 @@ __device__ inline void stage_compute(Acc<BM, BN, NW>& acc, const uint8_t* stage,
   }
 }
 
-// Waits until at most n of this wave's asm-issued stage loads are in flight
-// (n a multiple of the loads per stage, at most 2 stages' worth).
-template <int LPS>
-__device__ inline void wait_stage_loads(int pending_stages) {
-  if (pending_stages >= 2) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPS) : "memory");
-  } else if (pending_stages == 1) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS) : "memory");
-  } else {
+// Waits until at most `pending_stages` stages' worth of this wave's
+// asm-issued stage loads are in flight (LPS loads per stage; at most
+// MAXP stages, and MAXP * LPS fits the 6-bit load counter).
+template <int LPS, int P>
+__device__ inline void wait_pending(int pending_stages) {
+  if constexpr (P == 0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (pending_stages >= P)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(P * LPS) : "memory");
+    else
+      wait_pending<LPS, P - 1>(pending_stages);
   }
+}
+
+template <int LPS, int MAXP = 2>
+__device__ inline void wait_stage_loads(int pending_stages) {
+  static_assert(MAXP * LPS <= 63, "the load counter holds 63 loads");
+  wait_pending<LPS, MAXP>(pending_stages);
 }
 
 template <int BM, int BN, int NW>
@@ -494,7 +502,7 @@ __device__ inline void gemm_tile(Acc<BM, BN, NW>& acc, const Operands& op, int64
                                  BeforeStep before_step) {
   using C = TileCfg<BM, BN, BK, NSTAGES, NW>;
   constexpr int NS = C::NS;
-  static_assert(NS - 2 <= 2, "wait_stage_loads covers up to two pending stages");
+  constexpr int MAXP = NS - 2 > 0 ? NS - 2 : 0;  // stages that may stay in flight at a step's end
   uint8_t* l8 = reinterpret_cast<uint8_t*>(lds);
   acc_zero(acc);
   const TileAddr<BM, BN, BK, IND, NW> ta = tile_addr<BM, BN, BK, IND, NW>(op, m0);
@@ -510,7 +518,7 @@ __device__ inline void gemm_tile(Acc<BM, BN, NW>& acc, const Operands& op, int64
     stage_issue_b(ta, lbase + i * C::STAGE_BYTES, i * BK);
   }
   if (NS - 1 < steps) step_cols(NS - 1);
-  wait_stage_loads<C::LPS>(min(NS - 2, steps - 1));  // stage 0 has landed
+  wait_stage_loads<C::LPS, MAXP>(min(NS - 2, steps - 1));  // stage 0 has landed
   __syncthreads();
   for (int32_t s = 0; s < steps; ++s) {
     const int32_t nxt = s + NS - 1;  // stage issued during this step
@@ -518,7 +526,7 @@ __device__ inline void gemm_tile(Acc<BM, BN, NW>& acc, const Operands& op, int64
     stage_compute<BM, BN, BK, NW>(acc, l8 + (s % NS) * C::STAGE_BYTES, fa, pf);
     if (s + NS < steps) step_cols(s + NS);
     // Stage s+1 must have landed; the stages issued after it may stay in flight.
-    wait_stage_loads<C::LPS>(max(0, min(s + NS - 1, steps - 1) - (s + 1)));
+    wait_stage_loads<C::LPS, MAXP>(max(0, min(s + NS - 1, steps - 1) - (s + 1)));
     __syncthreads();
   }
 }
