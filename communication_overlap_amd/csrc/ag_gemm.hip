@@ -79,10 +79,11 @@ enum { kModeFused = 0, kModeBarrier = 1, kModeGemmOnly = 2 };
 //  - split (skinny, bandwidth-bound shapes, K split over workgroups): short
 //    K steps through a deep ring, so that more of B is in flight when a
 //    step waits for its stage.
-template <int BM_, int BN_, int BK_, int NS_, int NW_, bool SPLIT_>
+template <int BM_, int BN_, int BK_, int NS_, int NW_, bool SPLIT_, int NL_ = NW_>
 struct AgTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_, NW = NW_;
   static constexpr bool SPLIT = SPLIT_;
+  static constexpr int NL = NL_;  // waves that issue the stage loads (gemm_tile)
 };
 using TileBig = AgTile<256, 256, 64, 2, 8, false>;
 using TileSmall = AgTile<128, 128, 64, 2, 4, false>;
@@ -654,7 +655,7 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
     };
 
     Acc<BM, BN, NW> acc;
-    gemm_tile<BM, BN, T::BK, T::NS, false, NW>(acc, op, m0_op, lds, before_step);
+    gemm_tile<BM, BN, T::BK, T::NS, false, NW, T::NL>(acc, op, m0_op, lds, before_step);
     if (!T::SPLIT || a.splits == 1) {
       acc_store<BM, BN, 0, NW>(acc, a.c, a.n, m0, n0, a.m, a.n);
       trace_item();

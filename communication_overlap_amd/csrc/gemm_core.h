@@ -163,14 +163,19 @@ struct TileAddr {
   uint32_t b_qstep;    // bytes between consecutive B instructions
   uint32_t ldb_b;
   int32_t k;
+  uint32_t wl;         // this wave's index among the NW waves that issue the loads
 };
 
+// NW here counts the waves that issue the stage loads, and wl is this
+// wave's index among them.
 template <int BM, int BN, int BK, bool IND = false, int NW = 4>
-__device__ inline TileAddr<BM, BN, BK, IND, NW> tile_addr(const Operands& op, int64_t m0) {
+__device__ inline TileAddr<BM, BN, BK, IND, NW> tile_addr(const Operands& op, int64_t m0,
+                                                          uint32_t wl = threadIdx.x >> 6) {
   using C = TileCfg<BM, BN, BK, 0, NW>;
   TileAddr<BM, BN, BK, IND, NW> t;
   const uint32_t l = lane_id();
-  const uint32_t w = threadIdx.x >> 6;
+  const uint32_t w = wl;
+  t.wl = wl;
   t.ra = make_srd(op.a + m0 * op.lda, (op.m_valid - m0) * op.lda * 2);
   t.rb = make_srd(op.b + op.n0, op.k * op.ldb * 2 - op.n0 * 2);
   t.k = (int32_t)op.k;
@@ -225,7 +230,7 @@ __device__ inline uint32_t a_offset(const TileAddr<BM, BN, BK, IND, NW>& t, int 
 template <int BM, int BN, int BK, bool IND, int NW>
 __device__ inline void stage_issue_a(const TileAddr<BM, BN, BK, IND, NW>& t, uint32_t stage, int32_t k0) {
   using C = TileCfg<BM, BN, BK, 0, NW>;
-  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t w = __builtin_amdgcn_readfirstlane(t.wl);
 #pragma unroll
   for (int q = 0; q < C::QA; ++q) load_to_lds(t.ra, stage + (w * C::QA + q) * 1024, a_offset(t, q, k0));
 }
@@ -233,7 +238,7 @@ __device__ inline void stage_issue_a(const TileAddr<BM, BN, BK, IND, NW>& t, uin
 template <int BM, int BN, int BK, bool IND, int NW>
 __device__ inline void stage_issue_b(const TileAddr<BM, BN, BK, IND, NW>& t, uint32_t stage, int32_t k0) {
   using C = TileCfg<BM, BN, BK, 0, NW>;
-  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t w = __builtin_amdgcn_readfirstlane(t.wl);
   const uint32_t sb = stage + C::A_BYTES;
   const uint32_t kb = (uint32_t)k0 * t.ldb_b;
 #pragma unroll
@@ -248,7 +253,7 @@ __device__ inline void stage_issue_b(const TileAddr<BM, BN, BK, IND, NW>& t, uin
 template <int BM, int BN, int BK, bool IND, int NW, int Q>
 __device__ inline void stage_issue_one(const TileAddr<BM, BN, BK, IND, NW>& t, uint32_t stage, int32_t k0) {
   using C = TileCfg<BM, BN, BK, 0, NW>;
-  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t w = __builtin_amdgcn_readfirstlane(t.wl);
   if constexpr (Q < C::QA) {
     load_to_lds(t.ra, stage + (w * C::QA + Q) * 1024, a_offset(t, Q, k0));
   } else {
@@ -262,6 +267,8 @@ __device__ inline void stage_issue_one(const TileAddr<BM, BN, BK, IND, NW>& t, u
 // before (on == false: nothing to load).
 template <int BM, int BN, int BK, bool IND, int NW>
 struct Prefetch {
+  static constexpr int QA = TileCfg<BM, BN, BK, 0, NW>::QA;    // A loads per loading wave
+  static constexpr int LPS = TileCfg<BM, BN, BK, 0, NW>::LPS;  // loads per loading wave
   const TileAddr<BM, BN, BK, IND, NW>* t;
   uint32_t slot;
   int32_t k0;
@@ -425,8 +432,8 @@ __device__ inline void mfma_group(Acc<BM, BN, NW>& acc, const Frags<BM, BN, NW>&
   // on the 8-wave 256 x 256 tile: 4% faster than bursts in mid-step, which
   // left the B loads half a step to land; a 4-stage ring of 32-wide K steps,
   // with three steps of lookahead, was no faster.)
-  if constexpr (G == 0) issue_range<C::QA, C::LPS>(pf);
-  if constexpr (G == C::FM) issue_range<0, C::QA>(pf);
+  if constexpr (G == 0) issue_range<P::QA, P::LPS>(pf);
+  if constexpr (G == C::FM) issue_range<0, P::QA>(pf);
   OVL_SCHED_FENCE();
 }
 
@@ -497,15 +504,23 @@ __device__ inline void acc_zero(Acc<BM, BN, NW>& acc) {
 // calls it, before a workgroup barrier that precedes the first load of that
 // step (so a wave that acquires there orders the whole workgroup's loads).
 // Ends with a workgroup barrier, so LDS may be reused at once.
-template <int BM, int BN, int BK = 64, int NSTAGES = 0, bool IND = false, int NW = 4, class BeforeStep>
+// NL: how many of the NW waves issue the stage loads (the last NL).  With
+// NL = NW / 2 every SIMD holds one loading and one computing wave: when the
+// memory pipeline backs up, a loading wave stalls at its load instructions
+// while the other wave still has MFMAs to issue.
+template <int BM, int BN, int BK = 64, int NSTAGES = 0, bool IND = false, int NW = 4, int NL = NW,
+          class BeforeStep>
 __device__ inline void gemm_tile(Acc<BM, BN, NW>& acc, const Operands& op, int64_t m0, uint16_t* lds,
                                  BeforeStep before_step) {
-  using C = TileCfg<BM, BN, BK, NSTAGES, NW>;
+  static_assert(NL == NW || 2 * NL == NW, "all waves load, or the second half");
+  using C = TileCfg<BM, BN, BK, NSTAGES, NL>;  // stage geometry and the loads of one loading wave
   constexpr int NS = C::NS;
   constexpr int MAXP = NS - 2 > 0 ? NS - 2 : 0;  // stages that may stay in flight at a step's end
   uint8_t* l8 = reinterpret_cast<uint8_t*>(lds);
   acc_zero(acc);
-  const TileAddr<BM, BN, BK, IND, NW> ta = tile_addr<BM, BN, BK, IND, NW>(op, m0);
+  const int wl_raw = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) - (NW - NL);
+  const bool loader = wl_raw >= 0;
+  const TileAddr<BM, BN, BK, IND, NL> ta = tile_addr<BM, BN, BK, IND, NL>(op, m0, (uint32_t)(loader ? wl_raw : 0));
   const FragAddr<BM, BN, BK, NW> fa = frag_addr<BM, BN, BK, NW>();
   const int32_t steps = (int32_t)((op.k + BK - 1) / BK);
   const uint32_t lbase = lds_addr(l8);
@@ -513,16 +528,18 @@ __device__ inline void gemm_tile(Acc<BM, BN, NW>& acc, const Operands& op, int64
   auto step_cols = [&](int32_t i) { before_step((int64_t)i * BK, min((int64_t)(i + 1) * BK, op.k)); };
   for (int32_t i = 0; i < NS - 1 && i < steps; ++i) step_cols(i);
   __syncthreads();
-  for (int32_t i = 0; i < NS - 1 && i < steps; ++i) {
-    stage_issue_a(ta, lbase + i * C::STAGE_BYTES, i * BK);
-    stage_issue_b(ta, lbase + i * C::STAGE_BYTES, i * BK);
-  }
+  if (loader)
+    for (int32_t i = 0; i < NS - 1 && i < steps; ++i) {
+      stage_issue_a(ta, lbase + i * C::STAGE_BYTES, i * BK);
+      stage_issue_b(ta, lbase + i * C::STAGE_BYTES, i * BK);
+    }
   if (NS - 1 < steps) step_cols(NS - 1);
   wait_stage_loads<C::LPS, MAXP>(min(NS - 2, steps - 1));  // stage 0 has landed
   __syncthreads();
   for (int32_t s = 0; s < steps; ++s) {
     const int32_t nxt = s + NS - 1;  // stage issued during this step
-    const Prefetch<BM, BN, BK, IND, NW> pf{&ta, lbase + (uint32_t)(nxt % NS) * C::STAGE_BYTES, nxt * BK, nxt < steps};
+    const Prefetch<BM, BN, BK, IND, NL> pf{&ta, lbase + (uint32_t)(nxt % NS) * C::STAGE_BYTES, nxt * BK,
+                                           loader && nxt < steps};
     stage_compute<BM, BN, BK, NW>(acc, l8 + (s % NS) * C::STAGE_BYTES, fa, pf);
     if (s + NS < steps) step_cols(s + NS);
     // Stage s+1 must have landed; the stages issued after it may stay in flight.
