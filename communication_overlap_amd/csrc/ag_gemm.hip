@@ -548,12 +548,12 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
     }
   }
   for (int64_t w = 0;; ++w) {
-    int64_t j = w * Cn + (int64_t)x * per + q;
+    int64_t j = deal_item(w, x, q, groups, per, items);
+    if (j < 0) break;
     if (gr && (w + 1) * Cn <= items) {
       const int rr = Cn / a.tiles_n, rpd = rr / gr, cpd = a.tiles_n / gc;
       j = (w * rr + (x / gc) * rpd + q / cpd) * a.tiles_n + (x % gc) * cpd + q % cpd;
     }
-    if (j >= items) break;
     const int64_t tl = j / a.splits;
     const int sp = (int)(j % a.splits);
     const int rt = uniform(sorted[tl / a.tiles_n]);
@@ -1037,8 +1037,15 @@ ovl_status ag_gemm_launch(ag_gemm_plan_t p, const void* const* shards, const voi
     P = (int)std::min<int64_t>(P, (int64_t)a.num_units * a.unit_producers);
     if (P >= resident) return OVL_EINVAL;
   }
-  int64_t Cn = std::min<int64_t>(tiles * p->splits, resident - P);
-  if (Cn > kXcds) Cn -= Cn % kXcds;  // keep whole die groups
+  // Consumers: the fewest that finish the items in as few rounds as the
+  // resident ones allow, in whole die groups (448 tiles of 256 x 256 on 256
+  // resident workgroups: 224 consumers in two whole rounds ran the GEMM alone
+  // in 204 us, 256 consumers with a partial second round in 208-223 us).
+  const int64_t items = tiles * p->splits, room = resident - P;
+  int64_t Cn = std::min<int64_t>(items, room);
+  Cn = (items + (items + Cn - 1) / Cn - 1) / ((items + Cn - 1) / Cn);
+  const int64_t whole = (Cn + kXcds - 1) / kXcds * kXcds;
+  if (Cn > kXcds && whole <= room) Cn = whole;
   a.producers = P;
   a.consumers = (int32_t)Cn;
   a.split_sync = p->splits > 1 && tiles * p->splits <= Cn;  // every range in the first round

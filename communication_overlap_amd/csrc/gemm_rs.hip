@@ -188,8 +188,8 @@ __global__ __launch_bounds__(kRsThreads, 1) void gemm_rs_kernel(RsArgs a) {
   bool timed_out = false;
 
   for (int64_t w = 0;; ++w) {
-    const int64_t j = w * Cn + (int64_t)x * per + q;
-    if (j >= total) break;
+    const int64_t j = deal_item(w, x, q, groups, per, total);
+    if (j < 0) break;
     // Own tiles first, then peer tile pj of block rank+1+pj/tpb.
     const int64_t pj = j - tpb;
     const int blk = pj < 0 ? a.rank : (int)((a.rank + 1 + pj / tpb) % a.ranks);
