@@ -45,6 +45,10 @@ constexpr int kGbm = 256, kGbn = 256;  // grouped GEMM tile
 constexpr int kGbn8 = 128;
 constexpr int kA2aMaxMTiles = 1024;    // m-tiles whose consumer order is sorted in LDS
 constexpr int kA2aXcds = 8;
+// Trace layout (int64): [R] slice publish times, [kA2aTraceProducers]
+// producer finish times, then kA2aTraceItem values per work item.
+constexpr int kA2aTraceProducers = 64;
+constexpr int kA2aTraceItem = 8;
 // Wavefronts per workgroup of the fused launch: the bf16 tile runs as a
 // 2 x 4 grid of waves, two per SIMD (one's MFMAs cover the other's LDS
 // reads; measured faster than 4); the FP8 tile as a 2 x 2 grid.
@@ -69,6 +73,7 @@ struct A2aArgs {
   float* y;
   int64_t* flags;
   int64_t* counters;  // [R] slice arrival counters (workspace)
+  int64_t* trace;     // optional timestamps (a2a_trace_bytes), or null
   int64_t* ticket;    // next chunk to copy in the fused launch (workspace)
   ErrRec* err;
   int64_t tokens, hidden, n, cap;
@@ -380,6 +385,7 @@ __device__ inline void a2a_arrive(const A2aArgs& a, const Geometry* g, int pos, 
     // Acquire the other arrivals, then release them on with the flag.
     wave_acquire();
     __hip_atomic_store(a.flags + (int64_t)s * a.flag_stride, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.trace) a.trace[s] = now_ticks();
   }
   // A barrier after the thread-0 branch: callers loop over chunks and take
   // the next ticket in another thread-0 branch; with nothing between the two
@@ -457,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void a2a_produce_kernel(A2aArgs a) {
 // barrier.  Returns false on timeout.
 // The result is the same in every wave: wave 0's poll result goes through
 // LDS, because callers loop over this call and every barrier in it.
-__device__ bool wait_slice_helping(const A2aArgs& a, const Geometry* g, int s, int* sh) {
+__device__ bool wait_slice_helping(const A2aArgs& a, const Geometry* g, int s, int* sh, int* helped) {
   const int total = uniform(g->chunk_base[a.ranks]);
   const int64_t* flag = a.flags + (int64_t)s * a.flag_stride;
   int st;
@@ -478,7 +484,10 @@ __device__ bool wait_slice_helping(const A2aArgs& a, const Geometry* g, int s, i
     __syncthreads();
     if (st != 1) break;
     const int ch = take_chunk(a, total, sh);
-    if (ch < total) a2a_copy_chunk(a, g, ch);
+    if (ch < total) {
+      a2a_copy_chunk(a, g, ch);
+      ++*helped;
+    }
   }
   if (threadIdx.x < 64) {
     const bool ok = st != 2 || wave_poll(flag, a.epoch, a.spin_limit, a.err, kSiteA2aSlice, s);
@@ -527,12 +536,15 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
     // (>= tokens) and is never read past x[rank]'s rows; a bound selected
     // per tile made the compiler reserve scratch.
     const bool local = WAIT && pos_hi == 0;
+    const int64_t t_item = a.trace ? now_ticks() : 0;
+    int helped = 0;
     if (WAIT && !local) {
       while (waited_hi < pos_hi && !timed_out) {
         ++waited_hi;
-        if (!wait_slice_helping(a, g, slice_at(a, waited_hi), sh)) timed_out = true;
+        if (!wait_slice_helping(a, g, slice_at(a, waited_hi), sh, &helped)) timed_out = true;
       }
     }
+    const int64_t t_ready = a.trace ? now_ticks() : 0;
     // Row table of the tile: expert row r0 + i lies in the slice at the
     // first position whose expert prefix exceeds it.
     int32_t* tab = rowtab[wv & 1][0];
@@ -594,6 +606,17 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
         acc_store_rows<kGbm, TBN, NW>(acc, a.y, a.n, (int64_t)a.ranks * a.cap, tab, op.n0, a.n);
       }
     }
+    if (a.trace && threadIdx.x == 0) {
+      int64_t* rec = a.trace + a.ranks + kA2aTraceProducers + kA2aTraceItem * j;
+      rec[0] = t_item;
+      rec[1] = now_ticks();
+      rec[2] = t_ready - t_item;  // waiting for slices, copying chunks meanwhile
+      rec[3] = helped;
+      rec[4] = cidx;
+      rec[5] = e;
+      rec[6] = mt;
+      rec[7] = nt;
+    }
   }
 }
 
@@ -617,6 +640,7 @@ __global__ __launch_bounds__(64 * a2a_waves(F8), 1) void a2a_fused_kernel(A2aArg
       int pend_pos = 0, pend_n = 0;
       for (int ch; (ch = take_chunk(a, total, &sh)) < total;) a2a_copy_chunk_deferred(a, g, ch, &pend_pos, &pend_n);
       if (pend_n) a2a_arrive(a, g, pend_pos, pend_n);
+      if (a.trace && threadIdx.x == 0 && blockIdx.x < kA2aTraceProducers) a.trace[a.ranks + blockIdx.x] = now_ticks();
       return;
     }
   }
@@ -634,6 +658,17 @@ using namespace ovl;
 extern "C" size_t a2a_flags_bytes(const a2a_desc* d) {
   if (!d || d->ranks < 1 || d->flag_stride < 8) return 0;
   return (size_t)d->ranks * (size_t)d->flag_stride;
+}
+
+// Slice publish times, producer finish times, then a record per work item:
+// at most (R * cap / 256 + experts) m-tiles times the n-tiles of the
+// narrower (FP8) tile.
+extern "C" size_t a2a_trace_bytes(const a2a_desc* d) {
+  if (!d || d->ranks < 1 || d->experts_per_rank < 1 || d->n < 1 || d->tokens < 0) return 0;
+  const int64_t cap = d->tokens * std::min<int64_t>(d->topk, d->experts_per_rank);
+  const int64_t mts = ((int64_t)d->ranks * cap + kGbm - 1) / kGbm + d->experts_per_rank;
+  const int64_t nts = (d->n + kGbn8 - 1) / kGbn8;
+  return 8 * ((size_t)d->ranks + kA2aTraceProducers + (size_t)kA2aTraceItem * (size_t)(mts * nts));
 }
 
 // Error record, slice arrival counters, chunk ticket.
@@ -715,6 +750,7 @@ ovl_status a2a_run(const a2a_desc* d, bool f8, const void* const* x, const float
   a.err = static_cast<ErrRec*>(workspace);
   a.counters = reinterpret_cast<int64_t*>(static_cast<uint8_t*>(workspace) + OVL_ERROR_RECORD_BYTES);
   a.ticket = a.counters + kA2aMaxRanks;
+  a.trace = opts ? opts->trace : nullptr;
   a.tokens = d->tokens;
   a.hidden = d->hidden;
   a.n = d->n;

@@ -60,10 +60,6 @@ struct AgArgs {
   int64_t* arrivals;       // [num_units] monotone arrival counters (W > 1)
 };
 
-// The constant-rate (100 MHz) real-time counter, common to all compute units.
-__device__ inline int64_t now_ticks() { return (int64_t)__builtin_amdgcn_s_memrealtime(); }
-// The shader-clock cycle counter (its rate is the actual clock).
-__device__ inline int64_t now_cycles() { return (int64_t)__builtin_amdgcn_s_memtime(); }
 constexpr int kTraceItem = 6;  // int64 per traced work item
 
 constexpr int kMaxSplits = 8;

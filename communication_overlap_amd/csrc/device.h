@@ -43,6 +43,11 @@ __device__ inline void report_error(ErrRec* e, int32_t code, int32_t site, int64
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
 
+// The constant-rate (100 MHz) real-time counter, common to all compute units.
+__device__ inline int64_t now_ticks() { return (int64_t)__builtin_amdgcn_s_memrealtime(); }
+// The shader-clock cycle counter (its rate is the actual clock).
+__device__ inline int64_t now_cycles() { return (int64_t)__builtin_amdgcn_s_memtime(); }
+
 // A flag above the awaited epoch breaks the epoch rule (epochs increase from
 // run to run, and a producer stores exactly the run's epoch): the slot holds
 // a signal of a later run, or the caller awaits a stale epoch.  The wait

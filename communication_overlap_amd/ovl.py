@@ -35,7 +35,7 @@ EXPORTS = (
     "ag_gemm_plan", "ag_gemm_plan_destroy", "ag_gemm_num_units", "ag_gemm_flags_bytes",
     "ag_gemm_workspace_bytes", "ag_gemm_splits", "ag_gemm_run",
     "gemm_rs_flags_bytes", "gemm_rs_workspace_bytes", "gemm_rs_run",
-    "a2a_flags_bytes", "a2a_workspace_bytes", "a2a_dispatch_grouped_gemm_run",
+    "a2a_flags_bytes", "a2a_workspace_bytes", "a2a_trace_bytes", "a2a_dispatch_grouped_gemm_run",
     "a2a_combine_flags_bytes", "a2a_combine_workspace_bytes", "a2a_combine_run",
     "ovl_flags_reset", "ovl_check", "ovl_strerror", "ovl_copy",
     "ring_allreduce_flags_bytes", "ring_allreduce_workspace_bytes", "ring_allreduce_run",
@@ -124,6 +124,8 @@ def lib() -> ctypes.CDLL:
     L.a2a_flags_bytes.restype = c_size_t
     L.a2a_workspace_bytes.argtypes = [POINTER(A2aDesc)]
     L.a2a_workspace_bytes.restype = c_size_t
+    L.a2a_trace_bytes.argtypes = [POINTER(A2aDesc)]
+    L.a2a_trace_bytes.restype = c_size_t
     L.a2a_dispatch_grouped_gemm_run.argtypes = [POINTER(A2aDesc), POINTER(c_void_p), POINTER(c_void_p), c_void_p,
                                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                                 c_int64, POINTER(Opts), c_void_p]
@@ -314,10 +316,14 @@ def a2a_workspace_bytes(desc: A2aDesc) -> int:
     return lib().a2a_workspace_bytes(byref(desc))
 
 
+def a2a_trace_bytes(desc: A2aDesc) -> int:
+    return lib().a2a_trace_bytes(byref(desc))
+
+
 def a2a_dispatch_grouped_gemm_run(desc: A2aDesc, x, topk_idx, w, recv_x, recv_src, recv_count, y, flags,
                                   workspace, epoch: int, mode: int = MODE_FUSED, producers: int = 0,
-                                  spin_limit: int = 0, stream=None, raise_on_error: bool = True) -> int:
-    o = _opts(mode, producers, spin_limit)
+                                  spin_limit: int = 0, stream=None, raise_on_error: bool = True, trace=None) -> int:
+    o = _opts(mode, producers, spin_limit, trace)
     st = lib().a2a_dispatch_grouped_gemm_run(byref(desc), _ptr_array(x), _ptr_array(topk_idx), _ptr(w),
                                              _ptr(recv_x), _ptr(recv_src), _ptr(recv_count), _ptr(y), _ptr(flags),
                                              _ptr(workspace), epoch, byref(o), _stream(stream))
@@ -332,8 +338,8 @@ def fp8_quantize_rows(in_bf16, codes, scale, rows: int, cols: int, stream=None, 
 def a2a_dispatch_grouped_gemm_fp8_run(desc: A2aDesc, x8, x_scale, topk_idx, w8, w_scale, recv_x8, recv_scale,
                                       recv_src, recv_count, y, flags, workspace, epoch: int, mode: int = MODE_FUSED,
                                       producers: int = 0, spin_limit: int = 0, stream=None,
-                                      raise_on_error: bool = True) -> int:
-    o = _opts(mode, producers, spin_limit)
+                                      raise_on_error: bool = True, trace=None) -> int:
+    o = _opts(mode, producers, spin_limit, trace)
     st = lib().a2a_dispatch_grouped_gemm_fp8_run(byref(desc), _ptr_array(x8), _ptr_array(x_scale),
                                                  _ptr_array(topk_idx), _ptr(w8), _ptr(w_scale), _ptr(recv_x8),
                                                  _ptr(recv_scale), _ptr(recv_src), _ptr(recv_count), _ptr(y),

@@ -85,8 +85,9 @@ typedef struct ovl_opts {
   uint32_t mode;        /* OVL_MODE_* */
   uint32_t producers;   /* producer workgroups; 0 = library default */
   uint64_t spin_limit;  /* polls before a wait gives up (OVL_ETIMEOUT); 0 = default (~2^22) */
-  int64_t* trace;       /* AG-GEMM only: device buffer of ag_gemm_trace_bytes() bytes that the
-                           run fills with timestamps (see there), or NULL for none */
+  int64_t* trace;       /* AG-GEMM and dispatch: zero-filled device buffer of ag_gemm_trace_bytes()
+                           or a2a_trace_bytes() bytes that the run fills with timestamps (see
+                           there), or NULL for none */
   uint32_t jitter;      /* AG-GEMM only, a test aid: before moving each unit a producer
                            workgroup sleeps h(unit, epoch) mod (jitter + 1) intervals of about
                            64 shader clocks (h a fixed integer hash), so that units arrive in
@@ -338,6 +339,23 @@ typedef struct a2a_desc {
 
 size_t a2a_flags_bytes(const a2a_desc* desc);      /* ranks * flag_stride */
 size_t a2a_workspace_bytes(const a2a_desc* desc);
+
+/* Device trace of a fused dispatch -> grouped GEMM run (bf16 or FP8; the
+ * pages ask to profile overlap efficiency: "Triton-distributed Semantics",
+ * Best Practices), int64 records in 10 ns ticks of the 100 MHz real-time
+ * counter (as for ag_gemm_trace_bytes):
+ *   [s], s < R:        the time slice s's flag was published by a copy (0: not
+ *                      by a copy: an empty slice);
+ *   [R + p], p < 64:   the time producer workgroup p finished copying;
+ *   [R + 64 + 8 j + 0] work item j's start, [+1] its end (after its stores),
+ *                      [+2] ticks it spent waiting for slices (copying chunks
+ *                      meanwhile), [+3] chunks it copied while waiting, [+4] the
+ *                      consumer that ran it, [+5] expert, [+6] m-tile, [+7] n-tile
+ *                      (items in the launch's item order; unused records stay 0).
+ * A bound for any routing: 8 * (R + 64 + 8 * (R * cap / 256 + E) * ceil(n / 128))
+ * bytes, cap = tokens * min(topk, E); 0 for an invalid desc.  Only fused
+ * (and GEMM_ONLY: no waits) runs record items. */
+size_t a2a_trace_bytes(const a2a_desc* desc);
 
 /* x:        HOST array[R] of bf16 [tokens][hidden] device buffers.
  * topk_idx: HOST array[R] of int32 [tokens][topk] device buffers (global expert ids;

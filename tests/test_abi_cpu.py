@@ -219,6 +219,9 @@ def test_flag_and_workspace_sizes():
     ad = o.a2a_desc(8, 0, 4096, 4096, 1408, 2, 64, 8, 128)
     assert o.a2a_flags_bytes(ad) == 8 * 128
     assert o.a2a_workspace_bytes(ad) >= o.ERROR_RECORD_BYTES + 8 * 8
+    # the trace holds slices, 64 producers and 8 int64 per possible work item:
+    # m-tiles <= 8 * 8192 / 256 + 8, n-tiles of 128 columns: 11
+    assert o.a2a_trace_bytes(ad) == 8 * (8 + 64 + 8 * (8 * 8192 // 256 + 8) * 11)
 
 
 @pytest.mark.parametrize("name,tpf,splits", [

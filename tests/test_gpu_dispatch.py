@@ -47,7 +47,7 @@ class A2aCase:
         o.ovl_flags_reset(self.flags, self.fbytes, self.ws, self.ws.numel())
         self.fill = 0  # what rows past a slice's count hold
 
-    def run(self, epoch, mode=0, producers=0, spin_limit=0, poison=True):
+    def run(self, epoch, mode=0, producers=0, spin_limit=0, poison=True, trace=None):
         o = ovl()
         if poison and mode != o.MODE_GEMM_ONLY and self.recv_x.numel():
             self.recv_x.fill_(NAN_BF16)
@@ -55,7 +55,7 @@ class A2aCase:
         say(f"  a2a_run {self.cfg.name} epoch={epoch} mode={mode}")
         o.a2a_dispatch_grouped_gemm_run(self.desc, self.d_x, self.d_topk, self.d_w, self.recv_x, self.recv_src,
                                         self.recv_count, self.y, self.flags, self.ws, epoch, mode=mode,
-                                        producers=producers, spin_limit=spin_limit)
+                                        producers=producers, spin_limit=spin_limit, trace=trace)
         return o.ovl_check(self.ws, raise_on_error=False)
 
     def oracle_layout(self):
@@ -240,3 +240,37 @@ def test_repeated_local_expert_overflow_is_clipped_and_reported():
     assert np.array_equal(src, np.repeat(np.arange(cfg.tokens, dtype=np.int32), 3)[None, :cfg.cap].repeat(2, 0))
     with pytest.raises(ValueError):
         oracle.dispatch(case.x, topk, cfg.rank, cfg.experts_per_rank, cfg.cap)
+
+
+def test_trace_records_every_item_and_slice():
+    """The device trace of a fused run (a2a_trace_bytes): one record per work
+    item (m-tiles of 256 rows of each expert x n-tiles of 256 columns, from
+    the oracle's counts), each ending after it starts, run by a valid
+    consumer, with its expert and tiles in range; a publish time for every
+    slice with rows; outputs as without tracing."""
+    import torch
+    o = ovl()
+    cfg = _cfg("a2a_trace", R=4, T=300, H=256, N=296, E=3, rank=2, seed=12)
+    case = A2aCase(cfg)
+    tb = o.a2a_trace_bytes(case.desc)
+    R, E = cfg.ranks, cfg.experts_per_rank
+    tr = torch.zeros(tb // 8, dtype=torch.int64, device="cuda")
+    st, det = case.run(1, trace=tr)
+    assert st == 0, det
+    rx, rs, rc = case.check_layout(1)
+    y_ref = oracle.grouped_gemm(rx, rc, case.w)
+    assert max_err(host(case.y), y_ref) <= gemm_tol(cfg.hidden, float(np.abs(y_ref).max()))
+    t = host(tr)
+    slices, items = t[:R], t[R + 64:].reshape(-1, 8)
+    done = items[items[:, 1] > 0]
+    rows_e = rc.sum(axis=0)
+    n_items = int(sum(-(-int(r) // 256) for r in rows_e)) * -(-cfg.n // 256)
+    assert len(done) == n_items, (len(done), n_items)
+    assert (done[:, 1] >= done[:, 0]).all() and (done[:, 2] >= 0).all() and (done[:, 3] >= 0).all()
+    assert ((done[:, 5] >= 0) & (done[:, 5] < E)).all() and ((done[:, 7] >= 0) & (done[:, 7] < -(-cfg.n // 256))).all()
+    assert (done[:, 4] >= 0).all()
+    for e in range(E):  # each m-tile of each expert appears once per n-tile
+        mts = done[done[:, 5] == e][:, 6]
+        assert sorted(np.unique(mts).tolist()) == list(range(-(-int(rows_e[e]) // 256))), e
+    copied = [s for s in range(R) if rc[s].sum() > 0]
+    assert all(slices[s] > 0 for s in copied), slices
