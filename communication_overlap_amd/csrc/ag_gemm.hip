@@ -318,8 +318,9 @@ __device__ inline void produce(const AgArgs& a, int w, int P, const Sched* sc, b
 // producer order; a unit the order omits stays unmoved.
 template <int NT>
 __device__ inline void produce_boot(const AgArgs& a, int w, int G, const Sched& sc) {
-  const int items = sc.n_boot * a.batches;
-  for (int i = w; i < items; i += G)
+  // A loop around barriers: its bound and counter are scalars to the compiler.
+  const int items = uniform(sc.n_boot * a.batches);
+  for (int i = w; uniform(i) < items; i += G)
     if (uniform((sc.present[i >> 5] >> (i & 31)) & 1u))
       move_unit<NT>(a, uniform(sc.boot[i / a.batches]) * a.batches + i % a.batches, true);
 }

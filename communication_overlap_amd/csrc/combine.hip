@@ -264,7 +264,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
                          __HIP_MEMORY_SCOPE_AGENT);
     // Slices in position order rank+1, rank+2, ...: each is complete (and
     // signalled) before the next begins, so peers can start on it early.
-    for (int pos = 0; pos + 1 < a.ranks; ++pos) {
+    const int ranks = uniform(a.ranks);  // a loop around barriers: bounded by a scalar
+    for (int pos = 0; pos + 1 < ranks; ++pos) {
       const int s = cb_slice_at(a, pos);
       const int rows = uniform(g.rows[s]);
       if (rows) cb_put_slice(a, s, rows);
