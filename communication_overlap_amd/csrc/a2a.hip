@@ -74,7 +74,7 @@ struct A2aArgs {
   int64_t* flags;
   int64_t* counters;  // [R] slice arrival counters (workspace)
   int64_t* trace;     // optional timestamps (a2a_trace_bytes), or null
-  int64_t* ticket;    // next chunk to copy in the fused launch (workspace)
+  int64_t* ticket;    // [0] next chunk to copy, [1] next shared tile, in the fused launch (workspace)
   ErrRec* err;
   int64_t tokens, hidden, n, cap;
   int64_t row_bytes;    // bytes of one token row: hidden * 2 (bf16) or hidden (FP8)
@@ -170,7 +170,10 @@ __global__ __launch_bounds__(kThreads) void a2a_layout_kernel(A2aArgs a) {
     if (cnt < cnt_total) report_error(a.err, OVL_ESHAPE, kSiteA2aCap, s, (int64_t)base_total + cnt_total, a.cap);
     a.recv_count[s * a.experts + e] = cnt;
     if (e == 0) a.counters[s] = 0;
-    if (blockIdx.x == 0) *a.ticket = 0;
+    if (blockIdx.x == 0) {
+      a.ticket[0] = 0;
+      a.ticket[1] = 0;
+    }
   }
 }
 
@@ -500,8 +503,27 @@ __device__ bool wait_slice_helping(const A2aArgs& a, const Geometry* g, int s, i
   return ok != 0;
 }
 
+// The next tile of the shared tail (fused launch): every thread returns it.
+// The barrier before the thread-0 branch keeps it apart from the previous
+// tile's thread-0 trace record.
+__device__ inline int take_tile(const A2aArgs& a, int* sh) {
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *sh = (int)__hip_atomic_fetch_add(a.ticket + 1, (int64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int t = uniform(*sh);
+  __syncthreads();  // *sh is rewritten by the next call
+  return t;
+}
+
+// Tiles of one workgroup.  Consumer cidx (cidx >= 0) first takes its static
+// share of `srounds` whole rounds (tiles w * Cn + x * per + q: dies take
+// consecutive tiles); the tiles after those rounds form a tail that every
+// workgroup takes from a ticket counter once it is free: consumers after
+// their static share, producers (cidx < 0) once the copy is handed out, so
+// no compute unit idles at the end.
 template <bool WAIT, bool F8>
-__device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint16_t* lds) {
+__device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint16_t* lds, int64_t srounds) {
   __shared__ int sh[2];
   // Per tile (double-buffered): [0] the y row of each tile row (s * cap +
   // slice row; also the A row in recv_x), or -1; [1] for own-slice tiles,
@@ -517,8 +539,9 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
   const int x = cidx % groups, q = cidx / groups;
   int waited_hi = -1;  // slice positions [0, waited_hi] are acquired
   bool timed_out = false;
+  const int64_t tail = srounds * Cn;  // first tile of the shared tail
   for (int64_t wv = 0;; ++wv) {
-    const int64_t j = wv * Cn + (int64_t)x * per + q;
+    const int64_t j = (cidx >= 0 && wv < srounds) ? wv * Cn + (int64_t)x * per + q : tail + take_tile(a, sh);
     if (j >= total) break;
     int e, mt;
     mtile_at(a, g, (int)(j / ntn), &e, &mt);
@@ -620,6 +643,16 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
   }
 }
 
+// Whole rounds of the fused launch's tiles dealt statically to the
+// consumers: one round fewer than all workgroups would fill, so that the
+// tail (at least one round) is shared with the producers.
+__device__ inline int64_t a2a_static_rounds(const A2aArgs& a, const Geometry* g, bool f8) {
+  const int tbn = f8 ? kGbn8 : kGbn;
+  const int64_t total = (int64_t)uniform(g->n_mt) * ((a.n + tbn - 1) / tbn);
+  const int64_t r = total / (a.consumers + a.producers) - 1;
+  return r > 0 ? r : 0;
+}
+
 // Fused launch.  Producer workgroups take chunk tickets until none is
 // left; consumers take tickets too whenever the slice of their next tile is
 // not complete yet, so the first consumers copy the first slices together
@@ -641,10 +674,13 @@ __global__ __launch_bounds__(64 * a2a_waves(F8), 1) void a2a_fused_kernel(A2aArg
       for (int ch; (ch = take_chunk(a, total, &sh)) < total;) a2a_copy_chunk_deferred(a, g, ch, &pend_pos, &pend_n);
       if (pend_n) a2a_arrive(a, g, pend_pos, pend_n);
       if (a.trace && threadIdx.x == 0 && blockIdx.x < kA2aTraceProducers) a.trace[a.ranks + blockIdx.x] = now_ticks();
+      // The copy is handed out: take tiles of the shared tail.
+      a2a_consume<true, F8>(a, g, -1, lds, a2a_static_rounds(a, g, F8));
       return;
     }
   }
-  a2a_consume<MODE == 0, F8>(a, g, (int)blockIdx.x - a.producers, lds);
+  a2a_consume<MODE == 0, F8>(a, g, (int)blockIdx.x - a.producers, lds,
+                             MODE == 0 ? a2a_static_rounds(a, g, F8) : (int64_t)1 << 40);
 }
 
 constexpr int a2a_lds_bytes() { return kA2aGemmLds + (int)sizeof(Geometry); }
@@ -671,10 +707,10 @@ extern "C" size_t a2a_trace_bytes(const a2a_desc* d) {
   return 8 * ((size_t)d->ranks + kA2aTraceProducers + (size_t)kA2aTraceItem * (size_t)(mts * nts));
 }
 
-// Error record, slice arrival counters, chunk ticket.
+// Error record, slice arrival counters, chunk and tile tickets.
 extern "C" size_t a2a_workspace_bytes(const a2a_desc* d) {
   if (!d || d->ranks < 1) return 0;
-  return OVL_ERROR_RECORD_BYTES + 8 * (size_t)kA2aMaxRanks + 8;
+  return OVL_ERROR_RECORD_BYTES + 8 * (size_t)kA2aMaxRanks + 16;
 }
 
 namespace ovl {
@@ -794,12 +830,14 @@ ovl_status a2a_run(const a2a_desc* d, bool f8, const void* const* x, const float
   int P = 0;
   if (mode == OVL_MODE_FUSED) {
     // Few dedicated producers: consumers take chunks themselves whenever
-    // the slice they need is behind.  Measured with 256x256 tiles: 16
-    // producers beat 8 and 64 while every tile waited for a copied slice;
-    // with the own-slice tiles reading in place, 32 (fused 622-644 us)
-    // beat 16 (664-675), 24 and 48 (640-662) and 64 (689) for bf16 rows,
-    // and for FP8 rows 32 (447-448) beat 8, 16, 24 and 48 (451-492).
-    P = req ? (int)req : 4 * kA2aXcds;
+    // the slice they need is behind, and the producers take tiles of the
+    // shared tail once the copy is handed out.  Measured with 256x256
+    // tiles and the shared tail (one box, same run): 48 producers (bf16
+    // fused 586-587 us, FP8 433-434) beat 32 (603-646, 431-460), 40, 56,
+    // 64 (608, 456) and 96 or more; without the tail, 32 had been best
+    // (600-628, 455-473), as a producer's compute unit then idled after
+    // the copy.
+    P = req ? (int)req : 6 * kA2aXcds;
     if (P >= resident) return OVL_EINVAL;
   }
   int64_t Cn = resident - P;

@@ -350,7 +350,8 @@ size_t a2a_workspace_bytes(const a2a_desc* desc);
  *   [R + 64 + 8 j + 0] work item j's start, [+1] its end (after its stores),
  *                      [+2] ticks it spent waiting for slices (copying chunks
  *                      meanwhile), [+3] chunks it copied while waiting, [+4] the
- *                      consumer that ran it, [+5] expert, [+6] m-tile, [+7] n-tile
+ *                      consumer that ran it (-1: a producer, after the copy),
+ *                      [+5] expert, [+6] m-tile, [+7] n-tile
  *                      (items in the launch's item order; unused records stay 0).
  * A bound for any routing: 8 * (R + 64 + 8 * (R * cap / 256 + E) * ceil(n / 128))
  * bytes, cap = tokens * min(topk, E); 0 for an invalid desc.  Only fused
