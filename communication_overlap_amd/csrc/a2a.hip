@@ -97,43 +97,37 @@ __device__ inline int wave_incl_scan(int v) {
   return v;
 }
 
-// Exclusive scan of v over the workgroup (blockDim.x = 256); *total gets the sum.
-__device__ inline int block_excl_scan(int v, int* total, int* smem) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int incl = wave_incl_scan(v);
-  if (lane == 63) smem[wave] = incl;
-  __syncthreads();
-  int before = 0, sum = 0;
-  for (int i = 0; i < kThreads / 64; ++i) {
-    const int wsum = smem[i];
-    if (i < wave) before += wsum;
-    sum += wsum;
-  }
-  __syncthreads();
-  *total = sum;
-  return before + incl - v;
-}
+// Sum of v over the wavefront (every lane gets it).
+__device__ inline int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_incl_scan(v), 63); }
 
-// One workgroup per (source s, local expert e).  Each thread takes a
-// contiguous run of tokens; for the entries (token t, choice j) of its run it
-// counts those routed to local experts below e (which place expert e's
-// segment in the slice) and those routed to e, whose rows it then fills in
-// (t, j) order after an exclusive scan of the per-thread counts.  Rows of a
-// slice are thus ordered by (expert, token, choice), as the layout defines.
+// One workgroup per (source s, local expert e).  Wave w takes a contiguous
+// range of the source's (token, choice) entries and reads it 64 entries at a
+// time, lane l the l-th (coalesced; eight loads in flight).  Pass 1 counts
+// the entries routed to local experts below e (which place expert e's
+// segment in the slice) and to e; the wave totals give each wave's share of
+// the segment; pass 2 reads the range again and writes expert e's rows in
+// entry order, each matching lane at its wave's running count plus the
+// matches of the lanes below it (a ballot).  Rows of a slice are thus
+// ordered by (expert, token, choice), as the layout defines.
 __global__ __launch_bounds__(kThreads) void a2a_layout_kernel(A2aArgs a) {
-  __shared__ int smem[8];
+  constexpr int NWV = kThreads / 64;
+  constexpr int B = 8;  // 64-entry groups loaded before they are looked at
+  __shared__ int smem[2 * NWV];
   const int s = blockIdx.x / a.experts, e = blockIdx.x % a.experts;
   const int32_t* idx = a.topk[s];
   const int e_lo = a.rank * a.experts;
-  const int64_t T = a.tokens;
-  const int64_t per = (T + kThreads - 1) / kThreads;
-  const int64_t i0 = min(T, per * threadIdx.x) * a.topk_n, i1 = min(T, per * (threadIdx.x + 1)) * a.topk_n;
-  constexpr int B = 32;  // entries loaded before they are looked at
+  const int lane = lane_id(), wave = uniform(threadIdx.x >> 6);
+  const int64_t NE = a.tokens * a.topk_n;
+  const int64_t per_w = ((NE + NWV - 1) / NWV + 63) / 64 * 64;
+  const int64_t w0 = min(NE, wave * per_w), w1 = min(NE, w0 + per_w);
   int lt = 0, eq = 0;
-  for (int64_t i = i0; i < i1; i += B) {
+  for (int64_t i = w0; i < w1; i += 64 * B) {
     int32_t v[B];
 #pragma unroll
-    for (int q = 0; q < B; ++q) v[q] = i + q < i1 ? idx[i + q] : -1;
+    for (int q = 0; q < B; ++q) {
+      const int64_t k = i + 64 * q + lane;
+      v[q] = k < w1 ? idx[k] : -1;
+    }
 #pragma unroll
     for (int q = 0; q < B; ++q) {
       const int ex = v[q] - e_lo;
@@ -141,9 +135,20 @@ __global__ __launch_bounds__(kThreads) void a2a_layout_kernel(A2aArgs a) {
       eq += ex == e;
     }
   }
-  int base_total, cnt_total;
-  block_excl_scan(lt, &base_total, smem);
-  int pos = base_total + block_excl_scan(eq, &cnt_total, smem);
+  lt = wave_sum(lt);
+  eq = wave_sum(eq);
+  if (lane == 0) {
+    smem[wave] = eq;
+    smem[NWV + wave] = lt;
+  }
+  __syncthreads();
+  int base_total = 0, cnt_total = 0, before = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    base_total += smem[NWV + w];
+    cnt_total += smem[w];
+    if (w < wave) before += smem[w];
+  }
   // A slice holds at most cap rows.  Only routing rows that repeat a local
   // expert (which the call's contract excludes) can ask for more; then the
   // rows past cap are dropped, the counts are clipped so that every later
@@ -151,19 +156,23 @@ __global__ __launch_bounds__(kThreads) void a2a_layout_kernel(A2aArgs a) {
   const int64_t end = min((int64_t)base_total + cnt_total, a.cap);
   const int cnt = (int)max((int64_t)0, end - base_total);
   if (eq) {
-    // Loads in batches again: the stores below may alias them, so a plain
-    // loop would wait out one load per entry.
     int32_t* dst = a.recv_src + (int64_t)s * a.cap;
-    for (int64_t i = i0; i < i1; i += B) {
+    int64_t run = (int64_t)base_total + before;  // next row of this wave
+    for (int64_t i = w0; i < w1; i += 64 * B) {
       int32_t v[B];
 #pragma unroll
-      for (int q = 0; q < B; ++q) v[q] = i + q < i1 ? idx[i + q] : -1;
+      for (int q = 0; q < B; ++q) {
+        const int64_t k = i + 64 * q + lane;
+        v[q] = k < w1 ? idx[k] : -1;
+      }
 #pragma unroll
-      for (int q = 0; q < B; ++q)
-        if (v[q] - e_lo == e) {
-          if (pos < end) dst[pos] = (int32_t)((i + q) / a.topk_n);
-          ++pos;
-        }
+      for (int q = 0; q < B; ++q) {
+        const bool hit = v[q] - e_lo == e;
+        const uint64_t m = __ballot(hit);
+        const int64_t pos = run + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (hit && pos < end) dst[pos] = (int32_t)((i + 64 * q + lane) / a.topk_n);
+        run += __popcll(m);
+      }
     }
   }
   if (threadIdx.x == 0) {
