@@ -59,38 +59,33 @@ __device__ inline int wave_incl_scan(int v) {
   return v;
 }
 
-__device__ inline int block_excl_scan(int v, int* total, int* smem) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int incl = wave_incl_scan(v);
-  if (lane == 63) smem[wave] = incl;
-  __syncthreads();
-  int before = 0, sum = 0;
-  for (int i = 0; i < kThreads / 64; ++i) {
-    const int wsum = smem[i];
-    if (i < wave) before += wsum;
-    sum += wsum;
-  }
-  __syncthreads();
-  *total = sum;
-  return before + incl - v;
-}
+// Sum of v over the wavefront (every lane gets it).
+__device__ inline int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_incl_scan(v), 63); }
 
 // Workgroup (q, e): the choices of this rank's tokens that pick global
 // expert q*E + e take rows base + 0, 1, ... of q's slice, base = the count
-// of choices picking q's experts below e; order (token, choice).
+// of choices picking q's experts below e; order (token, choice).  Wave w
+// takes a contiguous range of the choices and reads it 64 at a time, lane l
+// the l-th (coalesced); the wave totals give each wave's first row, and a
+// ballot each matching lane's place after the matches of the lanes below.
 __global__ __launch_bounds__(kThreads) void combine_layout_kernel(CombineArgs a) {
-  __shared__ int smem[8];
+  constexpr int NWV = kThreads / 64;
+  constexpr int B = 8;  // 64-choice groups loaded before they are looked at
+  __shared__ int smem[2 * NWV];
   const int q = blockIdx.x / a.experts, e = blockIdx.x % a.experts;
   const int e_lo = q * a.experts;
-  const int64_t T = a.tokens;
-  const int64_t per = (T + kThreads - 1) / kThreads;
-  const int64_t i0 = min(T, per * threadIdx.x) * a.topk_n, i1 = min(T, per * (threadIdx.x + 1)) * a.topk_n;
-  constexpr int B = 32;
+  const int lane = lane_id(), wave = uniform(threadIdx.x >> 6);
+  const int64_t NE = a.tokens * a.topk_n;
+  const int64_t per_w = ((NE + NWV - 1) / NWV + 63) / 64 * 64;
+  const int64_t w0 = min(NE, wave * per_w), w1 = min(NE, w0 + per_w);
   int lt = 0, eq = 0;
-  for (int64_t i = i0; i < i1; i += B) {
+  for (int64_t i = w0; i < w1; i += 64 * B) {
     int32_t v[B];
 #pragma unroll
-    for (int j = 0; j < B; ++j) v[j] = i + j < i1 ? a.topk[i + j] : -1;
+    for (int j = 0; j < B; ++j) {
+      const int64_t k = i + 64 * j + lane;
+      v[j] = k < w1 ? a.topk[k] : -1;
+    }
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int ex = v[j] - e_lo;
@@ -98,17 +93,33 @@ __global__ __launch_bounds__(kThreads) void combine_layout_kernel(CombineArgs a)
       eq += ex == e;
     }
   }
-  int base_total, cnt_total;
-  block_excl_scan(lt, &base_total, smem);
-  int p = base_total + block_excl_scan(eq, &cnt_total, smem);
+  lt = wave_sum(lt);
+  eq = wave_sum(eq);
+  if (lane == 0) {
+    smem[wave] = eq;
+    smem[NWV + wave] = lt;
+  }
+  __syncthreads();
+  int run = 0;  // first row of this wave's matches
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) run += smem[NWV + w] + (w < wave ? smem[w] : 0);
   if (eq)
-    for (int64_t i = i0; i < i1; i += B) {  // loads batched again: the stores may alias them
+    for (int64_t i = w0; i < w1; i += 64 * B) {
       int32_t v[B];
 #pragma unroll
-      for (int j = 0; j < B; ++j) v[j] = i + j < i1 ? a.topk[i + j] : -1;
+      for (int j = 0; j < B; ++j) {
+        const int64_t k = i + 64 * j + lane;
+        v[j] = k < w1 ? a.topk[k] : -1;
+      }
 #pragma unroll
-      for (int j = 0; j < B; ++j)
-        if (v[j] - e_lo == e) a.pos[i + j] = p++;
+      for (int j = 0; j < B; ++j) {
+        const bool hit = v[j] - e_lo == e;
+        const uint64_t m = __ballot(hit);
+        if (hit)
+          a.pos[i + 64 * j + lane] =
+              run + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        run += __popcll(m);
+      }
     }
   if (blockIdx.x == 0 && threadIdx.x < a.ranks) a.counters[threadIdx.x] = 0;
 }
