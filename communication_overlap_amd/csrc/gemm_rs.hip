@@ -28,12 +28,13 @@ namespace ovl {
 namespace {
 
 constexpr int kRsMaxRanks = 16;
-constexpr int kRsTile = 256;
 constexpr int kRsXcds = 8;
-// Wavefronts per workgroup: the 256 x 256 tile as a 2 x 4 grid of waves, two
-// per SIMD (one's MFMAs cover the other's LDS reads; measured faster than 4).
-constexpr int kRsWaves = 8;
-constexpr int kRsThreads = 64 * kRsWaves;
+// Tiles: 256 x 256 (the default) or 128 x 128.  Wavefronts per workgroup:
+// the 256 x 256 tile as a 2 x 4 grid of waves, two per SIMD (one's MFMAs
+// cover the other's LDS reads; measured faster than 4); the 128 x 128 tile
+// as 2 x 2.
+template <int TILE>
+constexpr int rs_waves() { return TILE == 256 ? 8 : 4; }
 
 struct RsArgs {
   float* peer_out[kRsMaxRanks];
@@ -55,10 +56,12 @@ struct RsArgs {
   int32_t sync;         // 0: no in/out flag traffic (measurement of the work alone)
 };
 
-// Own-row space: own tile t owns rows [t*256, t*256 + 256) of it (tile row
-// trow*256 + r of the block, columns of tile column tcol).  Job j of J covers
-// [j*OR/J, (j+1)*OR/J), OR = tiles_per_block * 256.
-__device__ inline int64_t job_begin(int64_t j, int64_t J, int64_t OR) { return j * OR / J; }
+// Own-row space: own tile t owns rows [t*TILE, t*TILE + TILE) of it (tile
+// row trow*TILE + r of the block, columns of tile column tcol), cut into
+// lines of 64 lanes x 4 columns: one row of a 256-wide tile, two rows of a
+// 128-wide one.  Job j of J covers lines [j*OL/J, (j+1)*OL/J), OL =
+// tiles_per_block * TILE / rows per line.
+__device__ inline int64_t job_begin(int64_t j, int64_t J, int64_t OL) { return j * OL / J; }
 
 // 16 bytes per lane from global memory straight into LDS at lds_block +
 // 16 * lane (gfx950's global load to LDS; no registers hold the data).
@@ -66,16 +69,21 @@ __device__ inline void gload16_to_lds(const void* g, uint32_t lds_block) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds_block), "v"(g) : "memory", "m0");
 }
 
-// Rows [q0, q1) of the own-row space: out = acc + ((P_a + P_b) + ...), the
-// partials in ascending peer order.  64 lanes of 16 bytes cover one
-// 256-column row.  Each wave stages the accumulator row and the R-1 partial
-// rows of `rw` rows (1 KiB each) in its own 16 KiB of the idle GEMM stage
+// Lines [q0, q1) of the own-row space: out = acc + ((P_a + P_b) + ...), the
+// partials in ascending peer order.  64 lanes of 16 bytes cover one line
+// (a 256-column row, or two 128-column rows).  Each wave stages the
+// accumulator line and the R-1 partial lines of `rw` lines (1 KiB each) in
+// its own 16 KiB of the idle GEMM stage
 // area with global-to-LDS loads, all issued before the first add, then
 // sums them: twice the rows in flight that registers allowed (measured:
 // fused 169 -> 156-163 us, reduction-included GEMM-only 163-165 -> 151-152
 // us at 8192x4096x1792 over 8 ranks).  Index arithmetic is 32-bit (a block
 // has fewer than 2^31 elements).
+template <int TILE>
 __device__ void reduce_rows_lds(const RsArgs& a, int64_t q0, int64_t q1, uint16_t* lds) {
+  constexpr int LPR = TILE / 4;      // lanes per row
+  constexpr int RPL = 64 / LPR;      // rows per line
+  constexpr int LPT = TILE / RPL;    // lines per tile
   uint8_t* l8 = reinterpret_cast<uint8_t*>(lds);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -83,14 +91,14 @@ __device__ void reduce_rows_lds(const RsArgs& a, int64_t q0, int64_t q1, uint16_
   const int rw = R <= 8 ? 2 : 1;
   const uint32_t wbase = lds_addr(l8) + (uint32_t)w * 16384u;
   const int tc = a.tc, n = (int)a.n, bm = (int)a.bm;
-  for (int q = (int)q0 + w * rw; q < (int)q1; q += kRsWaves * rw) {
+  for (int q = (int)q0 + w * rw; q < (int)q1; q += rs_waves<TILE>() * rw) {
     for (int u = 0; u < rw; ++u) {
       const int qq = q + u;
-      const int t = qq / kRsTile;
-      const int row = (t / tc) * kRsTile + (qq % kRsTile);
-      const int col = (t % tc) * kRsTile + lane * 4;
-      if (qq >= (int)q1 || row >= bm) continue;  // wave-uniform
-      if (col >= n) continue;                    // lanes past N load nothing
+      const int t = qq / LPT;
+      const int row = (t / tc) * TILE + (qq % LPT) * RPL + lane / LPR;
+      const int col = (t % tc) * TILE + (lane % LPR) * 4;
+      if (qq >= (int)q1) continue;               // wave-uniform
+      if (row >= bm || col >= n) continue;       // lanes past M or N load nothing
       const int off = row * n + col;
       const uint32_t slot = wbase + (uint32_t)u * 8192u;
       gload16_to_lds(a.out + off, slot);
@@ -102,9 +110,9 @@ __device__ void reduce_rows_lds(const RsArgs& a, int64_t q0, int64_t q1, uint16_
     wave_drain();
     for (int u = 0; u < rw; ++u) {
       const int qq = q + u;
-      const int t = qq / kRsTile;
-      const int row = (t / tc) * kRsTile + (qq % kRsTile);
-      const int col = (t % tc) * kRsTile + lane * 4;
+      const int t = qq / LPT;
+      const int row = (t / tc) * TILE + (qq % LPT) * RPL + lane / LPR;
+      const int col = (t % tc) * TILE + (lane % LPR) * 4;
       if (qq >= (int)q1 || row >= bm || col >= n) continue;
       const uint8_t* slot = l8 + (size_t)w * 16384 + (size_t)u * 8192 + (size_t)lane * 16;
       const f32x4 acc = *OVL_LDS(const f32x4, slot);
@@ -115,10 +123,12 @@ __device__ void reduce_rows_lds(const RsArgs& a, int64_t q0, int64_t q1, uint16_
   }
 }
 
+template <int TILE>
 __device__ void reduce_job(const RsArgs& a, int64_t j, int64_t J, bool& timed_out, uint16_t* lds) {
+  constexpr int LPT = TILE * TILE / 256;  // lines per tile
   const int tpb = a.tr * a.tc;
-  const int64_t OR = (int64_t)tpb * kRsTile;
-  const int64_t q0 = job_begin(j, J, OR), q1 = job_begin(j + 1, J, OR);
+  const int64_t OL = (int64_t)tpb * LPT;
+  const int64_t q0 = job_begin(j, J, OL), q1 = job_begin(j + 1, J, OL);
   if (q0 >= q1) return;
   // Wave 0 waits for the own tiles this job touches and, with flags on, for
   // every peer's partial of them; the barrier hands the acquire to the
@@ -129,7 +139,7 @@ __device__ void reduce_job(const RsArgs& a, int64_t j, int64_t J, bool& timed_ou
   // t0 + i / R, and within it the own-tile flag (peer slot `rank`) or peer
   // p's in flag.
   if (threadIdx.x < 64 && !timed_out) {
-    const int64_t t0 = q0 / kRsTile, nt = (q1 - 1) / kRsTile - t0 + 1;
+    const int64_t t0 = q0 / LPT, nt = (q1 - 1) / LPT - t0 + 1;
     const int64_t nflags = nt * (a.sync ? a.ranks : 1);
     // (32-bit index arithmetic: a job has few flags, and a poll should not
     // pay for 64-bit divisions.)
@@ -170,13 +180,13 @@ __device__ void reduce_job(const RsArgs& a, int64_t j, int64_t J, bool& timed_ou
     wave_acquire();
   }
   __syncthreads();
-  reduce_rows_lds(a, q0, q1, lds);
+  reduce_rows_lds<TILE>(a, q0, q1, lds);
 }
 
-template <int SYNC>
-__global__ __launch_bounds__(kRsThreads, 1) void gemm_rs_kernel(RsArgs a) {
+template <int SYNC, int TILE>
+__global__ __launch_bounds__(64 * rs_waves<TILE>(), 1) void gemm_rs_kernel(RsArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
-  constexpr int BM = kRsTile, BN = kRsTile;
+  constexpr int BM = TILE, BN = TILE, NW = rs_waves<TILE>();
   const int tpb = a.tr * a.tc;
   const int64_t total = (int64_t)a.ranks * tpb;
   const int64_t J = (int64_t)(a.ranks - 1) * tpb;  // reduce jobs = peer tiles
@@ -215,8 +225,8 @@ __global__ __launch_bounds__(kRsThreads, 1) void gemm_rs_kernel(RsArgs a) {
     op.k = a.k;
     const int64_t m0 = (int64_t)trow * BM;
 
-    Acc<BM, BN, kRsWaves> acc;
-    gemm_tile<BM, BN, 64, 0, false, kRsWaves>(acc, op, m0, lds, [](int64_t, int64_t) {});
+    Acc<BM, BN, NW> acc;
+    gemm_tile<BM, BN, 64, 0, false, NW>(acc, op, m0, lds, [](int64_t, int64_t) {});
 
     // Partial and own tiles are stored with agent-scope stores (the sc1 bit:
     // complete at the device's point of coherence once drained), so their
@@ -229,17 +239,54 @@ __global__ __launch_bounds__(kRsThreads, 1) void gemm_rs_kernel(RsArgs a) {
       if (threadIdx.x == 0) __hip_atomic_store(f, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     if (blk != a.rank) {
-      acc_store<BM, BN, kAuxAgent, kRsWaves>(acc, a.peer_out[blk], a.n, m0, op.n0, a.bm, a.n);
+      acc_store<BM, BN, kAuxAgent, NW>(acc, a.peer_out[blk], a.n, m0, op.n0, a.bm, a.n);
       if (SYNC) publish(a.out_flags + ((int64_t)blk * tpb + t) * a.flag_stride);
-      reduce_job(a, pj, J, timed_out, lds);
+      reduce_job<TILE>(a, pj, J, timed_out, lds);
     } else {
-      acc_store<BM, BN, kAuxAgent, kRsWaves>(acc, a.out, a.n, m0, op.n0, a.bm, a.n);
+      acc_store<BM, BN, kAuxAgent, NW>(acc, a.out, a.n, m0, op.n0, a.bm, a.n);
       if (J > 0) publish(a.own_flags + t);
     }
   }
 }
 
-constexpr int rs_lds_bytes() { return TileCfg<kRsTile, kRsTile>::LDS_BYTES; }
+// LDS: the GEMM stages, which the reduction reuses as 16 KiB per wave.
+template <int TILE>
+constexpr int rs_lds_bytes() {
+  return std::max(TileCfg<TILE, TILE, 64, 0, rs_waves<TILE>()>::LDS_BYTES, rs_waves<TILE>() * 16384);
+}
+
+bool rs_tile_ok(const gemm_rs_desc* d) { return d->tile_m == d->tile_n && (d->tile_m == 256 || d->tile_m == 128); }
+
+template <int TILE>
+ovl_status rs_launch(const gemm_rs_desc* d, RsArgs& r, void* workspace, int64_t* out_flags, int64_t epoch,
+                     uint32_t mode, const DeviceInfo& di, hipStream_t stream) {
+  constexpr int threads = 64 * rs_waves<TILE>();
+  const int lds = rs_lds_bytes<TILE>();
+  ovl_status st = allow_lds(reinterpret_cast<const void*>(&gemm_rs_kernel<0, TILE>), lds);
+  if (st) return st;
+  st = allow_lds(reinterpret_cast<const void*>(&gemm_rs_kernel<1, TILE>), lds);
+  if (st) return st;
+  int occ = 0;
+  OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_rs_kernel<1, TILE>, threads, lds));
+  const int64_t total = (int64_t)d->ranks * r.tr * r.tc;
+  int64_t workers = std::min<int64_t>(total, (int64_t)std::max(occ, 1) * di.cus);
+  if (workers > kRsXcds) workers -= workers % kRsXcds;
+  r.workers = (int32_t)workers;
+  st = epoch_check(workspace, epoch);
+  if (st) return st;
+  if (d->ranks > 1 && mode == OVL_MODE_FUSED) {
+    st = epoch_accept(out_flags, epoch);
+    if (st) return st;
+  }
+  st = epoch_accept(workspace, epoch);
+  if (st) return st;
+  if (mode == OVL_MODE_FUSED)
+    hipLaunchKernelGGL((gemm_rs_kernel<1, TILE>), dim3(workers), dim3(threads), lds, stream, r);
+  else
+    hipLaunchKernelGGL((gemm_rs_kernel<0, TILE>), dim3(workers), dim3(threads), lds, stream, r);
+  OVL_HIP_TRY(hipGetLastError());
+  return OVL_OK;
+}
 
 }  // namespace
 
@@ -248,17 +295,18 @@ constexpr int rs_lds_bytes() { return TileCfg<kRsTile, kRsTile>::LDS_BYTES; }
 using namespace ovl;
 
 extern "C" size_t gemm_rs_flags_bytes(const gemm_rs_desc* d) {
-  if (!d || d->ranks < 1 || d->m < 1 || d->n < 1 || d->flag_stride < 8 || d->m % d->ranks) return 0;
+  if (!d || d->ranks < 1 || d->m < 1 || d->n < 1 || d->flag_stride < 8 || d->m % d->ranks || !rs_tile_ok(d))
+    return 0;
   const int64_t bm = d->m / d->ranks;
-  const int64_t tpb = ceil_div(bm, kRsTile) * ceil_div(d->n, kRsTile);
+  const int64_t tpb = ceil_div(bm, d->tile_m) * ceil_div(d->n, d->tile_n);
   return (size_t)(d->ranks * tpb * d->flag_stride);
 }
 
 // Error record, then one int64 flag per own tile.
 extern "C" size_t gemm_rs_workspace_bytes(const gemm_rs_desc* d) {
-  if (!d || d->ranks < 1 || d->m < 1 || d->n < 1 || d->m % d->ranks) return 0;
+  if (!d || d->ranks < 1 || d->m < 1 || d->n < 1 || d->m % d->ranks || !rs_tile_ok(d)) return 0;
   const int64_t bm = d->m / d->ranks;
-  const int64_t tpb = ceil_div(bm, kRsTile) * ceil_div(d->n, kRsTile);
+  const int64_t tpb = ceil_div(bm, d->tile_m) * ceil_div(d->n, d->tile_n);
   return OVL_ERROR_RECORD_BYTES + 8 * (size_t)tpb;
 }
 
@@ -269,7 +317,7 @@ extern "C" ovl_status gemm_rs_run(const gemm_rs_desc* d, const void* a, const vo
   if (!d || !a || !b || !out || !workspace) return OVL_EINVAL;
   if (d->ranks < 1 || d->rank < 0 || d->rank >= d->ranks) return OVL_EINVAL;
   if (d->ranks > kRsMaxRanks) return OVL_EUNSUPPORTED;
-  if (d->tile_m != kRsTile || d->tile_n != kRsTile) return OVL_EUNSUPPORTED;
+  if (!rs_tile_ok(d)) return OVL_EUNSUPPORTED;
   if (d->m < 1 || d->n < 8 || d->k < 8 || d->m % d->ranks) return OVL_ESHAPE;
   if (d->n % 8 || d->k % 8 || d->flag_stride < 8 || d->flag_stride % 8) return OVL_EALIGN;
   // Every operand below 1 GiB and rows below 2^20 elements: buffer offsets stay in 32 bits.
@@ -315,35 +363,9 @@ extern "C" ovl_status gemm_rs_run(const gemm_rs_desc* d, const void* a, const vo
   r.spin_limit = spin_limit_of(opts);
   r.ranks = d->ranks;
   r.rank = d->rank;
-  r.tr = (int32_t)ceil_div(r.bm, kRsTile);
-  r.tc = (int32_t)ceil_div(d->n, kRsTile);
+  r.tr = (int32_t)ceil_div(r.bm, d->tile_m);
+  r.tc = (int32_t)ceil_div(d->n, d->tile_n);
   r.sync = mode == OVL_MODE_FUSED;
-
-  const int lds = rs_lds_bytes();
-  const void* fn = (mode == OVL_MODE_FUSED) ? reinterpret_cast<const void*>(&gemm_rs_kernel<1>)
-                                            : reinterpret_cast<const void*>(&gemm_rs_kernel<0>);
-  st = allow_lds(fn, lds);
-  if (st) return st;
-  st = allow_lds(reinterpret_cast<const void*>(&gemm_rs_kernel<1>), lds);
-  if (st) return st;
-  int occ = 0;
-  OVL_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_rs_kernel<1>, kRsThreads, lds));
-  const int64_t total = (int64_t)d->ranks * r.tr * r.tc;
-  int64_t workers = std::min<int64_t>(total, (int64_t)std::max(occ, 1) * di.cus);
-  if (workers > kRsXcds) workers -= workers % kRsXcds;
-  r.workers = (int32_t)workers;
-  st = epoch_check(workspace, epoch);
-  if (st) return st;
-  if (d->ranks > 1 && mode == OVL_MODE_FUSED) {
-    st = epoch_accept(out_flags, epoch);
-    if (st) return st;
-  }
-  st = epoch_accept(workspace, epoch);
-  if (st) return st;
-  if (mode == OVL_MODE_FUSED)
-    hipLaunchKernelGGL(gemm_rs_kernel<1>, dim3(workers), dim3(kRsThreads), lds, stream, r);
-  else
-    hipLaunchKernelGGL(gemm_rs_kernel<0>, dim3(workers), dim3(kRsThreads), lds, stream, r);
-  OVL_HIP_TRY(hipGetLastError());
-  return OVL_OK;
+  return d->tile_m == 256 ? rs_launch<256>(d, r, workspace, out_flags, epoch, mode, di, stream)
+                          : rs_launch<128>(d, r, workspace, out_flags, epoch, mode, di, stream);
 }

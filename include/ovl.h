@@ -271,8 +271,8 @@ typedef struct gemm_rs_desc {
   int32_t ranks;        /* R, 1..16; m must be a multiple of R */
   int32_t rank;
   int64_t m, n, k;      /* n, k multiples of 8 */
-  int32_t tile_m;       /* flag tile: must be 256 */
-  int32_t tile_n;       /* flag tile: must be 256 */
+  int32_t tile_m;       /* output and flag tile: 256 x 256 (eight-wave workgroups) or */
+  int32_t tile_n;       /* 128 x 128 (four-wave); tile_m == tile_n */
   int32_t flag_stride;  /* bytes, multiple of 8, >= 8 */
 } gemm_rs_desc;
 
@@ -296,8 +296,10 @@ size_t gemm_rs_workspace_bytes(const gemm_rs_desc* desc);
  * accumulator, so out = acc + ((P_a + P_b) + ...).
  * Modes: FUSED, or GEMM_ONLY (same work and result, without in/out flag
  * traffic).
- * Errors as for ag_gemm_run; EUNSUPPORTED if tile_m/tile_n are not 256, if
- * m, n or k exceeds 2^20, or if A, B or the local product exceeds 1 GiB. */
+ * Errors as for ag_gemm_run; EUNSUPPORTED if tile_m x tile_n is not 256 x 256
+ * or 128 x 128 (the size queries then return 0), if m, n or k exceeds 2^20,
+ * or if A, B or the local product exceeds 1 GiB.  At 8192 x 4096 x 1792 over
+ * 8 ranks the 256-tile runs in about 150 us and the 128-tile in about 205. */
 ovl_status gemm_rs_run(const gemm_rs_desc* desc, const void* a, const void* b,
                        float* const* peer_out, const float* const* peer_in, float* out,
                        int64_t* out_flags, const int64_t* in_flags, void* workspace,

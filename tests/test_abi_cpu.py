@@ -179,14 +179,26 @@ def test_run_argument_errors_come_before_any_device_work():
     assert st == o.OVL_EALIGN
 
 
-@pytest.mark.parametrize("tile", [(128, 128), (128, 256), (256, 128), (512, 256), (0, 256)])
+@pytest.mark.parametrize("tile", [(128, 256), (256, 128), (512, 512), (64, 64), (0, 256), (0, 0)])
 def test_gemm_rs_refuses_tiles_it_does_not_implement(tile):
-    """gemm_rs_run implements 256 x 256 tiles only; every other pair is
-    refused with OVL_EUNSUPPORTED before any device work."""
+    """gemm_rs_run implements 256 x 256 and 128 x 128 tiles; every other pair
+    is refused with OVL_EUNSUPPORTED before any device work, and the size
+    queries return 0 for it."""
     o = ovl()
     desc = o.gemm_rs_desc(8, 0, 8192, 4096, 1792, tile_m=tile[0], tile_n=tile[1])
     st = o.gemm_rs_run(desc, 16, 16, [16] * 8, [16] * 8, 16, 16, 16, 16, 1, raise_on_error=False, stream=0)
     assert st == o.OVL_EUNSUPPORTED
+    assert o.gemm_rs_flags_bytes(desc) == 0 and o.gemm_rs_workspace_bytes(desc) == 0
+
+
+def test_gemm_rs_tile_sizes():
+    """Flag and workspace sizes follow the tile: one flag per tile of each
+    block (8192 x 4096 over 8 ranks: 4 x 16 tiles of 256, 8 x 32 of 128)."""
+    o = ovl()
+    for tile, tpb in ((256, 64), (128, 256)):
+        d = o.gemm_rs_desc(8, 0, 8192, 4096, 1792, tile, tile)
+        assert o.gemm_rs_flags_bytes(d) == 8 * tpb * 8
+        assert o.gemm_rs_workspace_bytes(d) == o.ERROR_RECORD_BYTES + 8 * tpb
 
 
 @pytest.mark.parametrize("f8,tile,ok", [

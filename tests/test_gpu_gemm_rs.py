@@ -16,13 +16,16 @@ def ovl():
     return _o
 
 
+TILES = (256, 128)  # the implemented tiles (tile_m = tile_n)
+
+
 class RsCase:
-    def __init__(self, cfg, kind="normal"):
+    def __init__(self, cfg, kind="normal", tile=256):
         o = ovl()
         self.cfg = cfg
         self.a, self.b, self.parts = synth.rs_inputs(cfg, kind)
         R, bm = cfg.ranks, cfg.block_m
-        self.desc = o.gemm_rs_desc(R, cfg.rank, cfg.m, cfg.n, cfg.k, 256, 256, 8)
+        self.desc = o.gemm_rs_desc(R, cfg.rank, cfg.m, cfg.n, cfg.k, tile, tile, 8)
         self.fbytes = o.gemm_rs_flags_bytes(self.desc)
         self.tpb = self.fbytes // 8 // R
         self.d_a, self.d_b = dev(self.a), dev(self.b)
@@ -48,7 +51,7 @@ class RsCase:
 
     def run(self, epoch, mode=0, spin_limit=0):
         o = ovl()
-        say(f"  gemm_rs_run {self.cfg.name} epoch={epoch} mode={mode}")
+        say(f"  gemm_rs_run {self.cfg.name} tile={self.desc.tile_m} epoch={epoch} mode={mode}")
         o.gemm_rs_run(self.desc, self.d_a, self.d_b, self.peer_out, self.peer_in, self.out, self.out_flags,
                       self.in_flags, self.ws, epoch, mode=mode, spin_limit=spin_limit)
         return o.ovl_check(self.ws, raise_on_error=False)
@@ -58,9 +61,10 @@ def _small(R=4, rank=1, bm=300, n=264, k=200, seed=9):
     return synth.GemmRsCfg("rs_small", R, R * bm, k, n, 256, 256, 1.0, 0.25, 1.0, seed, rank)
 
 
-def test_small_ragged_matches_oracle():
+@pytest.mark.parametrize("tile", TILES)
+def test_small_ragged_matches_oracle(tile):
     cfg = _small()
-    case = RsCase(cfg)
+    case = RsCase(cfg, tile=tile)
     case.set_in_flags(1)
     case.poison()
     st, det = case.run(1)
@@ -75,9 +79,10 @@ def test_small_ragged_matches_oracle():
     assert np.array_equal(fl, oracle.rs_expected_flags(cfg.ranks, cfg.rank, case.tpb, 8, 1))
 
 
-def test_small_integers_bit_exact():
+@pytest.mark.parametrize("tile", TILES)
+def test_small_integers_bit_exact(tile):
     cfg = _small(R=8, rank=0, bm=256, n=512, k=320)
-    case = RsCase(cfg, "smallint")
+    case = RsCase(cfg, "smallint", tile=tile)
     case.set_in_flags(1)
     assert case.run(1)[0] == 0
     loc, outb, own = oracle.gemm_rs(case.a, case.b, case.parts, cfg.rank, cfg.ranks)
@@ -86,19 +91,21 @@ def test_small_integers_bit_exact():
         assert np.array_equal(host(case.peer_out[p]), outb[p].astype(np.float32))
 
 
-def test_single_rank_is_plain_gemm():
+@pytest.mark.parametrize("tile", TILES)
+def test_single_rank_is_plain_gemm(tile):
     cfg = _small(R=1, rank=0, bm=520, n=136, k=64)
-    case = RsCase(cfg)
+    case = RsCase(cfg, tile=tile)
     st, det = case.run(1)
     assert st == 0, det
     ref = oracle.gemm(case.a, case.b)
     assert max_err(host(case.out), ref) <= gemm_tol(cfg.k, float(np.abs(ref).max()))
 
 
-def test_withheld_partial_times_out():
+@pytest.mark.parametrize("tile", TILES)
+def test_withheld_partial_times_out(tile):
     o = ovl()
     cfg = _small()
-    case = RsCase(cfg)
+    case = RsCase(cfg, tile=tile)
     case.set_in_flags(1)
     v = case.in_flags.view(dtype=__import__("torch").int64).view(cfg.ranks, case.tpb)
     v[3, 2] = 0  # peer 3 never sent tile 2 of this rank's block
@@ -132,13 +139,14 @@ def _check_all(case, exact=False):
     assert np.array_equal(fl, oracle.rs_expected_flags(cfg.ranks, cfg.rank, case.tpb, 8, case.last_epoch))
 
 
-@pytest.mark.parametrize("kind", ["normal", "smallint"])
-def test_full_size(kind):
-    """8192 x 4096 x 1792 over 8 ranks in the bench's launch configuration:
-    the own block and all 7 outbound partials compared in full (bit for bit
-    with small integers), flags exact, and GEMM_ONLY gives the same bits."""
+@pytest.mark.parametrize("kind,tile", [("normal", 256), ("smallint", 256), ("normal", 128), ("smallint", 128)])
+def test_full_size(kind, tile):
+    """8192 x 4096 x 1792 over 8 ranks in the bench's launch configuration
+    (256 x 256 tiles) and with 128 x 128 tiles: the own block and all 7
+    outbound partials compared in full (bit for bit with small integers),
+    flags exact, and GEMM_ONLY gives the same bits."""
     cfg = synth.CONFIGS["rs_r8_8192x4096x1792"]
-    case = RsCase(cfg, kind)
+    case = RsCase(cfg, kind, tile=tile)
     case.set_in_flags(1)
     case.poison()
     st, det = case.run(1)
