@@ -323,6 +323,13 @@ __device__ inline void copy_rows(const A2aArgs& a, int s, int r0, int r1) {
   const int pairs = units > wave ? (units - wave + 2 * W - 1) / (2 * W) : 0;
   const int steps = pairs * passes;
   u32x4 cur[2][V], nxt[2][V];
+  // Buffer loads and stores with no branch around them: a vector that does
+  // not exist gets an offset past its buffer (the load returns zeros, the
+  // store is dropped).  Guarded per vector, the compiler lost count of the
+  // loads in flight and waited for all of them before every store.
+  const rsrc_t rsrc = make_rsrc(src, a.tokens * a.row_bytes);
+  const rsrc_t rdst = make_rsrc(dst, a.cap * a.row_bytes);
+  const uint32_t rb = (uint32_t)a.row_bytes;
   auto load = [&](int st, u32x4 (&v)[2][V]) {
     const int u = wave + (st / passes) * 2 * W, c0 = (st % passes) * 64 * V;
     // every vector's source token first (all lanes read the same entries),
@@ -340,8 +347,8 @@ __device__ inline void copy_rows(const A2aArgs& a, int s, int r0, int r1) {
 #pragma unroll
       for (int q = 0; q < V; ++q) {
         const int c = multi ? ((q & ((1 << lg_qpr) - 1)) << 6) + lane : c0 + q * 64 + lane;
-        if (tok[h][q] < 0 || c >= vpr) continue;
-        v[h][q] = ld16_nt(src + (int64_t)tok[h][q] * a.row_bytes + c * 16);
+        const uint32_t off = (tok[h][q] >= 0 && c < vpr) ? (uint32_t)tok[h][q] * rb + (uint32_t)c * 16 : kOOB;
+        v[h][q] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 0);
       }
     }
   };
@@ -353,11 +360,25 @@ __device__ inline void copy_rows(const A2aArgs& a, int s, int r0, int r1) {
       for (int q = 0; q < V; ++q) {
         const int rr = r0 + (u + W * h) * rps + (multi ? q >> lg_qpr : 0);
         const int c = multi ? ((q & ((1 << lg_qpr) - 1)) << 6) + lane : c0 + q * 64 + lane;
-        if (rr >= r1 || c >= vpr) continue;
-        st16(dst + (int64_t)rr * a.row_bytes + c * 16, v[h][q]);
-        // FP8: the row's scale travels with it (from the lane holding its first vector)
-        if (xs && c == 0) a.recv_scale[(int64_t)s * a.cap + rr] = xs[srow[rr]];
+        const uint32_t off = (rr < r1 && c < vpr) ? (uint32_t)rr * rb + (uint32_t)c * 16 : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b128(v[h][q], rdst, (int)off, 0, 0);
       }
+    }
+    // FP8: each row's scale travels with it, read with scalar loads after
+    // the data stores: a vector load here would make every later store
+    // wait for all the loads in flight (vector memory counters complete in
+    // order).
+    if (xs) {
+      typedef const __attribute__((address_space(4))) int32_t* ctok_t;
+      typedef const __attribute__((address_space(4))) float* cscale_t;
+      const ctok_t ctok = (ctok_t)srow;
+      const cscale_t cxs = (cscale_t)xs;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        for (int k = 0; k < rps; ++k) {
+          const int rr = uniform(r0 + (u + W * h) * rps + k);
+          if (rr < r1 && lane == 0) a.recv_scale[(int64_t)s * a.cap + rr] = cxs[ctok[rr]];
+        }
     }
   };
   if (steps > 0) load(0, cur);
