@@ -107,12 +107,16 @@ namespace ovl {
 // division per vector.  The loads of block i+1 are issued before the stores
 // of block i, so that a lane always has a block in flight (vector memory
 // counters complete in order: waiting for the loads does not wait for the
-// stores issued after them).
+// stores issued after them).  Loads and stores are buffer operations with
+// no branch around them (a vector past the end gets an offset past the
+// buffer: the load returns zeros, the store is dropped): guarded one by one,
+// they made the compiler wait for every load in flight before each store.
 template <int NT, bool AGENT = false>
 __device__ inline void copy_block(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int64_t rows,
                                   int64_t cols, int64_t ld) {
   constexpr int U = 8;
-  const rsrc_t dr = make_rsrc(dst, rows * ld * 2);  // AGENT: the stores go through a buffer resource
+  const rsrc_t sr = make_rsrc(src, rows * ld * 2);
+  const rsrc_t dr = make_rsrc(dst, rows * ld * 2);
   const uint32_t vpr = (uint32_t)(cols / 8);
   const uint32_t total = (uint32_t)(rows * vpr);
   const uint32_t step_r = NT / vpr, step_c = NT % vpr;
@@ -120,14 +124,14 @@ __device__ inline void copy_block(const uint16_t* __restrict__ src, uint16_t* __
   const uint32_t blocks = (total + NT * U - 1) / (NT * U);
   struct Blk {
     u32x4 v[U];
-    uint32_t off[U];  // element offset, or ~0u past the end
+    uint32_t off[U];  // byte offset, or kOOB past the end
   };
   auto load = [&](uint32_t bi, Blk& b) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const bool in = bi * NT * U + j * NT + threadIdx.x < total;
-      b.off[j] = in ? r * (uint32_t)ld + c * 8 : ~0u;
-      if (in) b.v[j] = ld16_nt(src + b.off[j]);
+      b.off[j] = in ? (r * (uint32_t)ld + c * 8) * 2 : kOOB;
+      b.v[j] = __builtin_amdgcn_raw_buffer_load_b128(sr, (int)b.off[j], 0, 0);
       c += step_c;
       r += step_r;
       if (c >= vpr) {
@@ -139,12 +143,7 @@ __device__ inline void copy_block(const uint16_t* __restrict__ src, uint16_t* __
   auto store = [&](const Blk& b) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
-      if (b.off[j] != ~0u) {
-        if constexpr (AGENT)
-          __builtin_amdgcn_raw_buffer_store_b128(b.v[j], dr, (int)(b.off[j] * 2), 0, kAuxAgent);
-        else
-          st16(dst + b.off[j], b.v[j]);
-      }
+      __builtin_amdgcn_raw_buffer_store_b128(b.v[j], dr, (int)b.off[j], 0, AGENT ? kAuxAgent : 0);
   };
   Blk x, y;
   if (blocks > 0) load(0, x);
