@@ -159,7 +159,9 @@ extern "C" ovl_status ovl_copy(void* dst, const void* src, size_t bytes, int32_t
   ovl_status st = current_device_info(&di);
   if (st) return st;
   const size_t vecs = bytes / 16;
-  if (!blocks) blocks = (int32_t)std::min<size_t>((size_t)di.cus * 8, (vecs + 255) / 256);
+  // Default: one four-wave workgroup per compute unit (256 MiB at 256
+  // workgroups: 77 us, 7.0 TB/s read + written; 512: 84 us; 2048: 107 us).
+  if (!blocks) blocks = (int32_t)std::min<size_t>((size_t)di.cus, (vecs + 255) / 256);
   hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(256), 0, stream, (u32x4*)dst, (const u32x4*)src, vecs);
   OVL_HIP_TRY(hipGetLastError());
   return OVL_OK;

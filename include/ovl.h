@@ -529,7 +529,8 @@ ovl_status ovl_check(const void* workspace, int64_t* detail, hipStream_t stream)
 const char* ovl_strerror(ovl_status status);
 
 /* Plain 16-byte-vector copy of `bytes` bytes (a multiple of 16) from src to
- * dst, with `blocks` workgroups (0 = default).  A reference point for the
+ * dst, with `blocks` workgroups of 256 threads (0 = one per compute unit,
+ * the fastest count measured).  A reference point for the
  * HBM roofline and for scaling hardware byte counters. */
 ovl_status ovl_copy(void* dst, const void* src, size_t bytes, int32_t blocks, hipStream_t stream);
 
