@@ -703,6 +703,9 @@ __global__ __launch_bounds__(64 * a2a_waves(F8), 1) void a2a_fused_kernel(A2aArg
       int pend_pos = 0, pend_n = 0;
       for (int ch; (ch = take_chunk(a, total, &sh)) < total;) a2a_copy_chunk_deferred(a, g, ch, &pend_pos, &pend_n);
       if (pend_n) a2a_arrive(a, g, pend_pos, pend_n);
+      // No copy load may stay pending into the GEMM below: the compiler would
+      // otherwise wait for them at the top of every K-step.
+      wave_drain();
       if (a.trace && threadIdx.x == 0 && blockIdx.x < kA2aTraceProducers) a.trace[a.ranks + blockIdx.x] = now_ticks();
       // The copy is handed out: take tiles of the shared tail.
       a2a_consume<true, F8>(a, g, -1, lds, a2a_static_rounds(a, g, F8));

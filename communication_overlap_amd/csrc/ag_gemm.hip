@@ -586,6 +586,14 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
     // up to the first missing unit are there.
     int ready = (int)(k_lo / a.batch_cols) - 1;
     const int last = (int)((k_hi - 1) / a.batch_cols);
+    // covered: the columns of the item's K range (from k_lo) up to which this
+    // wave checks no flag.  For wave 0 of a fused item that reads the gathered
+    // operand, what the acquired batches cover (grown as batches are
+    // acquired); for every other wave and item, all of them.  Wave-uniform,
+    // so a step costs one scalar compare.  (A 64-bit division per step to
+    // find its batch took a few hundred instructions of wave 0 per K-step.)
+    const bool polls_flags = MODE == kModeFused && !own && uniform((int)threadIdx.x) < 64;
+    int covered = polls_flags ? (int)((int64_t)(ready + 1) * a.batch_cols - k_lo) : INT32_MAX;
     // The (shard, row panel) pairs that cover the tile's rows are consecutive
     // in unit numbering (unit = (shard * panels + panel) * batches + batch):
     // panel ids sp_lo .. sp_lo + npan - 1.  Computed once per item, so that a
@@ -598,44 +606,51 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
     const int64_t c_item = a.trace ? now_cycles() : 0;
     int64_t waited = 0;  // ticks wave 0 spent polling for this item (traced runs)
     auto before_step = [&](int64_t, int64_t k1) {
-      if (MODE != kModeFused || own || timed_out) return;
-      if (threadIdx.x >= 64) return;  // wave 0 waits for the workgroup (see gemm_tile)
-      const int need = (int)((k_lo + k1 - 1) / a.batch_cols);
-      if (need <= ready) return;
+      if (MODE != kModeFused || (int)k1 <= covered) return;  // wave 0 waits for the workgroup (see gemm_tile)
+      const int need = (int)((k_lo + k1 - 1) / a.batch_cols);  // > ready
       const int64_t t_wait = a.trace ? now_ticks() : 0;
       const int lane = lane_id();
       for (uint64_t polls = 0;; ++polls) {
         // One round trip reads the units of every remaining batch (numbered
         // batch-major: i -> batch ready + 1 + i / npan, panel i % npan),
-        // lanes in parallel; bad = first batch with a unit not there yet.
-        int bad = last + 1;
+        // lanes in parallel; miss = the first i whose unit is not there yet,
+        // seen holding the flag value it read.
+        int miss = INT32_MAX;
+        int64_t seen = 0;
         const int cnt = npan * (last - ready);
         for (int i = lane; i < cnt; i += 64) {
           const int bt = ready + 1 + i / npan;
           const int64_t u = (int64_t)(sp_lo + i % npan) * a.batches + bt;
           const int64_t v = __hip_atomic_load(a.flags + u * a.flag_stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (v < a.epoch) bad = min(bad, bt);
+          if (v < a.epoch && i < miss) {
+            miss = i;
+            seen = v;
+          }
           check_epoch(a.err, kSiteAgUnit, u, v, a.epoch);
         }
-        for (int d = 1; d < 64; d <<= 1) bad = min(bad, __shfl_xor(bad, d, 64));
-        bad = uniform(bad);
+        int first = miss;
+        for (int d = 1; d < 64; d <<= 1) first = min(first, __shfl_xor(first, d, 64));
+        first = uniform(first);
+        const int bad = first == INT32_MAX ? last + 1 : ready + 1 + first / npan;  // first batch not complete
         if (bad > need) {
           ready = bad - 1;
           break;
         }
         if (polls >= a.spin_limit) {
-          // Name the first missing unit in the error record.
-          for (int bt = ready + 1; bt <= need && !timed_out; ++bt)
-            for (int j = 0; j < npan && !timed_out; ++j) {
-              const int64_t u = (int64_t)(sp_lo + j) * a.batches + bt;
-              if (!wave_poll(a.flags + u * a.flag_stride, a.epoch, 0, a.err, kSiteAgUnit, u)) timed_out = true;
-            }
+          // Name the first missing unit in the error record: the lane that
+          // read it reports, with no further load (polls or error reports in
+          // a loop here made the compiler wait for every load in flight at
+          // the top of each K-step).
+          if (miss == first)
+            report_error(a.err, OVL_ETIMEOUT, kSiteAgUnit,
+                         (int64_t)(sp_lo + first % npan) * a.batches + ready + 1 + first / npan, seen, a.epoch);
           timed_out = true;
           break;
         }
         __builtin_amdgcn_s_sleep(2);
       }
       wave_acquire();  // one acquire for all the units seen
+      covered = uniform(timed_out ? INT32_MAX : (int)((int64_t)(ready + 1) * a.batch_cols - k_lo));
       if (a.trace) waited += now_ticks() - t_wait;
     };
     // Thread 0 (in wave 0, which holds `waited`) records the item.
@@ -665,11 +680,17 @@ __device__ void consume(const AgArgs& a, int cidx, const int* sorted, uint16_t* 
     // epilogue at all).
     acc_store<BM, BN, kAuxAgent, NW>(acc, a.partial + (int64_t)sp * a.m * a.n, a.n, m0, n0, a.m, a.n);
     int64_t* cnt = a.counters + 2 * tl;
-    const int64_t before = wg_arrive_agent(cnt);
+    // The count before the add (thread 0's, in every lane of wave 0) is used
+    // on both paths below: an atomic whose returned value stays pending into
+    // the next item makes the compiler wait for every load in flight at the
+    // top of each K-step.
+    const int64_t before = uniform64(wg_arrive_agent(cnt));
     if (a.split_sync) {
-      // Wait for the tile's other ranges, then sum stripe sp of its rows.
+      // Wait for the tile's other ranges (the last to arrive has seen them
+      // all), then sum stripe sp of its rows.
       if (threadIdx.x < 64 && !timed_out) {
-        if (!wave_poll(cnt, a.splits, a.spin_limit, a.err, kSiteAgSplit, tl)) timed_out = true;
+        if (before + 1 < a.splits && !wave_poll(cnt, a.splits, a.spin_limit, a.err, kSiteAgSplit, tl))
+          timed_out = true;
         wave_acquire();
       }
       __syncthreads();

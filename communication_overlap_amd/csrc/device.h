@@ -65,6 +65,12 @@ __device__ inline void check_epoch(ErrRec* e, int32_t site, int64_t index, int64
 // in fact: a loop whose exit it takes for divergent may be restructured so
 // that lanes leave it separately, splitting one barrier into several.
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// The same for a 64-bit value.
+__device__ inline int64_t uniform64(int64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // Work item of consumer (x, q) (die x, index q on its die) in round w of a
 // persistent deal over `groups` dies of `per` consumers: a whole round gives
@@ -119,7 +125,14 @@ __device__ inline bool wave_wait(const int64_t* flag, int64_t epoch, uint64_t sp
 
 // Waits until this wave's outstanding memory operations have completed
 // (stores included: they have reached the L2 of this die).
-__device__ inline void wave_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ inline void wave_drain() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // The same wait as a builtin, which the compiler's own wait insertion
+  // reads (it does not read inline asm): it then knows no load is pending
+  // here, and adds no wait for one later, e.g. at the top of every K-step of
+  // a GEMM that follows a copy.  vmcnt(0), expcnt(7), lgkmcnt(15).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
 
 // Workgroup-level publish: every thread calls this after its own stores of
 // the unit.  Each wave drains its stores, the workgroup barrier orders all of

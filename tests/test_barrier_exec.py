@@ -22,6 +22,7 @@ import shutil
 import pytest
 
 from tests import exec_check as ec
+from tests import kloop_check as kc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "communication_overlap_amd", "csrc")
@@ -45,21 +46,70 @@ def _flags():
 
 
 def _compile_and_check(src):
-    bad, n, _ = ec.check_asm(ec.device_asm(HIPCC, src, _flags()))
-    return os.path.basename(src), bad, n
+    asm = ec.device_asm(HIPCC, src, _flags())
+    bad, n, _ = ec.check_asm(asm)
+    waits, loops = kc.kloop_waits(asm)
+    return os.path.basename(src), bad, n, waits, loops
 
 
-def test_every_library_barrier_runs_with_full_exec():
+@pytest.fixture(scope="module")
+def library_checks():
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ProcessPoolExecutor(min(8, len(srcs))) as ex:
-        results = list(ex.map(_compile_and_check, srcs))
+        return list(ex.map(_compile_and_check, srcs))
+
+
+def test_every_library_barrier_runs_with_full_exec(library_checks):
     report = [f"{name}: {fn}: asm lines {[ln for ln, _ in sites]}"
-              for name, bad, _ in results for fn, sites in bad.items()]
+              for name, bad, _, _, _ in library_checks for fn, sites in bad.items()]
     assert not report, "barriers under a partial EXEC:\n" + "\n".join(report)
     # The kernels that synchronise workgroups were all seen.
-    seen = {name: n for name, _, n in results}
+    seen = {name: n for name, _, n, _, _ in library_checks}
     for name in ("ag_gemm.hip", "a2a.hip", "gemm_rs.hip", "combine.hip", "ring.hip"):
         assert seen[name] > 0, name
+
+
+def test_no_compiler_wait_ahead_of_a_k_step(library_checks):
+    """No GEMM K-loop of the library starts a step with a vector-memory wait
+    of the compiler's (kloop_check.py says why that loses the prefetch)."""
+    report = [f"{name}: {fn}: loop at asm line {ln}: {w}"
+              for name, _, _, waits, _ in library_checks for fn, sites in waits.items() for ln, w in sites]
+    assert not report, "\n".join(report)
+    loops = {name: n for name, _, _, _, n in library_checks}
+    # every kernel instantiation's tile loop was found
+    for name, least in (("ag_gemm.hip", 9), ("a2a.hip", 8), ("gemm_rs.hip", 4)):
+        assert loops[name] >= least, (name, loops[name])
+
+
+_LOOPS = """
+    .type k,@function
+k:
+    s_mov_b32 s0, 0
+.LBB0_1:
+    ds_read_b128 v[0:3], v8
+    s_waitcnt vmcnt(%s)
+    ds_read_b128 v[4:7], v8 offset:16
+    v_mfma_f32_32x32x16_bf16 a[0:15], v[0:3], v[4:7], a[0:15]
+    s_waitcnt vmcnt(2)
+    s_barrier
+    s_cbranch_scc1 .LBB0_1
+.LBB0_2:
+    s_waitcnt vmcnt(0)
+    v_mfma_f32_32x32x16_bf16 a[0:15], v[0:3], v[4:7], a[0:15]
+    s_cbranch_scc0 .LBB0_2
+    s_endpgm
+.Lfunc_end0:
+"""
+
+
+def test_kloop_check_reports_a_wait_ahead_of_the_first_mfma():
+    bad, n = kc.kloop_waits(_LOOPS % "5")
+    assert n == 2
+    assert [w for _, w in bad["k"]] == [["vmcnt(5)"], ["vmcnt(0)"]]
+    # A wait after the step's first MFMA (the step-end wait) is not reported.
+    ok = (_LOOPS % "5").replace("    s_waitcnt vmcnt(5)\n", "")
+    ok = ok.replace(".LBB0_2:\n    s_waitcnt vmcnt(0)\n", ".LBB0_2:\n")
+    assert kc.kloop_waits(ok) == ({}, 2)
 
 
 SYNTHETIC = r"""
