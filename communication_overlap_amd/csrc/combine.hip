@@ -19,11 +19,14 @@
 #include <algorithm>
 
 #include "device.h"
+#include "gemm_core.h"
 #include "host.h"
 
 namespace ovl {
 
 namespace {
+
+constexpr int kCbLoadAux = 2;  // the put reads each row once: nontemporal loads (the nt bit)
 
 constexpr int kCbMaxRanks = 16;
 constexpr int kCbBlocksPerCu = 2;
@@ -144,23 +147,28 @@ __device__ void cb_geometry(const CombineArgs& a, CbGeom* g) {
 
 // Reverse put of slice s: its rows of y[s] are contiguous, as are their
 // places in ret_out[s].  Every workgroup copies a grid-strided share of the
-// slice's 8-byte words, eight in flight per lane, with agent-scope stores,
-// and then arrives; the last of them to arrive sets out_flags[s].
+// slice's 16-byte vectors, eight in flight per lane, as buffer loads and
+// agent-scope buffer stores with no branch around them (a vector past the
+// end gets an offset past its buffer: the load returns zeros, the store is
+// dropped), and then arrives; the last of them to arrive sets out_flags[s].
 __device__ void cb_put_slice(const CombineArgs& a, int s, int64_t rows) {
-  const int64_t words = rows * a.n / 2;
-  const uint64_t* src = reinterpret_cast<const uint64_t*>(a.y + (int64_t)s * a.cap * a.n);
-  uint64_t* dst = reinterpret_cast<uint64_t*>(a.ret_out[s]);
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t vecs = (uint32_t)(rows * a.n / 4);  // the host keeps y under 1 GiB
+  const rsrc_t rs = make_rsrc(a.y + (int64_t)s * a.cap * a.n, (int64_t)vecs * 16);
+  const rsrc_t rd = make_rsrc(a.ret_out[s], (int64_t)vecs * 16);
+  const uint32_t stride = gridDim.x * kThreads;
   constexpr int U = 8;
-  for (; i + (U - 1) * stride < words; i += U * stride) {
-    uint64_t v[U];
+  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < vecs; i += U * stride) {
+    u32x4 v[U];
+    uint32_t off[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < U; ++u) {
+      const uint32_t k = i + u * stride;
+      off[u] = k < vecs ? k * 16 : kOOB;
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off[u], 0, kCbLoadAux);
+    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) st8_agent(dst + i + u * stride, v[u]);
+    for (int u = 0; u < U; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, (int)off[u], 0, kAuxAgent);
   }
-  for (; i < words; i += stride) st8_agent(dst + i, __builtin_nontemporal_load(src + i));
   const int64_t old = wg_arrive_agent(a.counters + s);
   if (threadIdx.x == 0 && old + 1 == (int64_t)gridDim.x) {
     wave_acquire();
