@@ -145,36 +145,61 @@ __device__ void cb_geometry(const CombineArgs& a, CbGeom* g) {
   __syncthreads();
 }
 
+// This workgroup's arrival for slice s, once every wave's stores of it are
+// complete: the last workgroup to arrive sets out_flags[s].
+__device__ void cb_arrive(const CombineArgs& a, int s) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int64_t old = __hip_atomic_fetch_add(a.counters + s, (int64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == (int64_t)gridDim.x) {
+      wave_acquire();
+      __hip_atomic_store(a.out_flags + (int64_t)s * a.flag_stride, a.epoch, __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();  // separates this thread-0 branch from the next one
+}
+
 // Reverse put of slice s: its rows of y[s] are contiguous, as are their
 // places in ret_out[s].  Every workgroup copies a grid-strided share of the
 // slice's 16-byte vectors, eight in flight per lane, as buffer loads and
 // agent-scope buffer stores with no branch around them (a vector past the
 // end gets an offset past its buffer: the load returns zeros, the store is
-// dropped), and then arrives; the last of them to arrive sets out_flags[s].
-__device__ void cb_put_slice(const CombineArgs& a, int s, int64_t rows) {
+// dropped).  The arrival for the previous slice `prev` (or -1) waits behind
+// this slice's first loads: the vector memory counter completes in order, so
+// once no more than those eight remain, the previous slice's stores are
+// complete, and the drain before an arrival no longer empties the pipeline.
+__device__ void cb_put_slice(const CombineArgs& a, int s, int64_t rows, int prev) {
+  constexpr int U = 8;  // 16 measured the same
   const uint32_t vecs = (uint32_t)(rows * a.n / 4);  // the host keeps y under 1 GiB
   const rsrc_t rs = make_rsrc(a.y + (int64_t)s * a.cap * a.n, (int64_t)vecs * 16);
   const rsrc_t rd = make_rsrc(a.ret_out[s], (int64_t)vecs * 16);
   const uint32_t stride = gridDim.x * kThreads;
-  constexpr int U = 8;
-  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < vecs; i += U * stride) {
-    u32x4 v[U];
-    uint32_t off[U];
+  u32x4 v[U];
+  uint32_t off[U];
+  auto load = [&](uint32_t i) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t k = i + u * stride;
       off[u] = k < vecs ? k * 16 : kOOB;
       v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off[u], 0, kCbLoadAux);
     }
+  };
+  uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  asm volatile("" ::: "memory");  // the previous slice's stores stay ahead of these loads
+  load(i);
+  static_assert(U == 8, "the wait below leaves the U loads in flight");
+  if (uniform(prev) >= 0) {
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    cb_arrive(a, prev);
+  }
+  for (;;) {
 #pragma unroll
     for (int u = 0; u < U; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, (int)off[u], 0, kAuxAgent);
+    i += U * stride;
+    if (i >= vecs) break;
+    load(i);
   }
-  const int64_t old = wg_arrive_agent(a.counters + s);
-  if (threadIdx.x == 0 && old + 1 == (int64_t)gridDim.x) {
-    wave_acquire();
-    __hip_atomic_store(a.out_flags + (int64_t)s * a.flag_stride, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();  // separates this thread-0 branch from the next slice's
 }
 
 // Tokens t0 + j * stride (j < J), by one wave.  The lanes first load every
@@ -284,10 +309,18 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     // Slices in position order rank+1, rank+2, ...: each is complete (and
     // signalled) before the next begins, so peers can start on it early.
     const int ranks = uniform(a.ranks);  // a loop around barriers: bounded by a scalar
+    int prev = -1;  // the slice put last, not arrived for yet
     for (int pos = 0; pos + 1 < ranks; ++pos) {
-      const int s = cb_slice_at(a, pos);
+      // scalars to the compiler: the slice picks the buffer resources
+      const int s = uniform(cb_slice_at(a, pos));
       const int rows = uniform(g.rows[s]);
-      if (rows) cb_put_slice(a, s, rows);
+      if (!rows) continue;
+      cb_put_slice(a, s, rows, prev);
+      prev = s;
+    }
+    if (uniform(prev) >= 0) {
+      wave_drain();
+      cb_arrive(a, prev);
     }
   }
   if (!a.do_sum) return;
