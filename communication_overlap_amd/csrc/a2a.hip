@@ -39,20 +39,20 @@ constexpr int kA2aMaxRanks = 16;
 constexpr int kA2aMaxExperts = 64;
 constexpr int kChunkRows = 32;
 constexpr int kGbm = 256, kGbn = 256;  // grouped GEMM tile
-// The FP8 tile is half as wide: its epilogue scales every accumulator, and
-// with 256 columns the compiler moves them all out of the accumulation
-// registers at once and spills.
-constexpr int kGbn8 = 128;
+// The FP8 tile: 256 x 256 over eight waves, each wave's share (128 x 64) as
+// in the four-wave 256 x 128 tile it replaced (a four-wave 256 x 256 tile
+// spilled: its scaled epilogue moved all 256 accumulators out at once).
+constexpr int kGbn8 = 256;
 constexpr int kA2aMaxMTiles = 1024;    // m-tiles whose consumer order is sorted in LDS
 constexpr int kA2aXcds = 8;
 // Trace layout (int64): [R] slice publish times, [kA2aTraceProducers]
 // producer finish times, then kA2aTraceItem values per work item.
 constexpr int kA2aTraceProducers = 64;
 constexpr int kA2aTraceItem = 8;
-// Wavefronts per workgroup of the fused launch: the bf16 tile runs as a
-// 2 x 4 grid of waves, two per SIMD (one's MFMAs cover the other's LDS
-// reads; measured faster than 4); the FP8 tile as a 2 x 2 grid.
-constexpr int a2a_waves(bool f8) { return f8 ? 4 : 8; }
+// Wavefronts per workgroup of the fused launch: both tiles run as a 2 x 4
+// grid of waves, two per SIMD (one's MFMAs cover the other's LDS reads;
+// measured faster than 4 for both).
+constexpr int a2a_waves(bool) { return 8; }
 // LDS of a grouped-GEMM tile, bf16 or FP8 (the geometry follows it).
 constexpr int kA2aGemmLds = TileCfg<kGbm, kGbn>::LDS_BYTES > F8Cfg<kGbm, kGbn8>::LDS_BYTES
                                 ? TileCfg<kGbm, kGbn>::LDS_BYTES
@@ -632,9 +632,18 @@ __device__ void a2a_consume(const A2aArgs& a, const Geometry* g, int cidx, uint1
       op.n0 = (int64_t)nt * TBN;
       op.n_valid = a.n;
       op.k = a.hidden;
-      gemm_tile_fp8<kGbm, TBN, true>(acc, op, reinterpret_cast<uint8_t*>(lds));
-      acc_store_rows_scaled<kGbm, TBN>(acc, a.y, a.n, (int64_t)a.ranks * a.cap, tab, scaletab[wv & 1],
-                                        a.w_scale + (int64_t)e * a.n, op.n0, a.n);
+      if (a.n - op.n0 <= TBN / 2) {
+        // A last column block at most half a tile wide: a half-width tile
+        // (the same K order per element, so the same bits).
+        Acc<kGbm, TBN / 2, NW> acc2;
+        gemm_tile_fp8<kGbm, TBN / 2, true, NW>(acc2, op, reinterpret_cast<uint8_t*>(lds));
+        acc_store_rows_scaled<kGbm, TBN / 2, NW>(acc2, a.y, a.n, (int64_t)a.ranks * a.cap, tab, scaletab[wv & 1],
+                                                 a.w_scale + (int64_t)e * a.n, op.n0, a.n);
+      } else {
+        gemm_tile_fp8<kGbm, TBN, true, NW>(acc, op, reinterpret_cast<uint8_t*>(lds));
+        acc_store_rows_scaled<kGbm, TBN, NW>(acc, a.y, a.n, (int64_t)a.ranks * a.cap, tab, scaletab[wv & 1],
+                                             a.w_scale + (int64_t)e * a.n, op.n0, a.n);
+      }
     } else {
       Operands op;
       op.a = reinterpret_cast<const uint16_t*>(a.recv_x);

@@ -1,7 +1,7 @@
 // FP8 (OCP E4M3) x FP8 -> fp32 tile GEMM on gfx950 matrix cores.
 //
-// One workgroup of 4 wavefronts computes a BM x BN output tile, the waves in
-// a 2 x 2 grid of (BM/2) x (BN/2) sub-tiles made of 32 x 32 blocks, each
+// One workgroup of NW = 4 or 8 wavefronts computes a BM x BN output tile, the
+// waves in a 2 x (NW/2) grid of sub-tiles made of 32 x 32 blocks, each
 // block a v_mfma_scale_f32_32x32x64_f8f6f4 (both operands E4M3, unit block
 // scales) per 64 codes of K.  Both operands are K-major: A as [row][k] codes
 // (optionally gathered through a row table), B transposed as [n][k] codes,
@@ -44,28 +44,30 @@ struct Operands8 {
   int64_t k;
 };
 
-template <int BM, int BN>
+template <int BM, int BN, int NW = 4>
 struct F8Cfg {
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile shape");
+  static_assert(NW == 4 || NW == 8, "waves per workgroup: a 2 x 2 or 2 x 4 grid");
+  static constexpr int WN = NW / 2;  // waves along N
+  static_assert(BM % 64 == 0 && BN % (32 * WN) == 0, "tile shape");
   static constexpr int FM = BM / 64;
-  static constexpr int FN = BN / 64;
+  static constexpr int FN = BN / (32 * WN);
   static constexpr int A_BYTES = BM * kF8BK;
   static constexpr int B_BYTES = BN * kF8BK;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
   static constexpr int RPI = 1024 / kF8BK;  // rows per load instruction
-  static constexpr int QA = BM / RPI / 4;   // A load instructions per wave per stage
-  static constexpr int QB = BN / RPI / 4;
+  static constexpr int QA = BM / RPI / NW;  // A load instructions per wave per stage
+  static constexpr int QB = BN / RPI / NW;
   static_assert(QA % 2 == 0 && QB % 2 == 0, "swizzle parity per instruction");
 };
 
 // Chunk permutation of a 128-byte row r (that of the bf16 core's BK = 64).
 __device__ inline uint32_t swz8(uint32_t r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int BM, int BN, bool IND>
+template <int BM, int BN, bool IND, int NW>
 struct F8Addr {
   u32x4 ra, rb;
-  uint32_t a_off[IND ? F8Cfg<BM, BN>::QA : 2];  // IND: per instruction (kOOB: no row); else by parity
+  uint32_t a_off[IND ? F8Cfg<BM, BN, NW>::QA : 2];  // IND: per instruction (kOOB: no row); else by parity
   uint32_t a_qstep;
   uint32_t lc[2];     // lane's logical chunk for instructions of parity 0 / 1
   uint32_t b_off[2];  // by parity
@@ -73,10 +75,10 @@ struct F8Addr {
   int32_t k;
 };
 
-template <int BM, int BN, bool IND>
-__device__ inline F8Addr<BM, BN, IND> f8_addr(const Operands8& op) {
-  using C = F8Cfg<BM, BN>;
-  F8Addr<BM, BN, IND> t;
+template <int BM, int BN, bool IND, int NW>
+__device__ inline F8Addr<BM, BN, IND, NW> f8_addr(const Operands8& op) {
+  using C = F8Cfg<BM, BN, NW>;
+  F8Addr<BM, BN, IND, NW> t;
   const uint32_t l = lane_id();
   const uint32_t w = threadIdx.x >> 6;
   t.ra = make_srd(op.a, op.m_valid * op.lda);
@@ -103,9 +105,9 @@ __device__ inline F8Addr<BM, BN, IND> f8_addr(const Operands8& op) {
   return t;
 }
 
-template <int BM, int BN, bool IND>
-__device__ inline void f8_issue(const F8Addr<BM, BN, IND>& t, uint32_t stage, int32_t k0) {
-  using C = F8Cfg<BM, BN>;
+template <int BM, int BN, bool IND, int NW>
+__device__ inline void f8_issue(const F8Addr<BM, BN, IND, NW>& t, uint32_t stage, int32_t k0) {
+  using C = F8Cfg<BM, BN, NW>;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int q = 0; q < C::QA; ++q) {
@@ -135,11 +137,11 @@ __device__ inline i32x8 f8_frag(const uint8_t* region, uint32_t row, int kk, uin
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <int BM, int BN>
-__device__ inline void f8_stage_compute(Acc<BM, BN>& acc, const uint8_t* stage) {
-  using C = F8Cfg<BM, BN>;
+template <int BM, int BN, int NW>
+__device__ inline void f8_stage_compute(Acc<BM, BN, NW>& acc, const uint8_t* stage) {
+  using C = F8Cfg<BM, BN, NW>;
   const uint32_t l = lane_id(), wave = threadIdx.x >> 6;
-  const uint32_t wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (BN / 2);
+  const uint32_t wm = (wave / C::WN) * (BM / 2), wn = (wave % C::WN) * (BN / C::WN);
   const uint32_t g = l >> 5, lr = l & 31;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
@@ -163,11 +165,11 @@ __device__ inline void f8_stage_compute(Acc<BM, BN>& acc, const uint8_t* stage) 
 // The K loop of one tile: the next stage's loads are issued at the start of
 // a step, before the MFMAs over the current one.  Ends with a workgroup
 // barrier, so LDS may be reused at once.
-template <int BM, int BN, bool IND = false>
-__device__ inline void gemm_tile_fp8(Acc<BM, BN>& acc, const Operands8& op, uint8_t* lds) {
-  using C = F8Cfg<BM, BN>;
+template <int BM, int BN, bool IND = false, int NW = 4>
+__device__ inline void gemm_tile_fp8(Acc<BM, BN, NW>& acc, const Operands8& op, uint8_t* lds) {
+  using C = F8Cfg<BM, BN, NW>;
   acc_zero(acc);
-  const F8Addr<BM, BN, IND> t = f8_addr<BM, BN, IND>(op);
+  const F8Addr<BM, BN, IND, NW> t = f8_addr<BM, BN, IND, NW>(op);
   const int32_t steps = (int32_t)((op.k + kF8BK - 1) / kF8BK);
   const uint32_t lbase = lds_addr(lds);
   __syncthreads();
@@ -176,7 +178,7 @@ __device__ inline void gemm_tile_fp8(Acc<BM, BN>& acc, const Operands8& op, uint
   __syncthreads();
   for (int32_t s = 0; s < steps; ++s) {
     if (s + 1 < steps) f8_issue(t, lbase + (uint32_t)((s + 1) & 1) * C::STAGE_BYTES, (s + 1) * kF8BK);
-    f8_stage_compute<BM, BN>(acc, lds + (s & 1) * C::STAGE_BYTES);
+    f8_stage_compute<BM, BN, NW>(acc, lds + (s & 1) * C::STAGE_BYTES);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
@@ -186,18 +188,18 @@ __device__ inline void gemm_tile_fp8(Acc<BM, BN>& acc, const Operands8& op, uint
 // row rows[i] of fp32 C (pitch ldc, c_rows rows; nothing where rows[i] < 0)
 // as acc * tile_scale[i] * col_scale[n0 + col], columns clipped to n_valid.
 // rows and tile_scale are LDS tables of BM entries.
-template <int BM, int BN>
-__device__ inline void acc_store_rows_scaled(const Acc<BM, BN>& acc, float* c, int64_t ldc, int64_t c_rows,
+template <int BM, int BN, int NW = 4>
+__device__ inline void acc_store_rows_scaled(const Acc<BM, BN, NW>& acc, float* c, int64_t ldc, int64_t c_rows,
                                              const int32_t* rows, const float* tile_scale, const float* col_scale,
                                              int64_t n0, int64_t n_valid) {
-  using C = F8Cfg<BM, BN>;
+  using C = F8Cfg<BM, BN, NW>;
   const rsrc_t r = make_rsrc(c, c_rows * ldc * 4);
   const uint32_t ldc_b = opaque((uint32_t)(ldc * 4));
   const int64_t n_left = n_valid - n0;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  const int wm = (wave >> 1) * (BM / 2);
-  const int wn = (wave & 1) * (BN / 2);
+  const int wm = (wave / C::WN) * (BM / 2);
+  const int wn = (wave % C::WN) * (BN / C::WN);
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll

@@ -333,9 +333,9 @@ typedef struct a2a_desc {
   int32_t flag_stride;       /* bytes, multiple of 8, >= 8 */
   int32_t tile_m, tile_n;    /* grouped-GEMM tile: tile_m rows of one expert's received rows
                                 (taken across slices) x tile_n output columns.  0, 0 = the
-                                default; the implemented tiles are 256 x 256 for bf16 rows
-                                (a last column block at most half a tile wide runs as 256 x 128)
-                                and 256 x 128 for FP8 rows.  Any other pair: OVL_EUNSUPPORTED.
+                                default; the implemented tile is 256 x 256 for bf16 and for FP8
+                                rows (a last column block at most half a tile wide runs as
+                                256 x 128).  Any other pair: OVL_EUNSUPPORTED.
                                 The combine does not read them. */
 } a2a_desc;
 

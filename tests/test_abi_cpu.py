@@ -203,11 +203,11 @@ def test_gemm_rs_tile_sizes():
 
 @pytest.mark.parametrize("f8,tile,ok", [
     (False, (0, 0), True), (False, (256, 256), True), (False, (256, 128), False), (False, (128, 128), False),
-    (True, (0, 0), True), (True, (256, 128), True), (True, (256, 256), False), (True, (128, 64), False),
+    (True, (0, 0), True), (True, (256, 256), True), (True, (256, 128), False), (True, (128, 64), False),
 ])
 def test_dispatch_tile_arguments(f8, tile, ok):
     """The grouped-GEMM tile of the dispatch descriptor: 0 x 0 (default) or
-    the implemented one (bf16 256 x 256, FP8 256 x 128) pass the argument
+    the implemented one (256 x 256 for bf16 and FP8 rows) pass the argument
     checks; any other pair is refused with OVL_EUNSUPPORTED before any device
     work.  (An accepted tile fails later on the null row buffers, with
     OVL_EINVAL: no device is touched either way.)"""
@@ -232,8 +232,8 @@ def test_flag_and_workspace_sizes():
     assert o.a2a_flags_bytes(ad) == 8 * 128
     assert o.a2a_workspace_bytes(ad) >= o.ERROR_RECORD_BYTES + 8 * 8
     # the trace holds slices, 64 producers and 8 int64 per possible work item:
-    # m-tiles <= 8 * 8192 / 256 + 8, n-tiles of 128 columns: 11
-    assert o.a2a_trace_bytes(ad) == 8 * (8 + 64 + 8 * (8 * 8192 // 256 + 8) * 11)
+    # m-tiles <= 8 * 8192 / 256 + 8, n-tiles of 256 columns: 6
+    assert o.a2a_trace_bytes(ad) == 8 * (8 + 64 + 8 * (8 * 8192 // 256 + 8) * 6)
 
 
 @pytest.mark.parametrize("name,tpf,splits", [
