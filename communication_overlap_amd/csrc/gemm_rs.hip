@@ -196,6 +196,13 @@ __global__ __launch_bounds__(64 * rs_waves<TILE>(), 1) void gemm_rs_kernel(RsArg
   const int cidx = blockIdx.x;
   const int x = cidx % groups, q = cidx / groups;
   bool timed_out = false;
+  // Half of each die's workgroups run their first reduce job after their
+  // next tile instead of right after the first: the workgroups would
+  // otherwise all reduce at once (memory-bound, matrix units idle) and all
+  // compute at once; staggered, one half's reduction overlaps the other
+  // half's tile.  Any order gives the same bits (a job's sum order is fixed).
+  const bool stagger = (q & 1) != 0;
+  int64_t deferred = -1;  // a peer tile whose reduce job waits for the next tile
 
   for (int64_t w = 0;; ++w) {
     const int64_t j = deal_item(w, x, q, groups, per, total);
@@ -241,10 +248,18 @@ __global__ __launch_bounds__(64 * rs_waves<TILE>(), 1) void gemm_rs_kernel(RsArg
     if (blk != a.rank) {
       acc_store<BM, BN, kAuxAgent, NW>(acc, a.peer_out[blk], a.n, m0, op.n0, a.bm, a.n);
       if (SYNC) publish(a.out_flags + ((int64_t)blk * tpb + t) * a.flag_stride);
-      reduce_job<TILE>(a, pj, J, timed_out, lds);
+      if (stagger && w == 0 && deal_item(1, x, q, groups, per, total) >= 0) {
+        deferred = pj;
+      } else {
+        reduce_job<TILE>(a, pj, J, timed_out, lds);
+      }
     } else {
       acc_store<BM, BN, kAuxAgent, NW>(acc, a.out, a.n, m0, op.n0, a.bm, a.n);
       if (J > 0) publish(a.own_flags + t);
+    }
+    if (w == 1 && deferred >= 0) {
+      reduce_job<TILE>(a, deferred, J, timed_out, lds);
+      deferred = -1;
     }
   }
 }
