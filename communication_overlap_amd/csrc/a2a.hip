@@ -109,8 +109,13 @@ __device__ inline int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_in
 // entry order, each matching lane at its wave's running count plus the
 // matches of the lanes below it (a ballot).  Rows of a slice are thus
 // ordered by (expert, token, choice), as the layout defines.
-__global__ __launch_bounds__(kThreads) void a2a_layout_kernel(A2aArgs a) {
-  constexpr int NWV = kThreads / 64;
+// Sixteen waves per (source, expert) workgroup: at the MoE workload (4096
+// tokens x top-2) each wave then reads its 512 entries in one round of loads
+// per pass.
+constexpr int kLayoutThreads = 1024;
+
+__global__ __launch_bounds__(kLayoutThreads) void a2a_layout_kernel(A2aArgs a) {
+  constexpr int NWV = kLayoutThreads / 64;
   constexpr int B = 8;  // 64-entry groups loaded before they are looked at
   __shared__ int smem[2 * NWV];
   const int s = blockIdx.x / a.experts, e = blockIdx.x % a.experts;
@@ -856,7 +861,7 @@ ovl_status a2a_run(const a2a_desc* d, bool f8, const void* const* x, const float
   if (mode != OVL_MODE_GEMM_ONLY) {
     st = epoch_accept(flags, epoch);
     if (st) return st;
-    hipLaunchKernelGGL(a2a_layout_kernel, dim3(d->ranks * d->experts_per_rank), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(a2a_layout_kernel, dim3(d->ranks * d->experts_per_rank), dim3(kLayoutThreads), 0, stream, a);
     OVL_HIP_TRY(hipGetLastError());
   }
   if (mode == OVL_MODE_COPY_ONLY) {

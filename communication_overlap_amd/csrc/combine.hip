@@ -71,8 +71,12 @@ __device__ inline int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_in
 // takes a contiguous range of the choices and reads it 64 at a time, lane l
 // the l-th (coalesced); the wave totals give each wave's first row, and a
 // ballot each matching lane's place after the matches of the lanes below.
-__global__ __launch_bounds__(kThreads) void combine_layout_kernel(CombineArgs a) {
-  constexpr int NWV = kThreads / 64;
+// Sixteen waves per (peer, expert) workgroup: at the MoE workload each wave
+// reads its share of the choices in one round of loads per pass.
+constexpr int kCbLayoutThreads = 1024;
+
+__global__ __launch_bounds__(kCbLayoutThreads) void combine_layout_kernel(CombineArgs a) {
+  constexpr int NWV = kCbLayoutThreads / 64;
   constexpr int B = 8;  // 64-choice groups loaded before they are looked at
   __shared__ int smem[2 * NWV];
   const int q = blockIdx.x / a.experts, e = blockIdx.x % a.experts;
@@ -427,7 +431,7 @@ extern "C" ovl_status a2a_combine_run(const a2a_desc* d, const float* y, const i
     st = epoch_accept(out_flags, epoch);
     if (st) return st;
   }
-  hipLaunchKernelGGL(combine_layout_kernel, dim3(d->ranks * d->experts_per_rank), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(combine_layout_kernel, dim3(d->ranks * d->experts_per_rank), dim3(kCbLayoutThreads), 0, stream, a);
   OVL_HIP_TRY(hipGetLastError());
   // Two workgroups per compute unit (the put's grid stride and the final
   // arrival count both use this number).
