@@ -485,7 +485,11 @@ __device__ inline int take_chunk(const A2aArgs& a, int total, int* sh) {
   return ch;
 }
 
-__global__ __launch_bounds__(kThreads) void a2a_produce_kernel(A2aArgs a) {
+// Copy-only producers run eight waves (FP8 rows: dispatch alone 88 -> 81.5
+// us; bf16 rows: the same 133 us as with four).
+constexpr int kProduceThreads = 512;
+
+__global__ __launch_bounds__(kProduceThreads) void a2a_produce_kernel(A2aArgs a) {
   __shared__ Geometry g;
   build_geometry(a, &g);
   a2a_produce(a, &g, blockIdx.x, gridDim.x, 0, uniform(g.chunk_base[a.ranks]));
@@ -870,7 +874,7 @@ ovl_status a2a_run(const a2a_desc* d, bool f8, const void* const* x, const float
     const int P = req ? (int)req : di.cus;
     a.producers = P;
     a.consumers = 0;
-    hipLaunchKernelGGL(a2a_produce_kernel, dim3(P), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(a2a_produce_kernel, dim3(P), dim3(kProduceThreads), 0, stream, a);
     OVL_HIP_TRY(hipGetLastError());
     return OVL_OK;
   }
